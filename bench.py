@@ -1,0 +1,291 @@
+"""Benchmark of the per-decode-step sparse KV assembly path on one MI355X.
+
+A step is one decode step of the whole hot path for every request and layer of
+the workload: slot lookup + sparse diff + LRU (diff_lru), hit gather (HBM),
+miss fetch + write-back (PCIe), split-K sparse MLA attention and combine.
+Inputs (host pool rows, Top-K streams, queries) are seeded and synthetic and
+are resident (pool in pinned host memory, the rest in HBM) before timing.
+
+Prints one JSON line.  ``value`` is selected KV tokens gathered per second
+(B * L * K per step); decode steps per second, the HBM and host-link
+bandwidth figures, the roofline of the dominant kernel and the CPU oracle
+baseline are fields of the same line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import kvs_workload as W  # noqa: E402
+
+METRIC = "selected KV tokens gathered/sec + decode steps/sec; % of HBM and PCIe peak GB/s"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+PCIE_PEAK_GBS = 63.0             # PCIe Gen5 x16, one direction: 32 GT/s * 16 * 128/130 / 8
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+ROW = W.ROW_BYTES
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30, help="timed decode steps")
+    p.add_argument("--warmup", type=int, default=2, help="untimed decode steps (step 0 is cold)")
+    p.add_argument("--workload", default=W.BENCH_WORKLOAD, choices=sorted(W.WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--parity-requests", type=int, default=2)
+    p.add_argument("--no-profile", action="store_true", help="skip per-kernel HIP events")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kvs_kernels.hip", "kvs_api.cpp", "kvs_internal.h"):
+        with open(os.path.join(ROOT, "token_level_gather_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they match this source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def measure_h2d_peak(torch, nbytes=1 << 30, reps=5) -> float:
+    """Best of `reps` hipMemcpyAsync copies of 1 GiB from pinned host memory, GB/s."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src, non_blocking=True)
+        e1.record()
+        e1.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
+def cpu_baseline(wl, host, topk, q, total_steps, seconds, keep_requests):
+    """Time the oracle replaying whole requests on one host thread.
+
+    Requests are replayed in order until `seconds` have passed (at least
+    `keep_requests` of them); the outputs and final maps of the first
+    `keep_requests` are returned for the parity check.
+    """
+    from threadpoolctl import threadpool_limits
+
+    from oracle import OracleUnit
+    units = 0
+    kept = {}
+    b = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while b < wl.batch:
+            for l in range(wl.layers):
+                u = OracleUnit(wl.context, wl.slots, wl.topk)
+                for t in range(total_steps):
+                    r = u.step(topk[t, l, b], host[b, l], q[t, l, b], wl.scale)
+                    if b < keep_requests:
+                        kept[(t, l, b)] = r.out
+                if b < keep_requests:
+                    kept[("state", l, b)] = (u.tok2slot.copy(), u.slot2tok.copy(),
+                                             u.last_used.copy())
+                units += 1
+            b += 1
+            if b >= keep_requests and time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    tokens = units * total_steps * wl.topk
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle replay of requests 0..{b - 1} x {wl.layers} layer(s) x "
+                      f"{total_steps} steps (K={wl.topk}) on 1 host thread, {dt:.1f} s"}, kept
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; run with --gpus 1 "
+                                   "(the path shards by request, see the design notes)"}))
+        sys.exit(2)
+    import torch
+
+    import token_level_gather_amd as kvs
+
+    wl = W.WORKLOADS[args.workload]
+    B, L, N, S, K = wl.batch, wl.layers, wl.context, wl.slots, wl.topk
+    total = args.warmup + args.steps
+    torch.cuda.set_device(0)
+    print(f"# workload {wl.name}: B={B} L={L} N={N} S={S} K={K} f={wl.fresh_rate} "
+          f"steps {args.warmup}+{args.steps}", file=sys.stderr, flush=True)
+
+    pool = kvs.Pool(B, L, N, S, K, scale=wl.scale)
+    W.fill_pool(pool.host.array, wl)
+    topk_np = W.topk_streams(wl, total)
+    topk = torch.from_numpy(topk_np).cuda()                         # [T][L][B][K]
+    q_np = np.stack([np.stack([W.queries(wl, l, t) for l in range(L)]) for t in range(total)])
+    q = torch.from_numpy(q_np.view(np.int16)).cuda().view(torch.bfloat16)  # [T][L][B][16][576]
+    out = torch.empty((total, L, B, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((total, L, B, 16), dtype=torch.float32, device="cuda")
+    print(f"# inputs ready, pool {pool.host.nbytes / 1e9:.2f} GB pinned", file=sys.stderr,
+          flush=True)
+
+    def run_step(t):
+        for l in range(L):
+            pool.step(l, topk[t, l], q[t, l], out[t, l], lse[t, l])
+
+    cold = None
+    for t in range(args.warmup):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_step(t)
+        torch.cuda.synchronize()
+        if t == 0:
+            cold = (time.perf_counter() - t0) * 1e3
+    rc, st0 = pool.sync_status()
+    assert rc == 0, kvs.strerror(rc)
+
+    if not args.no_profile:
+        pool.profile_begin(args.steps * L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, total):
+        run_step(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ktimes = pool.profile_end() if not args.no_profile else None
+    rc, st1 = pool.sync_status()
+    assert rc == 0, kvs.strerror(rc)
+    print(f"# timed {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr, flush=True)
+
+    ms_step = elapsed * 1e3 / args.steps
+    launches = args.steps * L
+    hits = st1.hits - st0.hits
+    misses = st1.misses - st0.misses
+    miss_rate = misses / max(1, hits + misses)
+    tokens_per_step = B * L * K
+    value = tokens_per_step / (ms_step * 1e-3)
+
+    # algorithmic bytes per launch (one kvs_step call = B units of one layer)
+    hit_l, miss_l = hits / launches, misses / launches
+    splits = pool.sizes.attn_splits
+    part_bytes = B * splits * 16 * (512 + 2) * 4
+    alg = {
+        "diff_lru": {"bound": "hbm", "bytes": B * (16 * K + 4 * S) + 32 * miss_l},
+        "hit_gather": {"bound": "hbm", "bytes": 2 * ROW * hit_l},
+        "miss_fetch": {"bound": "pcie", "bytes": ROW * miss_l, "hbm_write_bytes": 2 * ROW * miss_l},
+        "attention": {"bound": "hbm", "bytes": B * (K * ROW + 16 * 576 * 2) + part_bytes,
+                      "flop": B * 2 * 16 * K * (576 + 512)},
+        "combine": {"bound": "hbm", "bytes": part_bytes + B * 16 * 512 * 2},
+    }
+    kernels = {}
+    dominant = None
+    if ktimes is not None:
+        for name, a in alg.items():
+            avg_ms = ktimes[name] / max(1, ktimes["steps"])
+            gbs = a["bytes"] / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
+            peak = PCIE_PEAK_GBS if a["bound"] == "pcie" else HBM_PEAK_GBS
+            k = {"avg_ms": round(avg_ms, 5), "bound": a["bound"], "bytes_per_launch": int(a["bytes"]),
+                 "achieved_gbs": round(gbs, 2), "peak_gbs": peak, "frac": round(gbs / peak, 4)}
+            if "flop" in a:
+                tf = a["flop"] / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
+                k["tflops"] = round(tf, 2)
+                k["mfma_frac"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 5)
+            if "hbm_write_bytes" in a:
+                k["hbm_write_gbs"] = round(a["hbm_write_bytes"] / (avg_ms * 1e-3) / 1e9, 2)
+            kernels[name] = k
+            if dominant is None or avg_ms > kernels[dominant]["avg_ms"]:
+                dominant = name
+
+    h2d = measure_h2d_peak(torch)
+    roofline = None
+    if dominant is not None:
+        d = kernels[dominant]
+        roofline = {"kernel": dominant, "bound": d["bound"], "achieved": d["achieved_gbs"],
+                    "peak": d["peak_gbs"], "unit": "GB/s", "frac": d["frac"],
+                    "traffic": load_traffic(dominant, wl.name)}
+        if d["bound"] == "pcie":
+            roofline["frac_of_measured_h2d"] = round(d["achieved_gbs"] / h2d, 4)
+
+    # parity of sampled requests against the oracle, plus the CPU baseline
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        host = pool.host.array
+        npar = min(args.parity_requests, B)
+        cpu, rec = cpu_baseline(wl, host, topk_np, q_np, total, args.cpu_seconds, npar)
+        out_np = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        max_abs = max_rel = 0.0
+        state_ok = True
+        for b in range(npar):
+            for l in range(L):
+                for t in range(total):
+                    ref = rec[(t, l, b)]
+                    got = (out_np[t, l, b].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                    err = got - ref
+                    max_abs = max(max_abs, float(np.abs(err).max()))
+                    max_rel = max(max_rel, float(np.linalg.norm(err) / np.linalg.norm(ref)))
+                st = pool.read_state(b, l)
+                t2s, s2t, lu = rec[("state", l, b)]
+                state_ok &= bool(np.array_equal(st["tok2slot"], t2s) and
+                                 np.array_equal(st["slot2tok"], s2t) and
+                                 np.array_equal(st["last_used"], lu))
+        parity = {"requests_checked": npar, "steps_checked": total, "state_bit_exact": state_ok,
+                  "attn_max_abs": round(max_abs, 6), "attn_max_rel_l2": round(max_rel, 6),
+                  "pass": bool(state_ok and max_abs <= 2e-2 and max_rel <= 1e-2)}
+
+    hbm_bytes_step = sum(alg[k]["bytes"] for k in ("diff_lru", "hit_gather", "attention", "combine")) \
+        * L + 2 * ROW * miss_l * L
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "layers": L, "context": N, "slots": S,
+                   "topk": K, "fresh_rate": wl.fresh_rate, "fresh_dist": wl.dist,
+                   "heads": 16, "head_dim": 576, "v_dim": 512, "attn_splits": splits},
+        "decode_steps_per_s": round(1e3 / ms_step, 2),
+        "cold_step_ms": None if cold is None else round(cold, 4),
+        "miss_rate": round(miss_rate, 5),
+        "host_link_gbs_step": round(ROW * misses / args.steps / (ms_step * 1e-3) / 1e9, 3),
+        "hbm_gbs_step": round(hbm_bytes_step / (ms_step * 1e-3) / 1e9, 2),
+        "h2d_peak_measured_gbs": round(h2d, 2),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    pool.release()
+    pool.host.free()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

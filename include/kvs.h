@@ -1,0 +1,230 @@
+/*
+ * kvs.h - C ABI of a per-decode-step sparse KV assembly library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the library does, per decode step and per (request, layer) "unit":
+ * it takes the Top-K token indices chosen by a sparse-attention selector,
+ * looks them up in a device token-to-slot map of a fixed-size hot KV buffer in
+ * HBM, splits them into hits and misses (the sparse diff), evicts by a
+ * deterministic LRU rule, gathers hits from the hot buffer and misses from a
+ * full-history KV pool in pinned host memory into a contiguous compute buffer
+ * in Top-K order, writes the misses back into the hot buffer, and runs
+ * MLA-style Top-K sparse decode attention over the gathered rows.
+ *
+ * Passages this follows:
+ *  - "Sparse Attention-Driven KVCache Management for Domestic AI Supernodes"
+ *    (abstract; agenda "Sparse-Driven System Design"): full history in a host
+ *    memory pool, hot data cached on the device, an index mapping between them,
+ *    Top-K indices driving token-level access, on-demand assembly by an
+ *    index-based copy operator.
+ *  - SGLang/Tair hierarchical sparse attention summary: a Top-k LRU buffer on
+ *    the GPU (first paragraph), Top-k selection then attention over the
+ *    selected tokens (second), incremental transfer of sparse changes through a
+ *    "Sparse Diff Kernel" (third).
+ *  - "XM-Sparse", HiSparse integration section: the request lifecycle
+ *    publish -> fetch -> write-back -> free.
+ *
+ * Fixed by this library where the pages are silent:
+ *  - A KV row is one token of an MLA layer: 576 bf16 values (512 latent +
+ *    64 rope dims), 1152 bytes.  Attention uses all 576 dims for scores and
+ *    dims 0..511 as values, 16 query heads, fp32 softmax and accumulation,
+ *    bf16 output rounded to nearest-even.
+ *  - LRU rule: the victims for the m misses of a step are the m slots that
+ *    hold no token of the current Top-K set, taken in ascending
+ *    (last_used_step, slot) order; an empty slot has last_used_step = -1.  The
+ *    j-th miss in Top-K array order gets the j-th victim.  Hit slots and filled
+ *    slots are stamped with the unit's step counter t, which counts the unit's
+ *    valid steps (starting at 0).
+ *
+ * Conventions for every call:
+ *  - Return value: KVS_OK (0) or a negative KVS_E* code; kvs_strerror names it.
+ *  - "device" pointers are HIP device memory (for instance torch CUDA/HIP tensor
+ *    storage); "host" pointers are ordinary host memory.  The library never
+ *    allocates or frees device memory; the caller owns every buffer and keeps
+ *    it alive until kvs_release.
+ *  - A `stream` argument is a hipStream_t passed as void* (NULL = the default
+ *    stream).  Calls only enqueue work on it, except where stated.
+ *  - A pool is not thread-safe: calls on one pool must not overlap.
+ */
+#ifndef KVS_H_
+#define KVS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------ */
+#define KVS_OK 0
+#define KVS_EINVAL (-22)    /* bad argument or configuration */
+#define KVS_ENOMEM (-12)    /* a caller buffer is smaller than kvs_query_sizes asks */
+#define KVS_ERANGE (-34)    /* device saw a Top-K index outside [0, N) */
+#define KVS_EDUP (-17)      /* device saw a repeated Top-K index within one request */
+#define KVS_EHIP_BASE (-1000) /* KVS_EHIP_BASE - e: HIP runtime error e */
+
+/* ---- limits ------------------------------------------------------------ */
+#define KVS_HEADS 16
+#define KVS_HEAD_DIM 576
+#define KVS_V_DIM 512
+#define KVS_MAX_SLOTS 16384
+#define KVS_MAX_TOPK 8192
+
+/* Indices of the per-kernel times in kvs_kernel_times.ms_total. */
+#define KVS_KERNEL_DIFF_LRU 0   /* lookup + sparse diff + LRU + map update */
+#define KVS_KERNEL_HIT_GATHER 1 /* hot buffer -> compute buffer (HBM) */
+#define KVS_KERNEL_MISS_FETCH 2 /* host pool -> compute buffer + hot buffer (PCIe) */
+#define KVS_KERNEL_ATTENTION 3  /* split-K sparse MLA decode (MFMA) */
+#define KVS_KERNEL_COMBINE 4    /* merge of the split-K partials */
+#define KVS_NUM_KERNELS 5
+
+/*
+ * Shape of a pool.  B requests x L layers = B*L units; each unit has its own
+ * host-pool slice, hot buffer, maps and step counter.
+ */
+typedef struct kvs_config {
+  int32_t batch;        /* B >= 1 requests */
+  int32_t layers;       /* L >= 1 layers */
+  int64_t context;      /* N >= K tokens per unit in the host pool, N < 2^31 */
+  int32_t slots;        /* S hot-buffer rows per unit, K <= S <= KVS_MAX_SLOTS */
+  int32_t topk;         /* K Top-K indices per request per step, 1..KVS_MAX_TOPK */
+  int32_t heads;        /* must be KVS_HEADS */
+  int32_t head_dim;     /* must be KVS_HEAD_DIM */
+  int32_t v_dim;        /* must be KVS_V_DIM */
+  float scale;          /* softmax scale > 0, e.g. 1/sqrt(576) */
+  int32_t attn_splits;  /* token splits per request in attention; 0 = library's choice */
+  int32_t flags;        /* reserved, must be 0 */
+} kvs_config;
+
+/* Bytes each caller buffer must hold (see kvs_buffers). */
+typedef struct kvs_sizes {
+  uint64_t host_pool_bytes; /* B*L*N*576*2: the full-history pool, host */
+  uint64_t hot_bytes;       /* B*L*S*576*2: hot KV buffer, device */
+  uint64_t meta_bytes;      /* index maps, LRU state, counters, status, device */
+  uint64_t cbuf_bytes;      /* B*K*576*2: compute buffer of one step, device */
+  uint64_t scratch_bytes;   /* per-step lists and attention partials, device */
+  int32_t attn_splits;      /* the split count these sizes assume */
+} kvs_sizes;
+
+/*
+ * Buffers handed to kvs_create_pool.  Layouts (row = 576 bf16, row-major):
+ *   host_pool [B][L][N] rows: token n of unit (b, l) at row (b*L + l)*N + n.
+ *             Must come from kvs_host_alloc (pinned and mapped for the GPU).
+ *   hot       [B][L][S] rows, device.   cbuf [B][K] rows, device.
+ *   meta, scratch: opaque device memory, 256-byte aligned.
+ * The *_bytes fields state each buffer's capacity; a capacity below
+ * kvs_query_sizes gives KVS_ENOMEM.  meta is initialised by kvs_create_pool.
+ */
+typedef struct kvs_buffers {
+  const void* host_pool;
+  void* hot;
+  void* meta;
+  void* cbuf;
+  void* scratch;
+  uint64_t host_pool_bytes;
+  uint64_t hot_bytes;
+  uint64_t meta_bytes;
+  uint64_t cbuf_bytes;
+  uint64_t scratch_bytes;
+} kvs_buffers;
+
+/* Totals over all units since kvs_create_pool (kvs_sync_status). */
+typedef struct kvs_step_stats {
+  int64_t unit_steps;   /* valid (request, layer) steps taken */
+  int64_t hits;         /* Top-K entries found in the hot buffer */
+  int64_t misses;       /* Top-K entries fetched from the host pool */
+  int64_t evictions;    /* occupied slots overwritten */
+  int64_t host_bytes;   /* bytes read from the host pool (misses * 1152) */
+  int32_t status;       /* first device-detected error since the last sync, or KVS_OK */
+} kvs_step_stats;
+
+/* Host copies of one unit's state, for tests (kvs_debug_read_state).  Each
+ * pointer may be NULL; otherwise it must hold the stated count of int32. */
+typedef struct kvs_unit_state {
+  int32_t* tok2slot;    /* [N]: slot of token n, -1 if not resident */
+  int32_t* slot2tok;    /* [S]: token in slot s, -1 if empty */
+  int32_t* last_used;   /* [S]: step stamp of slot s, -1 if never used */
+  int32_t* lru_order;   /* [S]: slots in ascending (last_used, slot) order */
+  int32_t* slot_of;     /* [K]: last step of request b: slot of topk[i] before it, -1 = miss */
+  int32_t* miss_pos;    /* [K]: Top-K positions of the misses, first n_miss valid */
+  int32_t* victims;     /* [K]: slot given to the j-th miss, first n_miss valid */
+  int32_t* evicted;     /* [K]: token that slot held, -1 if empty, first n_miss valid */
+  int32_t* counts;      /* [4]: n_hit, n_miss, n_evicted, valid (1) / invalid input (0) */
+  int32_t step;         /* out: the unit's step counter (steps taken) */
+} kvs_unit_state;
+
+/* Per-kernel device time summed over the launches recorded between
+ * kvs_profile_begin and kvs_profile_end (HIP events on the launch streams). */
+typedef struct kvs_kernel_times {
+  int32_t steps;                      /* kvs_step calls recorded */
+  float ms_total[KVS_NUM_KERNELS];    /* sum of launch durations, milliseconds */
+} kvs_kernel_times;
+
+typedef struct kvs_pool kvs_pool;
+
+/* Validate `cfg` and report buffer sizes.  Pure host arithmetic, no GPU call.
+ * KVS_EINVAL if the configuration is outside the limits above. */
+int kvs_query_sizes(const kvs_config* cfg, kvs_sizes* out);
+
+/* Allocate `bytes` of pinned host memory that GPU kernels can read directly
+ * (same address on host and device).  *out receives the pointer; free it with
+ * kvs_host_free after the last pool using it is released. */
+int kvs_host_alloc(uint64_t bytes, void** out);
+int kvs_host_free(void* ptr);
+
+/* Create a pool over caller buffers and initialise its state on `stream`:
+ * every unit empty (maps -1, last_used -1, LRU order 0..S-1), step counters,
+ * stats and status 0.  Does not synchronise. */
+int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream,
+                    kvs_pool** out);
+
+/* Lifecycle "publish": copy `n_tok` rows (host, 1152 B each) into the host pool
+ * of unit (req, layer) starting at token `first_tok`.  Host memcpy; the caller
+ * must not publish into a token that is resident in the hot buffer (free the
+ * request first) nor while steps that read the pool are in flight. */
+int kvs_publish(kvs_pool* pool, int32_t req, int32_t layer, int64_t first_tok,
+                int64_t n_tok, const void* rows);
+
+/* Lifecycle "fetch + write-back" and the Top-K attention of one layer for all
+ * B requests.  Enqueued on `stream`; nothing is synchronised.
+ *   topk [B][K] int32, device: request b's Top-K token indices, unique, in [0, N).
+ *   q    [B][16][576] bf16, device: queries.
+ *   out  [B][16][512] bf16, device: attention output.
+ *   lse  [B][16] fp32, device, or NULL: natural-log log-sum-exp of the scores.
+ * The compute buffer receives request b's rows at cbuf[b][i] = row of topk[b][i].
+ * A request whose Top-K is invalid is skipped: its state is unchanged, its out
+ * row is zero and its lse is -inf; the error is latched for kvs_sync_status.
+ * Calls for one layer must be in decode order; cbuf is reused by every call. */
+int kvs_step(kvs_pool* pool, int32_t layer, const int32_t* topk, const void* q,
+             void* out, float* lse, void* stream);
+
+/* Lifecycle "free": empty every layer of request `req` (maps -1, last_used -1,
+ * LRU order 0..S-1).  Its step counters keep running.  Enqueued on `stream`. */
+int kvs_free_request(kvs_pool* pool, int32_t req, void* stream);
+
+/* Synchronise `stream` and the pool's internal stream, then return the first
+ * device-detected error (KVS_ERANGE / KVS_EDUP) since the last call, or KVS_OK,
+ * and clear it.  `stats` (may be NULL) receives the running totals. */
+int kvs_sync_status(kvs_pool* pool, void* stream, kvs_step_stats* stats);
+
+/* Synchronising copy of unit (req, layer)'s state into host arrays (tests). */
+int kvs_debug_read_state(kvs_pool* pool, int32_t req, int32_t layer, void* stream,
+                         kvs_unit_state* st);
+
+/* Record per-kernel HIP-event times for the next `max_steps` kvs_step calls. */
+int kvs_profile_begin(kvs_pool* pool, int32_t max_steps);
+/* Synchronise and report the recorded times; stops recording. */
+int kvs_profile_end(kvs_pool* pool, kvs_kernel_times* out);
+
+/* Destroy the pool's internal streams and events.  Caller buffers are untouched. */
+int kvs_release(kvs_pool* pool);
+
+/* Static description of a return code. */
+const char* kvs_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H_ */

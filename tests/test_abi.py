@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the header is plain C, struct layouts agree with the binding,
+and configuration / size validation behaves as documented."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import token_level_gather_amd as kvs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvs.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(kvs_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvs.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(kvs.EXPORTS) == declared
+
+
+def test_header_is_plain_c():
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        with open(src, "w") as f:
+            f.write('#include "kvs.h"\nint main(void){kvs_config c; (void)c; return 0;}\n')
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                        "-fsyntax-only", src], check=True)
+
+
+def test_struct_layouts_match_binding():
+    structs = {
+        "kvs_config": kvs.kvs_config, "kvs_sizes": kvs.kvs_sizes,
+        "kvs_buffers": kvs.kvs_buffers, "kvs_step_stats": kvs.kvs_step_stats,
+        "kvs_unit_state": kvs.kvs_unit_state, "kvs_kernel_times": kvs.kvs_kernel_times,
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kvs.h"', "int main(void){"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for field, _ in py._fields_:
+            lines.append(f'printf("{cname}.{field} %zu\\n", offsetof({cname}, {field}));')
+    lines.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    got = dict(l.split() for l in out.splitlines())
+    for cname, py in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for field, _ in py._fields_:
+            assert int(got[f"{cname}.{field}"]) == getattr(py, field).offset, (cname, field)
+
+
+def test_query_sizes_arithmetic():
+    cfg = kvs.make_config(batch=64, layers=1, context=16384, slots=4096, topk=2048)
+    s = kvs.query_sizes(cfg)
+    assert s.host_pool_bytes == 64 * 16384 * 1152 == 1_207_959_552
+    assert s.hot_bytes == 64 * 4096 * 1152 == 301_989_888
+    assert s.cbuf_bytes == 64 * 2048 * 1152 == 150_994_944
+    # maps: tok2slot + slot2tok + last_used + order (+ small counters)
+    assert s.meta_bytes >= 64 * (16384 * 4 + 4096 * 10)
+    assert s.meta_bytes < 64 * (16384 * 4 + 4096 * 10) + 64 * 64 + 4096
+    assert s.attn_splits == 8
+    per = 4 * 64 * 2048 * 4 + 64 * 16 + 64 * 8 * 16 * (512 + 2) * 4
+    assert per <= s.scratch_bytes < per + 8 * 256
+
+
+@pytest.mark.parametrize("bad", [
+    dict(batch=0), dict(layers=0), dict(topk=0), dict(slots=100, topk=200),
+    dict(context=100, topk=200, slots=300), dict(slots=16385), dict(topk=8193, slots=9000),
+    dict(heads=8), dict(head_dim=512), dict(v_dim=576), dict(scale=0.0),
+    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=1), dict(context=2**31),
+    dict(attn_splits=33),   # more splits than 64-token tiles (K = 2048 -> 32)
+])
+def test_bad_configs_rejected(bad):
+    args = dict(batch=2, layers=1, context=4096, slots=4096, topk=2048)
+    args.update(bad)
+    cfg = kvs.make_config(**args)
+    out = kvs.kvs_sizes()
+    assert kvs.lib().kvs_query_sizes(ctypes.byref(cfg), ctypes.byref(out)) == kvs.KVS_EINVAL
+
+
+def test_good_config_accepted():
+    cfg = kvs.make_config(batch=2, layers=1, context=4096, slots=4096, topk=2048)
+    out = kvs.kvs_sizes()
+    assert kvs.lib().kvs_query_sizes(ctypes.byref(cfg), ctypes.byref(out)) == kvs.KVS_OK
+
+
+def test_create_pool_argument_checks_before_any_gpu_call():
+    lib = kvs.lib()
+    cfg = kvs.make_config(batch=1, layers=1, context=4096, slots=512, topk=256)
+    handle = ctypes.c_void_p()
+    assert lib.kvs_create_pool(ctypes.byref(cfg), None, None, ctypes.byref(handle)) == kvs.KVS_EINVAL
+    fake = 1 << 20   # aligned, never dereferenced: the size check fails first
+    bufs = kvs.kvs_buffers(fake, fake, fake, fake, fake, 16, 16, 16, 16, 16)
+    assert lib.kvs_create_pool(ctypes.byref(cfg), ctypes.byref(bufs), None,
+                               ctypes.byref(handle)) == kvs.KVS_ENOMEM
+    nul = kvs.kvs_buffers(None, fake, fake, fake, fake, 1 << 40, 1 << 40, 1 << 40, 1 << 40, 1 << 40)
+    assert lib.kvs_create_pool(ctypes.byref(cfg), ctypes.byref(nul), None,
+                               ctypes.byref(handle)) == kvs.KVS_EINVAL
+    assert handle.value is None
+
+
+def test_null_pool_calls_are_rejected():
+    lib = kvs.lib()
+    assert lib.kvs_step(None, 0, None, None, None, None, None) == kvs.KVS_EINVAL
+    assert lib.kvs_free_request(None, 0, None) == kvs.KVS_EINVAL
+    assert lib.kvs_release(None) == kvs.KVS_EINVAL
+    assert lib.kvs_publish(None, 0, 0, 0, 0, None) == kvs.KVS_EINVAL
+    assert lib.kvs_profile_begin(None, 1) == kvs.KVS_EINVAL
+
+
+def test_strerror():
+    assert "duplicate" in kvs.strerror(kvs.KVS_EDUP)
+    assert "outside" in kvs.strerror(kvs.KVS_ERANGE)
+    assert kvs.strerror(kvs.KVS_OK) == "ok"
+    assert "HIP" in kvs.strerror(kvs.KVS_EHIP_BASE - 2)

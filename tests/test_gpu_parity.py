@@ -1,0 +1,248 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
+
+Bit-exact: slot lookup, sparse diff (miss positions), victims, evicted tokens,
+the index maps, LRU stamps and order, the gathered compute-buffer bytes and the
+hot-buffer bytes of every occupied slot.  Attention: per (step, layer,
+request) max-abs <= 2e-2 and relative L2 <= 1e-2 against the float64 oracle,
+and the log-sum-exp within 2e-3.
+
+Small shapes check every unit after every step; full-size workloads check
+sampled requests after every step (units are independent, so the oracle only
+needs the sampled units).
+"""
+import numpy as np
+import pytest
+
+import kvs_workload as W
+from oracle import KvsError as OracleError
+from oracle import OracleUnit
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L2 = 1e-2
+LSE_ABS = 2e-3
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+def _pool(wl, host=None):
+    import token_level_gather_amd as kvs
+    return kvs.Pool(wl.batch, wl.layers, wl.context, wl.slots, wl.topk, scale=wl.scale,
+                    host=host)
+
+
+def _u16(t):
+    torch = _torch()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class Harness:
+    """Drives one pool through a workload and checks sampled units each step."""
+
+    def __init__(self, wl, steps, check_reqs, fill="all"):
+        torch = _torch()
+        self.wl, self.steps = wl, steps
+        self.check_reqs = list(check_reqs)
+        self.pool = _pool(wl)
+        host = self.pool.host.array
+        if fill == "all":
+            W.fill_pool(host, wl)
+        else:   # only the checked requests need real rows; other units read whatever is there
+            for b in self.check_reqs:
+                for l in range(wl.layers):
+                    W.fill_unit_rows(host[b, l], wl, b, l)
+        self.topk = W.topk_streams(wl, steps)
+        self.oracle = {(b, l): OracleUnit(wl.context, wl.slots, wl.topk)
+                       for b in self.check_reqs for l in range(wl.layers)}
+        self.out = torch.empty((wl.batch, 16, 512), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((wl.batch, 16), dtype=torch.float32, device="cuda")
+        self.max_abs = 0.0
+        self.max_rel = 0.0
+
+    def device_step(self, t, l, topk=None):
+        torch = _torch()
+        tk = self.topk[t, l] if topk is None else topk
+        q = W.queries(self.wl, l, t)
+        self.q = q
+        self.pool.step(l, torch.from_numpy(np.ascontiguousarray(tk)).cuda(),
+                       torch.from_numpy(q.view(np.int16)).cuda(), self.out, self.lse)
+        torch.cuda.synchronize()
+        return tk, q
+
+    def check(self, t, l, tk, q):
+        wl = self.wl
+        out = _u16(self.out)
+        lse = self.lse.cpu().numpy()
+        for b in self.check_reqs:
+            u = self.oracle[(b, l)]
+            rec = u.step(tk[b], self.pool.host.array[b, l], q[b], wl.scale)
+            st = self.pool.read_state(b, l)
+            n = rec.n_miss
+            tag = f"step {t} layer {l} req {b}"
+            assert st["counts"].tolist() == [rec.n_hit, n, int((rec.evicted >= 0).sum()), 1], tag
+            assert np.array_equal(st["slot_of"], rec.slot_of), tag
+            assert np.array_equal(st["miss_pos"][:n], rec.miss_pos), tag
+            assert np.array_equal(st["victims"][:n], rec.victims), tag
+            assert np.array_equal(st["evicted"][:n], rec.evicted), tag
+            assert np.array_equal(st["tok2slot"], u.tok2slot), tag
+            assert np.array_equal(st["slot2tok"], u.slot2tok), tag
+            assert np.array_equal(st["last_used"], u.last_used), tag
+            order = np.lexsort((np.arange(wl.slots), u.last_used))
+            assert np.array_equal(st["lru_order"], order), tag
+            assert st["step"] == u.t, tag
+            row = wl.topk * 1152
+            cbuf = _u16(self.pool.cbuf[b * row:(b + 1) * row]).reshape(wl.topk, 576)
+            assert np.array_equal(cbuf, rec.cbuf), tag + " cbuf bytes"
+            hrow = wl.slots * 1152
+            hu = b * wl.layers + l
+            hot = _u16(self.pool.hot[hu * hrow:(hu + 1) * hrow]).reshape(wl.slots, 576)
+            occ = u.slot2tok >= 0
+            assert np.array_equal(hot[occ], u.hot[occ]), tag + " hot bytes"
+            got = _bf16_to_f64(out[b])
+            err = got - rec.out
+            max_abs = float(np.abs(err).max())
+            rel = float(np.linalg.norm(err) / np.linalg.norm(rec.out))
+            assert max_abs <= MAX_ABS and rel <= REL_L2, f"{tag}: max_abs {max_abs} rel {rel}"
+            assert float(np.abs(lse[b] - rec.lse).max()) <= LSE_ABS, tag + " lse"
+            self.max_abs = max(self.max_abs, max_abs)
+            self.max_rel = max(self.max_rel, rel)
+
+    def run(self):
+        for t in range(self.steps):
+            for l in range(self.wl.layers):
+                tk, q = self.device_step(t, l)
+                self.check(t, l, tk, q)
+        rc, stats = self.pool.sync_status()
+        assert rc == 0
+        return stats
+
+    def close(self):
+        self.pool.release()
+        self.pool.host.free()
+
+
+def _case(wl, steps, reqs, fill="all"):
+    h = Harness(wl, steps, reqs, fill)
+    try:
+        stats = h.run()
+        print(f"{wl.name}: steps {steps} max_abs {h.max_abs:.3g} max_rel {h.max_rel:.3g} "
+              f"miss rate {stats.misses / max(1, stats.hits + stats.misses):.3f}", flush=True)
+        return h, stats
+    finally:
+        h.close()
+
+
+# ---------------------------------------------------------------- small shapes, every unit
+
+def test_4k_context_single_request_all_steps():
+    wl = W.WORKLOADS["ctx4k_b1_k256"]
+    _case(wl, wl.steps, [0])
+
+
+@pytest.mark.parametrize("shape", [
+    dict(batch=3, layers=1, context=5000, slots=700, topk=300, fresh_rate=0.3),   # ragged tiles
+    dict(batch=2, layers=3, context=3000, slots=1100, topk=1025, fresh_rate=0.2),  # multi-layer
+    dict(batch=4, layers=1, context=900, slots=64, topk=64, fresh_rate=0.5),      # S == K
+    dict(batch=2, layers=1, context=2000, slots=40, topk=1, fresh_rate=1.0),      # K == 1
+    dict(batch=2, layers=1, context=130, slots=130, topk=130, fresh_rate=0.0),    # N == S == K
+    dict(batch=5, layers=2, context=20000, slots=16384, topk=8192, fresh_rate=0.4),  # limits
+])
+def test_small_shapes_every_unit(shape):
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="small", steps=6, **shape)
+    _case(wl, wl.steps, range(wl.batch))
+
+
+def test_zipf_stream_small():
+    wl = W.WORKLOADS["ctx128k_b32_l8_zipf"].shrunk(batch=3, layers=2, context=20000, steps=6)
+    _case(wl, wl.steps, range(wl.batch))
+
+
+# ---------------------------------------------------------------- lifecycle and errors
+
+def test_free_request_then_cold_refill():
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(batch=3, context=4000, slots=600, topk=256,
+                                                  steps=8)
+    h = Harness(wl, wl.steps, range(3))
+    try:
+        for t in range(4):
+            h.check(t, 0, *h.device_step(t, 0))
+        h.pool.free_request(1)
+        h.oracle[(1, 0)].reset()
+        for t in range(4, 8):
+            h.check(t, 0, *h.device_step(t, 0))
+        st = h.pool.read_state(1, 0)
+        assert st["step"] == 8
+    finally:
+        h.close()
+
+
+@pytest.mark.parametrize("kind", ["range", "negative", "duplicate"])
+def test_invalid_topk_leaves_request_untouched(kind):
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(batch=3, context=3000, slots=500, topk=200,
+                                                  steps=6)
+    h = Harness(wl, wl.steps, range(3))
+    try:
+        for t in range(2):
+            h.check(t, 0, *h.device_step(t, 0))
+        before = h.pool.read_state(1, 0)
+        bad = h.topk[2, 0].copy()
+        if kind == "range":
+            bad[1, 17] = wl.context
+        elif kind == "negative":
+            bad[1, 0] = -5
+        else:
+            bad[1, 9] = bad[1, 3]
+        with pytest.raises(OracleError):
+            h.oracle[(1, 0)].step(bad[1], h.pool.host.array[1, 0])
+        h.device_step(2, 0, topk=bad)
+        rc, _ = h.pool.sync_status()
+        assert rc == (kvs.KVS_EDUP if kind == "duplicate" else kvs.KVS_ERANGE)
+        after = h.pool.read_state(1, 0)
+        for key in ("tok2slot", "slot2tok", "last_used", "lru_order", "step"):
+            assert np.array_equal(np.asarray(before[key]), np.asarray(after[key])), key
+        assert after["counts"][3] == 0
+        assert not torch.any(h.out[1].float() != 0).item()
+        assert torch.isinf(h.lse[1]).all().item()
+        # the other requests took the step normally
+        for b in (0, 2):
+            rec = h.oracle[(b, 0)].step(bad[b], h.pool.host.array[b, 0])
+            assert np.array_equal(h.pool.read_state(b, 0)["slot2tok"], h.oracle[(b, 0)].slot2tok)
+            assert rec.t == 2
+        # the status was cleared and the request continues from its old state
+        assert h.pool.sync_status()[0] == 0
+        h.check_reqs = [1]
+        h.check(3, 0, *h.device_step(3, 0))
+    finally:
+        h.close()
+
+
+# ---------------------------------------------------------------- full-size workloads, sampled
+
+@pytest.mark.parametrize("name,reqs", [
+    ("ctx16k_b64_k2048", [0, 37, 63]),
+    ("ctx16k_b192_k2048_f20", [0, 191]),
+    ("ctx16k_b192_k2048_f40", [5, 100]),
+])
+def test_full_size_16k_sampled(name, reqs):
+    wl = W.WORKLOADS[name]
+    _case(wl, wl.steps, reqs, fill="checked")
+
+
+@pytest.mark.parametrize("name,reqs,steps", [
+    ("ctx128k_b32_l8_zipf", [0, 31], 6),
+    ("ctx1m_b4_l4", [3], 6),
+])
+def test_full_size_long_context_sampled(name, reqs, steps):
+    wl = W.WORKLOADS[name]
+    _case(wl, steps, reqs, fill="checked")

@@ -1,0 +1,280 @@
+"""Python binding of the MI355X sparse KV assembly library (``libkvs.so``).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch supplies device memory and streams.  The binding loads the
+in-tree ``libkvs.so`` and raises if it is missing; there is no fallback.
+
+Names follow the C ABI in ``include/kvs.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvs.so")
+
+KVS_OK = 0
+KVS_EINVAL = -22
+KVS_ENOMEM = -12
+KVS_ERANGE = -34
+KVS_EDUP = -17
+KVS_EHIP_BASE = -1000
+
+HEADS, HEAD_DIM, V_DIM = 16, 576, 512
+ROW_BYTES = HEAD_DIM * 2
+KERNEL_NAMES = ("diff_lru", "hit_gather", "miss_fetch", "attention", "combine")
+
+# Every exported symbol of include/kvs.h.
+EXPORTS = (
+    "kvs_query_sizes", "kvs_host_alloc", "kvs_host_free", "kvs_create_pool", "kvs_publish",
+    "kvs_step", "kvs_free_request", "kvs_sync_status", "kvs_debug_read_state",
+    "kvs_profile_begin", "kvs_profile_end", "kvs_release", "kvs_strerror",
+)
+
+
+class kvs_config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("layers", ctypes.c_int32), ("context", ctypes.c_int64),
+        ("slots", ctypes.c_int32), ("topk", ctypes.c_int32), ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("attn_splits", ctypes.c_int32), ("flags", ctypes.c_int32),
+    ]
+
+
+class kvs_sizes(ctypes.Structure):
+    _fields_ = [
+        ("host_pool_bytes", ctypes.c_uint64), ("hot_bytes", ctypes.c_uint64),
+        ("meta_bytes", ctypes.c_uint64), ("cbuf_bytes", ctypes.c_uint64),
+        ("scratch_bytes", ctypes.c_uint64), ("attn_splits", ctypes.c_int32),
+    ]
+
+
+class kvs_buffers(ctypes.Structure):
+    _fields_ = [
+        ("host_pool", ctypes.c_void_p), ("hot", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+        ("cbuf", ctypes.c_void_p), ("scratch", ctypes.c_void_p),
+        ("host_pool_bytes", ctypes.c_uint64), ("hot_bytes", ctypes.c_uint64),
+        ("meta_bytes", ctypes.c_uint64), ("cbuf_bytes", ctypes.c_uint64),
+        ("scratch_bytes", ctypes.c_uint64),
+    ]
+
+
+class kvs_step_stats(ctypes.Structure):
+    _fields_ = [
+        ("unit_steps", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
+        ("evictions", ctypes.c_int64), ("host_bytes", ctypes.c_int64), ("status", ctypes.c_int32),
+    ]
+
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+class kvs_unit_state(ctypes.Structure):
+    _fields_ = [
+        ("tok2slot", _I32P), ("slot2tok", _I32P), ("last_used", _I32P), ("lru_order", _I32P),
+        ("slot_of", _I32P), ("miss_pos", _I32P), ("victims", _I32P), ("evicted", _I32P),
+        ("counts", _I32P), ("step", ctypes.c_int32),
+    ]
+
+
+class kvs_kernel_times(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int32), ("ms_total", ctypes.c_float * len(KERNEL_NAMES))]
+
+
+class KvsError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvs.so (built by ``__graft_entry__.build()``); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python -m token_level_gather_amd._build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    sig = {
+        "kvs_query_sizes": [ctypes.POINTER(kvs_config), ctypes.POINTER(kvs_sizes)],
+        "kvs_host_alloc": [u64, ctypes.POINTER(vp)],
+        "kvs_host_free": [vp],
+        "kvs_create_pool": [ctypes.POINTER(kvs_config), ctypes.POINTER(kvs_buffers), vp,
+                            ctypes.POINTER(vp)],
+        "kvs_publish": [vp, i32, i32, i64, i64, vp],
+        "kvs_step": [vp, i32, vp, vp, vp, vp, vp],
+        "kvs_free_request": [vp, i32, vp],
+        "kvs_sync_status": [vp, vp, ctypes.POINTER(kvs_step_stats)],
+        "kvs_debug_read_state": [vp, i32, i32, vp, ctypes.POINTER(kvs_unit_state)],
+        "kvs_profile_begin": [vp, i32],
+        "kvs_profile_end": [vp, ctypes.POINTER(kvs_kernel_times)],
+        "kvs_release": [vp],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.kvs_strerror.argtypes = [ctypes.c_int]
+    L.kvs_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def strerror(code: int) -> str:
+    return lib().kvs_strerror(int(code)).decode()
+
+
+def _check(rc: int, what: str) -> int:
+    if rc != KVS_OK:
+        raise KvsError(rc, what)
+    return rc
+
+
+def make_config(batch, layers, context, slots, topk, scale=None, attn_splits=0, flags=0,
+                heads=HEADS, head_dim=HEAD_DIM, v_dim=V_DIM) -> kvs_config:
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(head_dim))
+    return kvs_config(batch, layers, context, slots, topk, heads, head_dim, v_dim, scale,
+                      attn_splits, flags)
+
+
+def query_sizes(cfg: kvs_config) -> kvs_sizes:
+    out = kvs_sizes()
+    _check(lib().kvs_query_sizes(ctypes.byref(cfg), ctypes.byref(out)), "kvs_query_sizes")
+    return out
+
+
+class HostPool:
+    """Pinned host memory from kvs_host_alloc, viewed as numpy uint16 [B][L][N][576]."""
+
+    def __init__(self, batch, layers, context):
+        self.shape = (batch, layers, context, HEAD_DIM)
+        self.nbytes = batch * layers * context * ROW_BYTES
+        ptr = ctypes.c_void_p()
+        _check(lib().kvs_host_alloc(self.nbytes, ctypes.byref(ptr)), "kvs_host_alloc")
+        self.ptr = ptr.value
+        buf = (ctypes.c_uint16 * (self.nbytes // 2)).from_address(self.ptr)
+        self.array = np.ctypeslib.as_array(buf).reshape(self.shape)
+
+    def free(self):
+        if self.ptr:
+            self.array = None
+            lib().kvs_host_free(self.ptr)
+            self.ptr = None
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class Pool:
+    """One pool of B requests x L layers: hot buffers, maps and the host pool.
+
+    Device buffers are torch tensors on the current HIP device; the host pool
+    is pinned memory from kvs_host_alloc (``self.host.array`` is its numpy
+    view).  ``step`` enqueues one layer's fetch + write-back + attention.
+    """
+
+    def __init__(self, batch, layers, context, slots, topk, scale=None, attn_splits=0,
+                 host: Optional[HostPool] = None, device=None, stream=None):
+        import torch
+        self.cfg = make_config(batch, layers, context, slots, topk, scale, attn_splits)
+        self.sizes = query_sizes(self.cfg)
+        self.B, self.L, self.N, self.S, self.K = batch, layers, context, slots, topk
+        self.device = torch.device("cuda" if device is None else device)
+        self.host = host if host is not None else HostPool(batch, layers, context)
+        if self.host.nbytes < self.sizes.host_pool_bytes:
+            raise KvsError(KVS_ENOMEM, "host pool")
+
+        def dev(nbytes):
+            return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+
+        self.hot = dev(self.sizes.hot_bytes)
+        self.meta = dev(self.sizes.meta_bytes)
+        self.cbuf = dev(self.sizes.cbuf_bytes)
+        self.scratch = dev(self.sizes.scratch_bytes)
+        bufs = kvs_buffers(self.host.ptr, self.hot.data_ptr(), self.meta.data_ptr(),
+                           self.cbuf.data_ptr(), self.scratch.data_ptr(), self.host.nbytes,
+                           self.hot.numel(), self.meta.numel(), self.cbuf.numel(),
+                           self.scratch.numel())
+        handle = ctypes.c_void_p()
+        _check(lib().kvs_create_pool(ctypes.byref(self.cfg), ctypes.byref(bufs),
+                                     _stream_ptr(stream), ctypes.byref(handle)),
+               "kvs_create_pool")
+        self.handle = handle
+
+    # -- lifecycle --------------------------------------------------------
+    def publish(self, req, layer, first_tok, rows: np.ndarray):
+        rows = np.ascontiguousarray(rows, dtype=np.uint16)
+        assert rows.ndim == 2 and rows.shape[1] == HEAD_DIM
+        _check(lib().kvs_publish(self.handle, req, layer, first_tok, rows.shape[0],
+                                 rows.ctypes.data), "kvs_publish")
+
+    def step(self, layer, topk, q, out, lse=None, stream=None):
+        """topk [B][K] int32, q [B][16][576] bf16/uint16, out [B][16][512] bf16 (device)."""
+        self._check_dev(topk, (self.B, self.K), 4)
+        self._check_dev(q, (self.B, HEADS, HEAD_DIM), 2)
+        self._check_dev(out, (self.B, HEADS, V_DIM), 2)
+        lse_ptr = None
+        if lse is not None:
+            self._check_dev(lse, (self.B, HEADS), 4)
+            lse_ptr = lse.data_ptr()
+        _check(lib().kvs_step(self.handle, layer, topk.data_ptr(), q.data_ptr(), out.data_ptr(),
+                              lse_ptr, _stream_ptr(stream)), "kvs_step")
+
+    def free_request(self, req, stream=None):
+        _check(lib().kvs_free_request(self.handle, req, _stream_ptr(stream)), "kvs_free_request")
+
+    def sync_status(self, stream=None):
+        """Returns (status code, kvs_step_stats); the status is cleared."""
+        st = kvs_step_stats()
+        rc = lib().kvs_sync_status(self.handle, _stream_ptr(stream), ctypes.byref(st))
+        if rc not in (KVS_OK, KVS_ERANGE, KVS_EDUP):
+            raise KvsError(rc, "kvs_sync_status")
+        return rc, st
+
+    def read_state(self, req, layer, stream=None) -> dict:
+        arr = {
+            "tok2slot": np.empty(self.N, np.int32), "slot2tok": np.empty(self.S, np.int32),
+            "last_used": np.empty(self.S, np.int32), "lru_order": np.empty(self.S, np.int32),
+            "slot_of": np.empty(self.K, np.int32), "miss_pos": np.empty(self.K, np.int32),
+            "victims": np.empty(self.K, np.int32), "evicted": np.empty(self.K, np.int32),
+            "counts": np.empty(4, np.int32),
+        }
+        st = kvs_unit_state(*[a.ctypes.data_as(_I32P) for a in arr.values()], 0)
+        _check(lib().kvs_debug_read_state(self.handle, req, layer, _stream_ptr(stream),
+                                          ctypes.byref(st)), "kvs_debug_read_state")
+        arr["step"] = int(st.step)
+        return arr
+
+    def profile_begin(self, max_steps):
+        _check(lib().kvs_profile_begin(self.handle, max_steps), "kvs_profile_begin")
+
+    def profile_end(self) -> dict:
+        t = kvs_kernel_times()
+        _check(lib().kvs_profile_end(self.handle, ctypes.byref(t)), "kvs_profile_end")
+        return {"steps": t.steps, **{n: t.ms_total[i] for i, n in enumerate(KERNEL_NAMES)}}
+
+    def release(self):
+        if self.handle:
+            _check(lib().kvs_release(self.handle), "kvs_release")
+            self.handle = None
+
+    # -- helpers ----------------------------------------------------------
+    def _check_dev(self, t, shape, itemsize):
+        if not t.is_cuda or tuple(t.shape) != shape or t.element_size() != itemsize \
+                or not t.is_contiguous():
+            raise ValueError(f"expected a contiguous device tensor {shape} of {itemsize}-byte "
+                             f"elements, got {tuple(t.shape)} {t.dtype} on {t.device}")

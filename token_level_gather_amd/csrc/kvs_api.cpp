@@ -1,0 +1,397 @@
+// Host runtime behind the C ABI in include/kvs.h: configuration and buffer
+// validation, host-pool allocation, launch orchestration of one decode step on
+// the caller's stream plus one internal stream (fork/join by events), status
+// and statistics readback, and per-kernel event timing.
+//
+// The request lifecycle follows "XM-Sparse" (HiSparse integration section):
+// publish = kvs_publish, fetch + write-back = kvs_step, free = kvs_free_request.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "kvs_internal.h"
+
+namespace kvs {
+
+static uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+int make_layout(const kvs_config* c, Layout* lay) {
+  if (c == nullptr || lay == nullptr) return KVS_EINVAL;
+  if (c->batch < 1 || c->batch > 65535 || c->layers < 1) return KVS_EINVAL;
+  if (c->topk < 1 || c->topk > KVS_MAX_TOPK) return KVS_EINVAL;
+  if (c->slots < c->topk || c->slots > KVS_MAX_SLOTS) return KVS_EINVAL;
+  if (c->context < c->topk || c->context > 0x7fffffffLL) return KVS_EINVAL;
+  if (c->heads != KVS_HEADS || c->head_dim != KVS_HEAD_DIM || c->v_dim != KVS_V_DIM)
+    return KVS_EINVAL;
+  if (!(c->scale > 0.f) || !isfinite(c->scale)) return KVS_EINVAL;
+  if (c->attn_splits < 0 || c->attn_splits > 64 || c->flags != 0) return KVS_EINVAL;
+  if ((int64_t)c->batch * c->layers > 0x7fffffffLL) return KVS_EINVAL;
+
+  const uint64_t B = c->batch, L = c->layers, N = c->context, S = c->slots, K = c->topk;
+  const uint64_t U = B * L;
+  const int ntiles = (int)((K + 63) / 64);
+  int splits = c->attn_splits;
+  if (splits == 0) {
+    // about two attention workgroups per compute unit (256 CUs), at least one tile each
+    splits = (int)((512 + B - 1) / B);
+    if (splits > ntiles) splits = ntiles;
+    if (splits > 64) splits = 64;
+    if (splits < 1) splits = 1;
+  } else if (splits > ntiles) {
+    return KVS_EINVAL;
+  }
+
+  lay->B = c->batch;
+  lay->L = c->layers;
+  lay->S = c->slots;
+  lay->K = c->topk;
+  lay->N = c->context;
+  lay->splits = splits;
+
+  uint64_t o = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  lay->tok2slot = take(U * N * 4);
+  lay->slot2tok = take(U * S * 4);
+  lay->last_used = take(U * S * 4);
+  lay->order = take(U * S * 2);
+  lay->stepctr = take(U * 4);
+  lay->stats = take(U * 4 * 8);
+  lay->status = take(16);
+  lay->meta_bytes = o;
+
+  o = 0;
+  lay->slot_of = take(B * K * 4);
+  lay->miss_pos = take(B * K * 4);
+  lay->victims = take(B * K * 4);
+  lay->evicted = take(B * K * 4);
+  lay->counts = take(B * 16);
+  lay->part_o = take(B * (uint64_t)splits * kHeads * kVDim * 4);
+  lay->part_ml = take(B * (uint64_t)splits * kHeads * 2 * 4);
+  lay->scratch_bytes = o;
+  return KVS_OK;
+}
+
+}  // namespace kvs
+
+using namespace kvs;
+
+struct kvs_pool {
+  kvs_config cfg;
+  Layout lay;
+  DevPtrs d;
+  uint8_t* host_pool;       // host address of the pool (for kvs_publish)
+  int device;
+  hipStream_t side;         // miss fetch runs here, beside the hit gather
+  hipEvent_t ev_fork, ev_join;
+  // per-kernel timing: events [max_steps][KVS_NUM_KERNELS][2]
+  std::vector<hipEvent_t> prof_ev;
+  int prof_max;
+  int prof_n;
+};
+
+static int hip_err(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP_BASE - (int)e; }
+
+#define KVS_TRY_HIP(expr)                       \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_err(e_);   \
+  } while (0)
+
+static hipEvent_t* prof_slot(kvs_pool* p, int kernel) {
+  if (p->prof_n >= p->prof_max) return nullptr;
+  return &p->prof_ev[((size_t)p->prof_n * KVS_NUM_KERNELS + kernel) * 2];
+}
+
+// Launch `fn` on `s`, bracketed by timing events when profiling.
+template <typename F>
+static hipError_t timed(kvs_pool* p, int kernel, hipStream_t s, F fn) {
+  hipEvent_t* ev = prof_slot(p, kernel);
+  if (ev != nullptr) {
+    hipError_t e = hipEventRecord(ev[0], s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = fn();
+  if (e == hipSuccess && ev != nullptr) e = hipEventRecord(ev[1], s);
+  return e;
+}
+
+extern "C" {
+
+int kvs_query_sizes(const kvs_config* cfg, kvs_sizes* out) {
+  if (out == nullptr) return KVS_EINVAL;
+  Layout lay;
+  const int rc = make_layout(cfg, &lay);
+  if (rc != KVS_OK) return rc;
+  const uint64_t B = cfg->batch, L = cfg->layers, N = cfg->context, S = cfg->slots,
+                 K = cfg->topk;
+  out->host_pool_bytes = B * L * N * kRowBytes;
+  out->hot_bytes = B * L * S * kRowBytes;
+  out->meta_bytes = lay.meta_bytes;
+  out->cbuf_bytes = B * K * kRowBytes;
+  out->scratch_bytes = lay.scratch_bytes;
+  out->attn_splits = lay.splits;
+  return KVS_OK;
+}
+
+int kvs_host_alloc(uint64_t bytes, void** out) {
+  if (out == nullptr || bytes == 0) return KVS_EINVAL;
+  *out = nullptr;
+  // Pinned, mapped into the GPU's address space at the same address.  The
+  // pool is read by GPU kernels over PCIe and written only by the host while
+  // no step is in flight, so coarse-grained (non-coherent) memory suffices;
+  // KVS_HOST_COHERENT=1 selects fine-grained memory instead.
+  unsigned flags = hipHostMallocMapped | hipHostMallocPortable;
+  const char* coh = getenv("KVS_HOST_COHERENT");
+  flags |= (coh != nullptr && coh[0] == '1') ? hipHostMallocCoherent : hipHostMallocNonCoherent;
+  void* p = nullptr;
+  const hipError_t e = hipHostMalloc(&p, (size_t)bytes, flags);
+  if (e != hipSuccess) return hip_err(e);
+  *out = p;
+  return KVS_OK;
+}
+
+int kvs_host_free(void* ptr) {
+  if (ptr == nullptr) return KVS_EINVAL;
+  return hip_err(hipHostFree(ptr));
+}
+
+int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream,
+                    kvs_pool** out) {
+  if (out == nullptr || bufs == nullptr) return KVS_EINVAL;
+  *out = nullptr;
+  kvs_sizes need;
+  int rc = kvs_query_sizes(cfg, &need);
+  if (rc != KVS_OK) return rc;
+  if (bufs->host_pool == nullptr || bufs->hot == nullptr || bufs->meta == nullptr ||
+      bufs->cbuf == nullptr || bufs->scratch == nullptr)
+    return KVS_EINVAL;
+  if (bufs->host_pool_bytes < need.host_pool_bytes || bufs->hot_bytes < need.hot_bytes ||
+      bufs->meta_bytes < need.meta_bytes || bufs->cbuf_bytes < need.cbuf_bytes ||
+      bufs->scratch_bytes < need.scratch_bytes)
+    return KVS_ENOMEM;
+  const uintptr_t mis = (uintptr_t)bufs->host_pool | (uintptr_t)bufs->hot |
+                        (uintptr_t)bufs->cbuf;
+  if ((mis & 15) != 0 || ((uintptr_t)bufs->meta & 255) != 0 ||
+      ((uintptr_t)bufs->scratch & 255) != 0)
+    return KVS_EINVAL;
+
+  // the pool must be pinned host memory the GPU can address
+  void* pool_dev = nullptr;
+  if (hipHostGetDevicePointer(&pool_dev, const_cast<void*>(bufs->host_pool), 0) != hipSuccess ||
+      pool_dev == nullptr) {
+    (void)hipGetLastError();
+    return KVS_EINVAL;
+  }
+
+  kvs_pool* p = new (std::nothrow) kvs_pool();
+  if (p == nullptr) return KVS_ENOMEM;
+  p->cfg = *cfg;
+  make_layout(cfg, &p->lay);
+  p->prof_max = 0;
+  p->prof_n = 0;
+  p->host_pool = (uint8_t*)const_cast<void*>(bufs->host_pool);
+
+  uint8_t* meta = (uint8_t*)bufs->meta;
+  uint8_t* scr = (uint8_t*)bufs->scratch;
+  const Layout& L = p->lay;
+  DevPtrs& d = p->d;
+  d.pool = (const uint16_t*)pool_dev;
+  d.hot = (uint16_t*)bufs->hot;
+  d.cbuf = (uint16_t*)bufs->cbuf;
+  d.tok2slot = (int32_t*)(meta + L.tok2slot);
+  d.slot2tok = (int32_t*)(meta + L.slot2tok);
+  d.last_used = (int32_t*)(meta + L.last_used);
+  d.order = (uint16_t*)(meta + L.order);
+  d.stepctr = (int32_t*)(meta + L.stepctr);
+  d.stats = (long long*)(meta + L.stats);
+  d.status = (int32_t*)(meta + L.status);
+  d.slot_of = (int32_t*)(scr + L.slot_of);
+  d.miss_pos = (int32_t*)(scr + L.miss_pos);
+  d.victims = (int32_t*)(scr + L.victims);
+  d.evicted = (int32_t*)(scr + L.evicted);
+  d.counts = (int32_t*)(scr + L.counts);
+  d.part_o = (float*)(scr + L.part_o);
+  d.part_ml = (float*)(scr + L.part_ml);
+
+  hipError_t e = hipGetDevice(&p->device);
+  if (e == hipSuccess) e = prepare_kernels();
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess)
+    e = launch_init_units(L, d, 0, L.B * L.L, /*reset_counters=*/true, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_err(e);
+  }
+  *out = p;
+  return KVS_OK;
+}
+
+int kvs_publish(kvs_pool* p, int32_t req, int32_t layer, int64_t first_tok, int64_t n_tok,
+                const void* rows) {
+  if (p == nullptr || rows == nullptr) return KVS_EINVAL;
+  if (req < 0 || req >= p->lay.B || layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
+  if (first_tok < 0 || n_tok < 0 || first_tok + n_tok > p->lay.N) return KVS_EINVAL;
+  const uint64_t row0 = ((uint64_t)req * p->lay.L + layer) * (uint64_t)p->lay.N + first_tok;
+  memcpy(p->host_pool + row0 * kRowBytes, rows, (size_t)n_tok * kRowBytes);
+  return KVS_OK;
+}
+
+int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, void* out,
+             float* lse, void* stream) {
+  if (p == nullptr || topk == nullptr || q == nullptr || out == nullptr) return KVS_EINVAL;
+  if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
+  const hipStream_t s = (hipStream_t)stream;
+  const Layout& L = p->lay;
+  const DevPtrs& d = p->d;
+  KVS_TRY_HIP(timed(p, KVS_KERNEL_DIFF_LRU, s, [&] { return launch_diff_lru(L, d, layer, topk, s); }));
+  KVS_TRY_HIP(hipEventRecord(p->ev_fork, s));
+  KVS_TRY_HIP(hipStreamWaitEvent(p->side, p->ev_fork, 0));
+  KVS_TRY_HIP(timed(p, KVS_KERNEL_MISS_FETCH, p->side,
+                    [&] { return launch_miss_fetch(L, d, layer, topk, p->side); }));
+  KVS_TRY_HIP(hipEventRecord(p->ev_join, p->side));
+  KVS_TRY_HIP(timed(p, KVS_KERNEL_HIT_GATHER, s, [&] { return launch_hit_gather(L, d, layer, s); }));
+  KVS_TRY_HIP(hipStreamWaitEvent(s, p->ev_join, 0));
+  KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s,
+                    [&] { return launch_attention(L, d, (const uint16_t*)q, p->cfg.scale, s); }));
+  KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
+                    [&] { return launch_combine(L, d, (uint16_t*)out, lse, s); }));
+  if (p->prof_n < p->prof_max) ++p->prof_n;
+  return KVS_OK;
+}
+
+int kvs_free_request(kvs_pool* p, int32_t req, void* stream) {
+  if (p == nullptr || req < 0 || req >= p->lay.B) return KVS_EINVAL;
+  KVS_TRY_HIP(hipStreamWaitEvent((hipStream_t)stream, p->ev_join, 0));
+  return hip_err(launch_init_units(p->lay, p->d, req * p->lay.L, p->lay.L, false,
+                                   (hipStream_t)stream));
+}
+
+int kvs_sync_status(kvs_pool* p, void* stream, kvs_step_stats* stats) {
+  if (p == nullptr) return KVS_EINVAL;
+  const hipStream_t s = (hipStream_t)stream;
+  KVS_TRY_HIP(hipStreamSynchronize(p->side));
+  KVS_TRY_HIP(hipStreamSynchronize(s));
+  int32_t status[4];
+  KVS_TRY_HIP(hipMemcpyAsync(status, p->d.status, sizeof(status), hipMemcpyDeviceToHost, s));
+  if (stats != nullptr) {
+    const size_t units = (size_t)p->lay.B * p->lay.L;
+    std::vector<long long> st(units * 4);
+    KVS_TRY_HIP(hipMemcpyAsync(st.data(), p->d.stats, st.size() * sizeof(long long),
+                               hipMemcpyDeviceToHost, s));
+    KVS_TRY_HIP(hipStreamSynchronize(s));
+    memset(stats, 0, sizeof(*stats));
+    for (size_t u = 0; u < units; ++u) {
+      stats->unit_steps += st[4 * u + 0];
+      stats->hits += st[4 * u + 1];
+      stats->misses += st[4 * u + 2];
+      stats->evictions += st[4 * u + 3];
+    }
+    stats->host_bytes = stats->misses * kRowBytes;
+    stats->status = status[0];
+  }
+  KVS_TRY_HIP(hipStreamSynchronize(s));
+  if (status[0] != 0) {
+    KVS_TRY_HIP(launch_clear_status(p->d, s));
+    KVS_TRY_HIP(hipStreamSynchronize(s));
+  }
+  return status[0];
+}
+
+int kvs_debug_read_state(kvs_pool* p, int32_t req, int32_t layer, void* stream,
+                         kvs_unit_state* st) {
+  if (p == nullptr || st == nullptr) return KVS_EINVAL;
+  if (req < 0 || req >= p->lay.B || layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
+  const hipStream_t s = (hipStream_t)stream;
+  const Layout& L = p->lay;
+  const DevPtrs& d = p->d;
+  const long long u = (long long)req * L.L + layer;
+  KVS_TRY_HIP(hipStreamSynchronize(p->side));
+  auto get = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
+    if (dst == nullptr) return hipSuccess;
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
+  };
+  KVS_TRY_HIP(get(st->tok2slot, d.tok2slot + u * L.N, (size_t)L.N * 4));
+  KVS_TRY_HIP(get(st->slot2tok, d.slot2tok + u * L.S, (size_t)L.S * 4));
+  KVS_TRY_HIP(get(st->last_used, d.last_used + u * L.S, (size_t)L.S * 4));
+  KVS_TRY_HIP(get(st->slot_of, d.slot_of + (long long)req * L.K, (size_t)L.K * 4));
+  KVS_TRY_HIP(get(st->miss_pos, d.miss_pos + (long long)req * L.K, (size_t)L.K * 4));
+  KVS_TRY_HIP(get(st->victims, d.victims + (long long)req * L.K, (size_t)L.K * 4));
+  KVS_TRY_HIP(get(st->evicted, d.evicted + (long long)req * L.K, (size_t)L.K * 4));
+  KVS_TRY_HIP(get(st->counts, d.counts + 4LL * req, 16));
+  std::vector<uint16_t> order(st->lru_order ? L.S : 0);
+  KVS_TRY_HIP(get(st->lru_order ? order.data() : nullptr, d.order + u * L.S, (size_t)L.S * 2));
+  int32_t step = 0;
+  KVS_TRY_HIP(get(&step, d.stepctr + u, 4));
+  KVS_TRY_HIP(hipStreamSynchronize(s));
+  if (st->lru_order)
+    for (int i = 0; i < L.S; ++i) st->lru_order[i] = order[i];
+  st->step = step;
+  return KVS_OK;
+}
+
+int kvs_profile_begin(kvs_pool* p, int32_t max_steps) {
+  if (p == nullptr || max_steps < 0) return KVS_EINVAL;
+  const size_t need = (size_t)max_steps * KVS_NUM_KERNELS * 2;
+  while (p->prof_ev.size() < need) {
+    hipEvent_t e;
+    KVS_TRY_HIP(hipEventCreate(&e));
+    p->prof_ev.push_back(e);
+  }
+  p->prof_max = max_steps;
+  p->prof_n = 0;
+  return KVS_OK;
+}
+
+int kvs_profile_end(kvs_pool* p, kvs_kernel_times* out) {
+  if (p == nullptr || out == nullptr) return KVS_EINVAL;
+  memset(out, 0, sizeof(*out));
+  const int n = p->prof_n;
+  p->prof_max = 0;   // stop recording
+  for (int i = 0; i < n; ++i) {
+    for (int k = 0; k < KVS_NUM_KERNELS; ++k) {
+      hipEvent_t* ev = &p->prof_ev[((size_t)i * KVS_NUM_KERNELS + k) * 2];
+      KVS_TRY_HIP(hipEventSynchronize(ev[1]));
+      float ms = 0.f;
+      KVS_TRY_HIP(hipEventElapsedTime(&ms, ev[0], ev[1]));
+      out->ms_total[k] += ms;
+    }
+  }
+  out->steps = n;
+  p->prof_n = 0;
+  return KVS_OK;
+}
+
+int kvs_release(kvs_pool* p) {
+  if (p == nullptr) return KVS_EINVAL;
+  hipError_t e = hipStreamSynchronize(p->side);
+  for (hipEvent_t ev : p->prof_ev) (void)hipEventDestroy(ev);
+  (void)hipEventDestroy(p->ev_fork);
+  (void)hipEventDestroy(p->ev_join);
+  (void)hipStreamDestroy(p->side);
+  delete p;
+  return hip_err(e);
+}
+
+const char* kvs_strerror(int code) {
+  switch (code) {
+    case KVS_OK: return "ok";
+    case KVS_EINVAL: return "invalid argument or configuration";
+    case KVS_ENOMEM: return "buffer smaller than kvs_query_sizes requires";
+    case KVS_ERANGE: return "Top-K index outside [0, context)";
+    case KVS_EDUP: return "duplicate Top-K index within a request";
+    default: break;
+  }
+  if (code <= KVS_EHIP_BASE) return "HIP runtime error (KVS_EHIP_BASE - hipError_t)";
+  return "unknown error";
+}
+
+}  // extern "C"

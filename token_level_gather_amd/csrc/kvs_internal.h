@@ -1,0 +1,86 @@
+// Internal layout and launch interfaces shared by the host runtime and the
+// gfx950 kernels of the sparse KV assembly library.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvs.h"
+
+namespace kvs {
+
+constexpr int kRowElems = KVS_HEAD_DIM;          // 576 bf16 per KV row
+constexpr int kRowBytes = kRowElems * 2;         // 1152
+constexpr int kRowChunks = kRowBytes / 16;       // 72 x 16-byte chunks per row
+constexpr int kHeads = KVS_HEADS;                // 16
+constexpr int kVDim = KVS_V_DIM;                 // 512
+
+// Byte offsets of every array inside the caller's meta and scratch buffers.
+struct Layout {
+  int32_t B, L, S, K, splits;
+  int64_t N;
+  // meta (persistent state)
+  uint64_t tok2slot;   // int32 [B*L][N]
+  uint64_t slot2tok;   // int32 [B*L][S]
+  uint64_t last_used;  // int32 [B*L][S]
+  uint64_t order;      // uint16 [B*L][S]: slots in ascending (last_used, slot)
+  uint64_t stepctr;    // int32 [B*L]
+  uint64_t stats;      // int64 [B*L][4]: steps, hits, misses, evictions
+  uint64_t status;     // int32 [4]: sticky first error
+  uint64_t meta_bytes;
+  // scratch (per kvs_step call; request-indexed, reused across layers)
+  uint64_t slot_of;    // int32 [B][K]
+  uint64_t miss_pos;   // int32 [B][K]
+  uint64_t victims;    // int32 [B][K]
+  uint64_t evicted;    // int32 [B][K]
+  uint64_t counts;     // int32 [B][4]: n_hit, n_miss, n_evict, valid
+  uint64_t part_o;     // float [B][splits][16][512]
+  uint64_t part_ml;    // float [B][splits][16][2]: running max (log2 units), sum
+  uint64_t scratch_bytes;
+};
+
+// Validates cfg and fills `lay`; returns KVS_OK or KVS_EINVAL.
+int make_layout(const kvs_config* cfg, Layout* lay);
+
+// Dynamic LDS bytes of the diff/LRU kernel for a layout.
+size_t diff_lds_bytes(int S, int K);
+
+// Device pointers of one pool, resolved from the caller's buffers.
+struct DevPtrs {
+  const uint16_t* pool;  // host pool, device-visible address
+  uint16_t* hot;
+  uint16_t* cbuf;
+  int32_t* tok2slot;
+  int32_t* slot2tok;
+  int32_t* last_used;
+  uint16_t* order;
+  int32_t* stepctr;
+  long long* stats;
+  int32_t* status;
+  int32_t* slot_of;
+  int32_t* miss_pos;
+  int32_t* victims;
+  int32_t* evicted;
+  int32_t* counts;
+  float* part_o;
+  float* part_ml;
+};
+
+// Kernel launchers (kvs_kernels.hip).  Each returns the launch's hipError_t.
+// prepare_kernels sets per-kernel attributes on the current device (once per pool).
+hipError_t prepare_kernels();
+hipError_t launch_init_units(const Layout& lay, const DevPtrs& d, int unit_begin,
+                             int unit_count, bool reset_counters, hipStream_t s);
+hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer,
+                           const int32_t* topk, hipStream_t s);
+hipError_t launch_hit_gather(const Layout& lay, const DevPtrs& d, int layer,
+                             hipStream_t s);
+hipError_t launch_miss_fetch(const Layout& lay, const DevPtrs& d, int layer,
+                             const int32_t* topk, hipStream_t s);
+hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t* q,
+                            float scale, hipStream_t s);
+hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out,
+                          float* lse, hipStream_t s);
+hipError_t launch_clear_status(const DevPtrs& d, hipStream_t s);
+
+}  // namespace kvs

@@ -1,0 +1,706 @@
+// gfx950 (MI355X) kernels of the per-decode-step sparse KV assembly path.
+//
+// One kvs_step of layer l runs, for the B units (b, l):
+//   diff_lru    one workgroup per unit: slot lookup + validation, sparse diff
+//               (misses compacted in Top-K order with wave ballots and a
+//               workgroup prefix sum), hit touch, LRU victim choice from an
+//               LDS copy of the unit's LRU order array, map update.
+//   hit_gather  hot buffer -> compute buffer for the hits (HBM to HBM).
+//   miss_fetch  host pool -> compute buffer and hot buffer for the misses,
+//               by direct loads from pinned host memory over PCIe.
+//   attention   split-K sparse MLA decode over the K gathered rows:
+//               v_mfma_f32_16x16x32_bf16 for Q.K^T and P.V, fp32 online softmax.
+//   combine     merges the split partials, writes bf16 out and fp32 lse.
+//
+// Passages: index mapping / host pool / device cache / index-copy assembly
+// ("Sparse Attention-Driven KVCache Management for Domestic AI Supernodes",
+// abstract and agenda); Top-k LRU buffer, Sparse Diff Kernel and Top-k
+// attention (SGLang/Tair hierarchical sparse attention summary, paragraphs
+// 1-3).
+#include <math.h>
+
+#include "kvs_internal.h"
+
+namespace kvs {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
+
+__device__ __forceinline__ unsigned long long lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;   // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ------------------------------------------------------------------ init
+// Empties units [u0, u0 + count): maps -1, last_used -1, LRU order 0..S-1.
+__global__ void init_units_kernel(int32_t* tok2slot, int32_t* slot2tok, int32_t* last_used,
+                                  uint16_t* order, long long n_tok, long long n_slot, int S) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  const long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (long long i = i0; i < n_tok; i += stride) tok2slot[i] = -1;
+  for (long long i = i0; i < n_slot; i += stride) {
+    slot2tok[i] = -1;
+    last_used[i] = -1;
+    order[i] = (uint16_t)(i % S);
+  }
+}
+
+__global__ void reset_counters_kernel(int32_t* stepctr, long long* stats, int32_t* status,
+                                      int units) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < units) {
+    stepctr[i] = 0;
+    stats[4 * i + 0] = 0;
+    stats[4 * i + 1] = 0;
+    stats[4 * i + 2] = 0;
+    stats[4 * i + 3] = 0;
+  }
+  if (i < 4) status[i] = 0;
+}
+
+__global__ void clear_status_kernel(int32_t* status) {
+  if (threadIdx.x < 4) status[threadIdx.x] = 0;
+}
+
+// ------------------------------------------------------------------ diff + LRU
+constexpr int kDiffThreads = 1024;
+constexpr int kDiffWaves = kDiffThreads / 64;
+constexpr int kDiffItems = KVS_MAX_TOPK / kDiffThreads;   // Top-K entries per thread
+
+struct DiffArgs {
+  const int32_t* topk;     // [B][K]
+  int32_t* tok2slot;       // [B*L][N]
+  int32_t* slot2tok;       // [B*L][S]
+  int32_t* last_used;      // [B*L][S]
+  uint16_t* order;         // [B*L][S]
+  int32_t* stepctr;        // [B*L]
+  long long* stats;        // [B*L][4]
+  int32_t* status;
+  int32_t* slot_of;        // [B][K]
+  int32_t* miss_pos;       // [B][K]
+  int32_t* victims;        // [B][K]
+  int32_t* evicted;        // [B][K]
+  int32_t* counts;         // [B][4]
+  long long N;
+  int S, K, L, layer, hash_bits;
+};
+
+// Rank of this thread among the threads of the workgroup whose `pred` holds,
+// counted in thread order; `total` receives the number of such threads.
+// Must be reached by every thread of the workgroup.
+__device__ __forceinline__ int wg_rank(bool pred, int* wtot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long m = __ballot(pred);
+  const int in_wave = __popcll(m & lanemask_lt());
+  if (lane == 0) wtot[wave] = __popcll(m);
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kDiffWaves; ++w) {
+    const int v = wtot[w];
+    off += (w < wave) ? v : 0;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return off + in_wave;
+}
+
+__global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int wtot[kDiffWaves];
+  __shared__ int err_bits;
+  __shared__ int n_evict;
+
+  const int S = a.S, K = a.K;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const long long u = (long long)b * a.L + a.layer;
+  const int H = 1 << a.hash_bits;
+
+  // LDS: LRU order copy [S] u16 | per-slot flag [S] u8 (1 = hit, 2 = victim) |
+  //      token hash set [H] i32, reused after validation as miss list [K] + victims [K]
+  uint16_t* ord = reinterpret_cast<uint16_t*>(smem);
+  uint8_t* flag = smem + ((S * 2 + 15) & ~15);
+  int32_t* hash = reinterpret_cast<int32_t*>(smem + ((S * 2 + 15) & ~15) + ((S + 15) & ~15));
+  int32_t* lmiss = hash;
+  int32_t* lvict = hash + K;
+
+  int32_t* tok2slot = a.tok2slot + u * a.N;
+  int32_t* slot2tok = a.slot2tok + u * S;
+  int32_t* lu = a.last_used + u * S;
+  uint16_t* gorder = a.order + u * S;
+  const int32_t* topk = a.topk + (long long)b * K;
+  const long long bk = (long long)b * K;
+  const int t = a.stepctr[u];
+
+  for (int s = tid; s < S; s += kDiffThreads) {
+    ord[s] = gorder[s];
+    flag[s] = 0;
+  }
+  for (int h = tid; h < H; h += kDiffThreads) hash[h] = -1;
+  if (tid == 0) {
+    err_bits = 0;
+    n_evict = 0;
+  }
+  __syncthreads();
+
+  // 1. lookup + validation (range, duplicates via an LDS open-addressing set)
+  const int items = (K + kDiffThreads - 1) / kDiffThreads;
+  int my_slot[kDiffItems];
+#pragma unroll
+  for (int j = 0; j < kDiffItems; ++j) {
+    my_slot[j] = -1;
+    const int i = tid + j * kDiffThreads;
+    if (j < items && i < K) {
+      const int tok = topk[i];
+      if (tok < 0 || (long long)tok >= a.N) {
+        atomicOr(&err_bits, 1);
+      } else {
+        unsigned h = ((unsigned)tok * 2654435761u) >> (32 - a.hash_bits);
+        while (true) {
+          const int prev = atomicCAS(&hash[h], -1, tok);
+          if (prev == -1) break;
+          if (prev == tok) {
+            atomicOr(&err_bits, 2);
+            break;
+          }
+          h = (h + 1) & (unsigned)(H - 1);
+        }
+        const int s = tok2slot[tok];
+        if (s >= 0 && s < S) {
+          my_slot[j] = s;
+          flag[s] = 1;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (err_bits) {   // invalid Top-K: leave the unit untouched, latch the error
+    if (tid == 0) {
+      a.counts[4 * b + 0] = 0;
+      a.counts[4 * b + 1] = 0;
+      a.counts[4 * b + 2] = 0;
+      a.counts[4 * b + 3] = 0;
+      atomicCAS(a.status, 0, (err_bits & 1) ? KVS_ERANGE : KVS_EDUP);
+    }
+    return;
+  }
+
+  // 2. sparse diff: record slot_of, touch hits, compact misses in Top-K order
+  int running = 0;
+#pragma unroll
+  for (int j = 0; j < kDiffItems; ++j) {
+    if (j < items) {
+      const int i = tid + j * kDiffThreads;
+      const bool in = i < K;
+      const bool miss = in && my_slot[j] < 0;
+      if (in) {
+        a.slot_of[bk + i] = my_slot[j];
+        if (!miss) lu[my_slot[j]] = t;
+      }
+      int total;
+      const int r = wg_rank(miss, wtot, total);
+      if (miss) lmiss[running + r] = i;
+      running += total;
+    }
+  }
+  const int m = running;
+  const int n_hit = K - m;
+
+  // 3. victims: the first m non-hit slots of the LRU order; the other non-hit
+  //    slots keep their relative order at the front of the new order
+  running = 0;
+  for (int c = 0; c < S; c += kDiffThreads) {
+    const int p = c + tid;
+    const bool in = p < S;
+    const int s = in ? ord[p] : 0;
+    const bool nonhit = in && flag[s] == 0;
+    int total;
+    const int r = running + wg_rank(nonhit, wtot, total);
+    if (nonhit) {
+      if (r < m) {
+        lvict[r] = s;
+        flag[s] = 2;
+      } else {
+        gorder[r - m] = (uint16_t)s;
+      }
+    }
+    running += total;
+  }
+  __syncthreads();
+
+  // 4. the K touched slots (hits and victims, all stamped t) close the order,
+  //    ascending by slot
+  running = 0;
+  for (int c = 0; c < S; c += kDiffThreads) {
+    const int s = c + tid;
+    const bool touched = s < S && flag[s] != 0;
+    int total;
+    const int r = running + wg_rank(touched, wtot, total);
+    if (touched) gorder[S - K + r] = (uint16_t)s;
+    running += total;
+  }
+
+  // 5. map update: the j-th miss takes the j-th victim
+  for (int j = tid; j < m; j += kDiffThreads) {
+    const int i = lmiss[j];
+    const int tok = topk[i];
+    const int v = lvict[j];
+    const int old = slot2tok[v];
+    if (old >= 0) {
+      tok2slot[old] = -1;
+      atomicAdd(&n_evict, 1);
+    }
+    slot2tok[v] = tok;
+    tok2slot[tok] = v;
+    lu[v] = t;
+    a.miss_pos[bk + j] = i;
+    a.victims[bk + j] = v;
+    a.evicted[bk + j] = old;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    a.counts[4 * b + 0] = n_hit;
+    a.counts[4 * b + 1] = m;
+    a.counts[4 * b + 2] = n_evict;
+    a.counts[4 * b + 3] = 1;
+    a.stats[4 * u + 0] += 1;
+    a.stats[4 * u + 1] += n_hit;
+    a.stats[4 * u + 2] += m;
+    a.stats[4 * u + 3] += n_evict;
+    a.stepctr[u] = t + 1;
+  }
+}
+
+// ------------------------------------------------------------------ gathers
+constexpr int kCopyThreads = 256;
+constexpr int kCopyRows = 32;                                   // rows per block
+constexpr int kCopyItems = kCopyRows * kRowChunks / kCopyThreads;  // 9 chunks / thread
+static_assert(kCopyItems * kCopyThreads == kCopyRows * kRowChunks, "copy tiling");
+
+// Hits: cbuf[b][i] = hot[b][l][slot_of[b][i]] for every hit position i.
+__global__ __launch_bounds__(kCopyThreads) void hit_gather_kernel(
+    const u32x4* __restrict__ hot, u32x4* __restrict__ cbuf, const int32_t* __restrict__ slot_of,
+    const int32_t* __restrict__ counts, int L, int layer, int S, int K) {
+  const int b = blockIdx.y;
+  if (counts[4 * b + 3] == 0) return;
+  const long long u = (long long)b * L + layer;
+  const int i0 = blockIdx.x * kCopyRows;
+  u32x4 v[kCopyItems];
+  long long dst[kCopyItems];
+#pragma unroll
+  for (int j = 0; j < kCopyItems; ++j) {
+    const int c = j * kCopyThreads + threadIdx.x;
+    const int r = c / kRowChunks;
+    const int col = c - r * kRowChunks;
+    const int i = i0 + r;
+    dst[j] = -1;
+    if (i < K) {
+      const int s = slot_of[(long long)b * K + i];
+      if (s >= 0) {
+        v[j] = hot[(u * S + s) * kRowChunks + col];
+        dst[j] = ((long long)b * K + i) * kRowChunks + col;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCopyItems; ++j)
+    if (dst[j] >= 0) cbuf[dst[j]] = v[j];
+}
+
+// Misses: row = pool[b][l][tok_j]; cbuf[b][miss_pos_j] = row; hot[b][l][victim_j] = row.
+// The pool pointer is pinned host memory: every load crosses PCIe.
+__global__ __launch_bounds__(kCopyThreads) void miss_fetch_kernel(
+    const u32x4* __restrict__ pool, u32x4* __restrict__ hot, u32x4* __restrict__ cbuf,
+    const int32_t* __restrict__ topk, const int32_t* __restrict__ miss_pos,
+    const int32_t* __restrict__ victims, const int32_t* __restrict__ counts, int L, int layer,
+    long long N, int S, int K) {
+  const int b = blockIdx.y;
+  if (counts[4 * b + 3] == 0) return;
+  const int n = counts[4 * b + 1];
+  const int j0 = blockIdx.x * kCopyRows;
+  if (j0 >= n) return;
+  const long long u = (long long)b * L + layer;
+  const long long bk = (long long)b * K;
+  u32x4 v[kCopyItems];
+  long long dc[kCopyItems], dh[kCopyItems];
+#pragma unroll
+  for (int j = 0; j < kCopyItems; ++j) {
+    const int c = j * kCopyThreads + threadIdx.x;
+    const int r = c / kRowChunks;
+    const int col = c - r * kRowChunks;
+    const int jj = j0 + r;
+    dc[j] = -1;
+    if (jj < n) {
+      const int i = miss_pos[bk + jj];
+      const int tok = topk[bk + i];
+      v[j] = pool[(u * N + tok) * kRowChunks + col];
+      dc[j] = (bk + i) * kRowChunks + col;
+      dh[j] = (u * S + victims[bk + jj]) * kRowChunks + col;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCopyItems; ++j) {
+    if (dc[j] >= 0) {
+      cbuf[dc[j]] = v[j];
+      hot[dh[j]] = v[j];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attention
+constexpr int kAttnThreads = 256;
+constexpr int kTile = 64;                       // tokens per LDS tile (16 per wave in Q.K^T)
+constexpr int kLdsRow = kRowBytes + 16;         // padded row: 16-B aligned, spreads banks
+constexpr int kAttnItems = kTile * kRowChunks / kAttnThreads;   // 18 chunks / thread
+constexpr int kKSteps = kRowElems / 32;         // 18 MFMA k-steps over 576 dims
+constexpr int kPRow = kTile + 8;                // bf16 P row stride (144 B)
+constexpr int kMaxSplits = 64;
+static_assert(kAttnItems * kAttnThreads == kTile * kRowChunks, "attention tiling");
+
+struct AttnArgs {
+  const uint16_t* cbuf;   // [B][K][576]
+  const uint16_t* q;      // [B][16][576]
+  const int32_t* counts;  // [B][4]
+  float* part_o;          // [B][splits][16][512]
+  float* part_ml;         // [B][splits][16][2]
+  int K, splits;
+  float scale_log2;       // softmax scale * log2(e): scores are kept in log2 units
+};
+
+// One workgroup = (split sp, request b): the tiles [tb, te) of request b's
+// gathered rows.  MFMA operand layout used (v_mfma_f32_16x16x32_bf16): lane l
+// supplies row (l % 16) of A and column (l % 16) of B with 8 consecutive
+// k-values selected by l / 16; the result lane l holds rows 4*(l/16)+j,
+// column l % 16.  Both operands of each product take their k-values through
+// the same (l/16, j) -> k assignment, so the sum is over the intended k.
+__global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char kv[kTile * kLdsRow];
+  __shared__ float sc[kHeads * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t pb[kHeads * kPRow];
+  __shared__ float alpha_s[kHeads];
+
+  const int b = blockIdx.y, sp = blockIdx.x;
+  if (a.counts[4 * b + 3] == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int K = a.K;
+  const int ntiles = (K + kTile - 1) / kTile;
+  const int tb = (int)((long long)sp * ntiles / a.splits);
+  const int te = (int)((long long)(sp + 1) * ntiles / a.splits);
+  const u32x4* rows = reinterpret_cast<const u32x4*>(a.cbuf + (long long)b * K * kRowElems);
+
+  // Q as A-operand fragments: head r16, dims ks*32 + g*8 .. +7
+  bf16x8 qf[kKSteps];
+  {
+    const u32x4* qh = reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = as_bf16x8(qh[ks * 4 + g]);
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;   // per head, replicated over its 16 softmax threads
+  f32x4 acc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 pre[kAttnItems];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < kAttnItems; ++j) {
+      const int c = j * kAttnThreads + tid;
+      const int r = c / kRowChunks;
+      const int col = c - r * kRowChunks;
+      const int tok = tile * kTile + r;
+      pre[j] = tok < K ? rows[(long long)tok * kRowChunks + col] : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int j = 0; j < kAttnItems; ++j) {
+      const int c = j * kAttnThreads + tid;
+      const int r = c / kRowChunks;
+      const int col = c - r * kRowChunks;
+      *reinterpret_cast<u32x4*>(kv + r * kLdsRow + col * 16) = pre[j];
+    }
+  };
+
+  if (tb < te) {
+    load_tile(tb);
+    store_tile();
+  }
+  __syncthreads();
+
+  for (int tile = tb; tile < te; ++tile) {
+    if (tile + 1 < te) load_tile(tile + 1);   // next tile's rows in flight during compute
+
+    // scores: wave w takes tokens [16w, 16w + 16) of the tile, all 16 heads
+    {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      const unsigned char* krow = kv + (wave * 16 + r16) * kLdsRow + g * 16;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + ks * 64));
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kf, s, 0, 0, 0);
+      }
+      const int col = wave * 16 + r16;
+      const bool valid = tile * kTile + col < K;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sc[(4 * g + j) * kTile + col] = valid ? s[j] * a.scale_log2 : -INFINITY;
+    }
+    __syncthreads();
+
+    // online softmax: head h = tid / 16, tokens 4*(tid % 16) .. +3
+    {
+      const int h = tid >> 4, c4 = (tid & 15) * 4;
+      const float x0 = sc[h * kTile + c4 + 0], x1 = sc[h * kTile + c4 + 1];
+      const float x2 = sc[h * kTile + c4 + 2], x3 = sc[h * kTile + c4 + 3];
+      float mx = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+      const float p0 = exp2f(x0 - m_new), p1 = exp2f(x1 - m_new);
+      const float p2 = exp2f(x2 - m_new), p3 = exp2f(x3 - m_new);
+      float ps = (p0 + p1) + (p2 + p3);
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) ps += __shfl_xor(ps, o);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      uint16_t* prow = pb + h * kPRow + c4;
+      prow[0] = f32_to_bf16_rne(p0);
+      prow[1] = f32_to_bf16_rne(p1);
+      prow[2] = f32_to_bf16_rne(p2);
+      prow[3] = f32_to_bf16_rne(p3);
+      if ((tid & 15) == 0) alpha_s[h] = alpha;
+    }
+    __syncthreads();
+
+    // P.V: wave w owns value columns [128w, 128w + 128) as 8 MFMA column tiles
+    {
+      float al[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) al[j] = alpha_s[4 * g + j];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[nt][j] *= al[j];
+#pragma unroll
+      for (int kk = 0; kk < kTile / 32; ++kk) {
+        const bf16x8 pf =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(pb + r16 * kPRow + kk * 32 + g * 8));
+        const unsigned char* vbase = kv + (kk * 32 + g * 8) * kLdsRow;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const int e = wave * 128 + nt * 16 + r16;
+          u16x8 vv;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj)
+            vv[jj] = *reinterpret_cast<const uint16_t*>(vbase + jj * kLdsRow + e * 2);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              pf, __builtin_bit_cast(bf16x8, vv), acc[nt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    if (tile + 1 < te) {
+      store_tile();
+      __syncthreads();
+    }
+  }
+
+  // partials: acc lane holds O[h = 4g + j][e = 128w + 16nt + r16]
+  const long long part = (long long)b * a.splits + sp;
+  float* po = a.part_o + part * kHeads * kVDim;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) po[(4 * g + j) * kVDim + wave * 128 + nt * 16 + r16] = acc[nt][j];
+  if ((tid & 15) == 0) {
+    const int h = tid >> 4;
+    a.part_ml[(part * kHeads + h) * 2 + 0] = m_run;
+    a.part_ml[(part * kHeads + h) * 2 + 1] = l_run;
+  }
+}
+
+// Merge of the split partials of request b: out = sum_s 2^(m_s - M) O_s / L,
+// L = sum_s 2^(m_s - M) l_s, lse = (M + log2 L) * ln 2.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      const int32_t* __restrict__ counts,
+                                                      uint16_t* __restrict__ out,
+                                                      float* __restrict__ lse, int splits) {
+  __shared__ float w[kMaxSplits * kHeads];
+  __shared__ float inv_l[kHeads];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  u32x4* ob = reinterpret_cast<u32x4*>(out + (long long)b * kHeads * kVDim);
+  if (counts[4 * b + 3] == 0) {
+    for (int i = tid; i < kHeads * kVDim / 8; i += blockDim.x) ob[i] = u32x4{0u, 0u, 0u, 0u};
+    if (lse != nullptr && tid < kHeads) lse[b * kHeads + tid] = -INFINITY;
+    return;
+  }
+  const float* ml = part_ml + (long long)b * splits * kHeads * 2;
+  if (tid < kHeads) {
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(s * kHeads + tid) * 2]);
+    float L = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float ws = exp2f(ml[(s * kHeads + tid) * 2] - M);
+      w[s * kHeads + tid] = ws;
+      L += ws * ml[(s * kHeads + tid) * 2 + 1];
+    }
+    inv_l[tid] = 1.f / L;
+    if (lse != nullptr) lse[b * kHeads + tid] = (M + log2f(L)) * 0.69314718055994531f;
+  }
+  __syncthreads();
+  const float* pob = part_o + (long long)b * splits * kHeads * kVDim;
+  for (int i8 = tid; i8 < kHeads * kVDim / 8; i8 += blockDim.x) {
+    const int h = (i8 * 8) / kVDim;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < splits; ++s) {
+      const float ws = w[s * kHeads + h];
+      const float4* src = reinterpret_cast<const float4*>(pob + (long long)s * kHeads * kVDim + i8 * 8);
+      const float4 x = src[0], y = src[1];
+      o[0] += ws * x.x; o[1] += ws * x.y; o[2] += ws * x.z; o[3] += ws * x.w;
+      o[4] += ws * y.x; o[5] += ws * y.y; o[6] += ws * y.z; o[7] += ws * y.w;
+    }
+    const float il = inv_l[h];
+    u32x4 r;
+    r[0] = (uint32_t)f32_to_bf16_rne(o[0] * il) | ((uint32_t)f32_to_bf16_rne(o[1] * il) << 16);
+    r[1] = (uint32_t)f32_to_bf16_rne(o[2] * il) | ((uint32_t)f32_to_bf16_rne(o[3] * il) << 16);
+    r[2] = (uint32_t)f32_to_bf16_rne(o[4] * il) | ((uint32_t)f32_to_bf16_rne(o[5] * il) << 16);
+    r[3] = (uint32_t)f32_to_bf16_rne(o[6] * il) | ((uint32_t)f32_to_bf16_rne(o[7] * il) << 16);
+    ob[i8] = r;
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+size_t diff_lds_bytes(int S, int K) {
+  int hb = 1;
+  while ((1 << hb) < 2 * K) ++hb;
+  return (size_t)((S * 2 + 15) & ~15) + (size_t)((S + 15) & ~15) + (size_t)4 * (1u << hb);
+}
+
+static int hash_bits_for(int K) {
+  int hb = 1;
+  while ((1 << hb) < 2 * K) ++hb;
+  return hb;
+}
+
+hipError_t launch_init_units(const Layout& lay, const DevPtrs& d, int unit_begin, int unit_count,
+                             bool reset_counters, hipStream_t s) {
+  const long long n_tok = (long long)unit_count * lay.N;
+  const long long n_slot = (long long)unit_count * lay.S;
+  const long long work = n_tok > n_slot ? n_tok : n_slot;
+  long long blocks = (work + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(init_units_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     d.tok2slot + (long long)unit_begin * lay.N,
+                     d.slot2tok + (long long)unit_begin * lay.S,
+                     d.last_used + (long long)unit_begin * lay.S,
+                     d.order + (long long)unit_begin * lay.S, n_tok, n_slot, lay.S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !reset_counters) return e;
+  const int units = lay.B * lay.L;
+  hipLaunchKernelGGL(reset_counters_kernel, dim3((units + 255) / 256), dim3(256), 0, s, d.stepctr,
+                     d.stats, d.status, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_status(const DevPtrs& d, hipStream_t s) {
+  hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, s, d.status);
+  return hipGetLastError();
+}
+
+hipError_t prepare_kernels() {
+  // the diff kernel's dynamic LDS can exceed the 64 KiB default (up to 112 KiB)
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(diff_lru_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)diff_lds_bytes(KVS_MAX_SLOTS, KVS_MAX_TOPK));
+}
+
+hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
+                           hipStream_t s) {
+  const size_t lds = diff_lds_bytes(lay.S, lay.K);
+  DiffArgs a;
+  a.topk = topk;
+  a.tok2slot = d.tok2slot;
+  a.slot2tok = d.slot2tok;
+  a.last_used = d.last_used;
+  a.order = d.order;
+  a.stepctr = d.stepctr;
+  a.stats = d.stats;
+  a.status = d.status;
+  a.slot_of = d.slot_of;
+  a.miss_pos = d.miss_pos;
+  a.victims = d.victims;
+  a.evicted = d.evicted;
+  a.counts = d.counts;
+  a.N = lay.N;
+  a.S = lay.S;
+  a.K = lay.K;
+  a.L = lay.L;
+  a.layer = layer;
+  a.hash_bits = hash_bits_for(lay.K);
+  hipLaunchKernelGGL(diff_lru_kernel, dim3(lay.B), dim3(kDiffThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_hit_gather(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s) {
+  dim3 grid((lay.K + kCopyRows - 1) / kCopyRows, lay.B);
+  hipLaunchKernelGGL(hit_gather_kernel, grid, dim3(kCopyThreads), 0, s,
+                     reinterpret_cast<const u32x4*>(d.hot), reinterpret_cast<u32x4*>(d.cbuf),
+                     d.slot_of, d.counts, lay.L, layer, lay.S, lay.K);
+  return hipGetLastError();
+}
+
+hipError_t launch_miss_fetch(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
+                             hipStream_t s) {
+  dim3 grid((lay.K + kCopyRows - 1) / kCopyRows, lay.B);
+  hipLaunchKernelGGL(miss_fetch_kernel, grid, dim3(kCopyThreads), 0, s,
+                     reinterpret_cast<const u32x4*>(d.pool), reinterpret_cast<u32x4*>(d.hot),
+                     reinterpret_cast<u32x4*>(d.cbuf), topk, d.miss_pos, d.victims, d.counts,
+                     lay.L, layer, (long long)lay.N, lay.S, lay.K);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t* q, float scale,
+                            hipStream_t s) {
+  AttnArgs a;
+  a.cbuf = d.cbuf;
+  a.q = q;
+  a.counts = d.counts;
+  a.part_o = d.part_o;
+  a.part_ml = d.part_ml;
+  a.K = lay.K;
+  a.splits = lay.splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(attention_kernel, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(lay.B), dim3(256), 0, s, d.part_o, d.part_ml, d.counts,
+                     out, lse, lay.splits);
+  return hipGetLastError();
+}
+
+}  // namespace kvs
