@@ -46,7 +46,19 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--parity-requests", type=int, default=2)
     p.add_argument("--no-profile", action="store_true", help="skip per-kernel HIP events")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy three times (the known-size "
+                        "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -128,6 +140,10 @@ def main():
                                    "(the path shards by request, see the design notes)"}))
         sys.exit(2)
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     import token_level_gather_amd as kvs
 
