@@ -46,6 +46,13 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--parity-requests", type=int, default=2)
     p.add_argument("--no-profile", action="store_true", help="skip per-kernel HIP events")
+    p.add_argument("--breakdown-steps", type=int, default=8,
+                   help="extra steps after the timed region with events around every kernel")
+    p.add_argument("--fetch-groups", type=int, default=0, help="0 = library's choice")
+    p.add_argument("--fetch-blocks", type=int, default=0, help="0 = library's choice")
+    p.add_argument("--attn-splits", type=int, default=0, help="0 = library's choice")
+    p.add_argument("--hit-gather-first", action="store_true",
+                   help="finish the hit gather before the miss fetch starts")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (the known-size "
                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -149,12 +156,15 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     B, L, N, S, K = wl.batch, wl.layers, wl.context, wl.slots, wl.topk
-    total = args.warmup + args.steps
+    breakdown = 0 if args.no_profile else args.breakdown_steps
+    total = args.warmup + args.steps + breakdown
     torch.cuda.set_device(0)
     print(f"# workload {wl.name}: B={B} L={L} N={N} S={S} K={K} f={wl.fresh_rate} "
-          f"steps {args.warmup}+{args.steps}", file=sys.stderr, flush=True)
+          f"steps {args.warmup}+{args.steps}+{breakdown}", file=sys.stderr, flush=True)
 
-    pool = kvs.Pool(B, L, N, S, K, scale=wl.scale)
+    pool = kvs.Pool(B, L, N, S, K, scale=wl.scale, attn_splits=args.attn_splits,
+                    fetch_groups=args.fetch_groups, fetch_blocks=args.fetch_blocks,
+                    flags=kvs.KVS_FLAG_HIT_GATHER_FIRST if args.hit_gather_first else 0)
     W.fill_pool(pool.host.array, wl)
     topk_np = W.topk_streams(wl, total)
     topk = torch.from_numpy(topk_np).cuda()                         # [T][L][B][K]
@@ -169,78 +179,115 @@ def main():
         for l in range(L):
             pool.step(l, topk[t, l], q[t, l], out[t, l], lse[t, l])
 
+    # warm-up; the last warm-up step is timed per kernel to find the dominant kernel
     cold = None
+    dominant = "miss_fetch"
     for t in range(args.warmup):
+        probe = (not args.no_profile) and t == args.warmup - 1 and t > 0
+        if probe:
+            pool.profile_begin(L)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         run_step(t)
         torch.cuda.synchronize()
         if t == 0:
             cold = (time.perf_counter() - t0) * 1e3
+        if probe:
+            kt = pool.profile_end()
+            dominant = max(kvs.KERNEL_NAMES, key=lambda k: kt[k])
     rc, st0 = pool.sync_status()
     assert rc == 0, kvs.strerror(rc)
 
+    # timed region: events bracket the dominant kernel only
     if not args.no_profile:
-        pool.profile_begin(args.steps * L)
+        pool.profile_begin(args.steps * L, kernels=(dominant,))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for t in range(args.warmup, total):
+    for t in range(args.warmup, args.warmup + args.steps):
         run_step(t)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ktimes = pool.profile_end() if not args.no_profile else None
+    tdom = pool.profile_end() if not args.no_profile else None
     rc, st1 = pool.sync_status()
     assert rc == 0, kvs.strerror(rc)
     print(f"# timed {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr, flush=True)
 
+    # per-kernel breakdown after the timed region: events around every kernel
+    ktimes = None
+    if breakdown:
+        pool.profile_begin(breakdown * L)
+        for t in range(args.warmup + args.steps, total):
+            run_step(t)
+        torch.cuda.synchronize()
+        ktimes = pool.profile_end()
+        rc, st2 = pool.sync_status()
+        assert rc == 0, kvs.strerror(rc)
+
     ms_step = elapsed * 1e3 / args.steps
-    launches = args.steps * L
     hits = st1.hits - st0.hits
     misses = st1.misses - st0.misses
     miss_rate = misses / max(1, hits + misses)
     tokens_per_step = B * L * K
     value = tokens_per_step / (ms_step * 1e-3)
-
-    # algorithmic bytes per launch (one kvs_step call = B units of one layer)
-    hit_l, miss_l = hits / launches, misses / launches
     splits = pool.sizes.attn_splits
     part_bytes = B * splits * 16 * (512 + 2) * 4
-    alg = {
-        "diff_lru": {"bound": "hbm", "bytes": B * (16 * K + 4 * S) + 32 * miss_l},
-        "hit_gather": {"bound": "hbm", "bytes": 2 * ROW * hit_l},
-        "miss_fetch": {"bound": "pcie", "bytes": ROW * miss_l, "hbm_write_bytes": 2 * ROW * miss_l},
-        "attention": {"bound": "hbm", "bytes": B * (K * ROW + 16 * 576 * 2) + part_bytes,
-                      "flop": B * 2 * 16 * K * (576 + 512)},
-        "combine": {"bound": "hbm", "bytes": part_bytes + B * 16 * 512 * 2},
-    }
-    kernels = {}
-    dominant = None
-    if ktimes is not None:
-        for name, a in alg.items():
-            avg_ms = ktimes[name] / max(1, ktimes["steps"])
-            gbs = a["bytes"] / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
+
+    def algorithmic(hit_l, miss_l):
+        """Algorithmic bytes (and flops) of one kvs_step call, per kernel."""
+        return {
+            "diff_lru": {"bound": "hbm", "bytes": B * (16 * K + 4 * S) + 32 * miss_l},
+            "hit_gather": {"bound": "hbm", "bytes": 2 * ROW * hit_l},
+            "miss_fetch": {"bound": "pcie", "bytes": ROW * miss_l,
+                           "hbm_write_bytes": 2 * ROW * miss_l},
+            "attention": {"bound": "hbm", "bytes": B * (K * ROW + 16 * 576 * 2) + part_bytes,
+                          "flop": B * 2 * 16 * K * (576 + 512)},
+            "combine": {"bound": "hbm", "bytes": part_bytes + B * 16 * 512 * 2},
+        }
+
+    def kernel_stats(kt, alg, names):
+        res = {}
+        calls = max(1, kt["steps"]) * 1
+        for name in names:
+            a = alg[name]
+            launches = kt["launches"][name]
+            if launches == 0:
+                continue
+            per_call = launches / calls                    # launches per kvs_step call
+            avg_ms = kt[name] / launches                   # average launch duration
+            b_launch = a["bytes"] / per_call               # algorithmic bytes per launch
+            gbs = b_launch / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
             peak = PCIE_PEAK_GBS if a["bound"] == "pcie" else HBM_PEAK_GBS
-            k = {"avg_ms": round(avg_ms, 5), "bound": a["bound"], "bytes_per_launch": int(a["bytes"]),
-                 "achieved_gbs": round(gbs, 2), "peak_gbs": peak, "frac": round(gbs / peak, 4)}
+            k = {"avg_ms": round(avg_ms, 5), "launches_per_call": round(per_call, 3),
+                 "ms_per_call": round(kt[name] / calls, 5), "bound": a["bound"],
+                 "bytes_per_launch": int(b_launch), "achieved_gbs": round(gbs, 2),
+                 "peak_gbs": peak, "frac": round(gbs / peak, 4)}
             if "flop" in a:
-                tf = a["flop"] / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
+                tf = a["flop"] / per_call / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
                 k["tflops"] = round(tf, 2)
                 k["mfma_frac"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 5)
             if "hbm_write_bytes" in a:
-                k["hbm_write_gbs"] = round(a["hbm_write_bytes"] / (avg_ms * 1e-3) / 1e9, 2)
-            kernels[name] = k
-            if dominant is None or avg_ms > kernels[dominant]["avg_ms"]:
-                dominant = name
+                k["hbm_write_gbs"] = round(a["hbm_write_bytes"] / per_call / (avg_ms * 1e-3) / 1e9, 2)
+            res[name] = k
+        return res
+
+    calls_timed = args.steps * L
+    alg = algorithmic(hits / calls_timed, misses / calls_timed)
+    dom = kernel_stats(tdom, alg, (dominant,)).get(dominant) if tdom is not None else None
+    kernels = None
+    if ktimes is not None:
+        calls_b = breakdown * L
+        alg_b = algorithmic((st2.hits - st1.hits) / calls_b, (st2.misses - st1.misses) / calls_b)
+        kernels = kernel_stats(ktimes, alg_b, kvs.KERNEL_NAMES)
 
     h2d = measure_h2d_peak(torch)
     roofline = None
-    if dominant is not None:
-        d = kernels[dominant]
-        roofline = {"kernel": dominant, "bound": d["bound"], "achieved": d["achieved_gbs"],
-                    "peak": d["peak_gbs"], "unit": "GB/s", "frac": d["frac"],
-                    "traffic": load_traffic(dominant, wl.name)}
-        if d["bound"] == "pcie":
-            roofline["frac_of_measured_h2d"] = round(d["achieved_gbs"] / h2d, 4)
+    if dom is not None:
+        roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved_gbs"],
+                    "peak": dom["peak_gbs"], "unit": "GB/s", "frac": dom["frac"],
+                    "traffic": load_traffic(dominant, wl.name), "avg_ms": dom["avg_ms"],
+                    "bytes_per_launch": dom["bytes_per_launch"]}
+        if dom["bound"] == "pcie":
+            roofline["frac_of_measured_h2d"] = round(dom["achieved_gbs"] / h2d, 4)
 
     # parity of sampled requests against the oracle, plus the CPU baseline
     cpu = None
@@ -269,8 +316,8 @@ def main():
                   "attn_max_abs": round(max_abs, 6), "attn_max_rel_l2": round(max_rel, 6),
                   "pass": bool(state_ok and max_abs <= 2e-2 and max_rel <= 1e-2)}
 
-    hbm_bytes_step = sum(alg[k]["bytes"] for k in ("diff_lru", "hit_gather", "attention", "combine")) \
-        * L + 2 * ROW * miss_l * L
+    hbm_bytes_step = (sum(alg[k]["bytes"] for k in ("diff_lru", "hit_gather", "attention", "combine"))
+                      + alg["miss_fetch"]["hbm_write_bytes"]) * L
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -286,7 +333,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "layers": L, "context": N, "slots": S,
                    "topk": K, "fresh_rate": wl.fresh_rate, "fresh_dist": wl.dist,
-                   "heads": 16, "head_dim": 576, "v_dim": 512, "attn_splits": splits},
+                   "heads": 16, "head_dim": 576, "v_dim": 512, "attn_splits": splits,
+                   "fetch_groups": pool.sizes.fetch_groups, "fetch_blocks": pool.sizes.fetch_blocks,
+                   "hit_gather_first": bool(args.hit_gather_first)},
         "decode_steps_per_s": round(1e3 / ms_step, 2),
         "cold_step_ms": None if cold is None else round(cold, 4),
         "miss_rate": round(miss_rate, 5),
@@ -294,6 +343,9 @@ def main():
         "hbm_gbs_step": round(hbm_bytes_step / (ms_step * 1e-3) / 1e9, 2),
         "h2d_peak_measured_gbs": round(h2d, 2),
         "kernels": kernels,
+        "kernels_note": f"per-kernel HIP events around every launch over {breakdown} extra steps "
+                        "after the timed region; inside the timed region only the dominant "
+                        "kernel is bracketed",
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,

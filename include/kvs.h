@@ -93,9 +93,17 @@ typedef struct kvs_config {
   int32_t head_dim;     /* must be KVS_HEAD_DIM */
   int32_t v_dim;        /* must be KVS_V_DIM */
   float scale;          /* softmax scale > 0, e.g. 1/sqrt(576) */
-  int32_t attn_splits;  /* token splits per request in attention; 0 = library's choice */
-  int32_t flags;        /* reserved, must be 0 */
+  int32_t attn_splits;  /* token splits per request in attention, 1..64; 0 = library's choice */
+  int32_t fetch_groups; /* request groups one step is pipelined over: the attention of group g
+                           runs while the misses of group g+1 are fetched; 1..64, 0 = library's
+                           choice */
+  int32_t fetch_blocks; /* workgroups of one group's miss fetch, 1..65535; 0 = library's choice */
+  int32_t flags;        /* KVS_FLAG_* bits, 0 = default schedule */
 } kvs_config;
+
+/* kvs_config.flags: run the hit gather to completion before the miss fetch
+ * starts (default: the two run concurrently on two streams). */
+#define KVS_FLAG_HIT_GATHER_FIRST 1
 
 /* Bytes each caller buffer must hold (see kvs_buffers). */
 typedef struct kvs_sizes {
@@ -105,6 +113,8 @@ typedef struct kvs_sizes {
   uint64_t cbuf_bytes;      /* B*K*576*2: compute buffer of one step, device */
   uint64_t scratch_bytes;   /* per-step lists and attention partials, device */
   int32_t attn_splits;      /* the split count these sizes assume */
+  int32_t fetch_groups;     /* resolved kvs_config.fetch_groups */
+  int32_t fetch_blocks;     /* resolved kvs_config.fetch_blocks */
 } kvs_sizes;
 
 /*
@@ -158,6 +168,7 @@ typedef struct kvs_unit_state {
  * kvs_profile_begin and kvs_profile_end (HIP events on the launch streams). */
 typedef struct kvs_kernel_times {
   int32_t steps;                      /* kvs_step calls recorded */
+  int32_t launches[KVS_NUM_KERNELS];  /* launches recorded per kernel */
   float ms_total[KVS_NUM_KERNELS];    /* sum of launch durations, milliseconds */
 } kvs_kernel_times;
 
@@ -212,8 +223,11 @@ int kvs_sync_status(kvs_pool* pool, void* stream, kvs_step_stats* stats);
 int kvs_debug_read_state(kvs_pool* pool, int32_t req, int32_t layer, void* stream,
                          kvs_unit_state* st);
 
-/* Record per-kernel HIP-event times for the next `max_steps` kvs_step calls. */
-int kvs_profile_begin(kvs_pool* pool, int32_t max_steps);
+/* Record HIP-event times (one event pair around every launch of a kernel
+ * whose bit (1 << KVS_KERNEL_*) is set in `kernel_mask`, on the stream it runs
+ * on) for the next `max_steps` kvs_step calls.  Each event pair adds a few
+ * microseconds to the step, so timing runs bracket only the kernels they need. */
+int kvs_profile_begin(kvs_pool* pool, int32_t max_steps, uint32_t kernel_mask);
 /* Synchronise and report the recorded times; stops recording. */
 int kvs_profile_end(kvs_pool* pool, kvs_kernel_times* out);
 

@@ -80,7 +80,8 @@ def test_query_sizes_arithmetic():
     dict(batch=0), dict(layers=0), dict(topk=0), dict(slots=100, topk=200),
     dict(context=100, topk=200, slots=300), dict(slots=16385), dict(topk=8193, slots=9000),
     dict(heads=8), dict(head_dim=512), dict(v_dim=576), dict(scale=0.0),
-    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=1), dict(context=2**31),
+    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=2), dict(context=2**31),
+    dict(fetch_groups=65), dict(fetch_groups=-1), dict(fetch_blocks=-1), dict(fetch_blocks=65536),
     dict(attn_splits=33),   # more splits than 64-token tiles (K = 2048 -> 32)
 ])
 def test_bad_configs_rejected(bad):
@@ -118,7 +119,7 @@ def test_null_pool_calls_are_rejected():
     assert lib.kvs_free_request(None, 0, None) == kvs.KVS_EINVAL
     assert lib.kvs_release(None) == kvs.KVS_EINVAL
     assert lib.kvs_publish(None, 0, 0, 0, 0, None) == kvs.KVS_EINVAL
-    assert lib.kvs_profile_begin(None, 1) == kvs.KVS_EINVAL
+    assert lib.kvs_profile_begin(None, 1, 1) == kvs.KVS_EINVAL
 
 
 def test_strerror():
@@ -126,3 +127,19 @@ def test_strerror():
     assert "outside" in kvs.strerror(kvs.KVS_ERANGE)
     assert kvs.strerror(kvs.KVS_OK) == "ok"
     assert "HIP" in kvs.strerror(kvs.KVS_EHIP_BASE - 2)
+
+
+def test_pipelining_knobs_resolve():
+    s = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096, topk=2048,
+                                        fetch_groups=4, fetch_blocks=128))
+    assert (s.fetch_groups, s.fetch_blocks) == (4, 128)
+    assert s.attn_splits == 32          # sized for one 16-request group
+    s = kvs.query_sizes(kvs.make_config(batch=3, layers=1, context=4096, slots=512, topk=256,
+                                        fetch_groups=8))
+    assert s.fetch_groups == 3          # never more groups than requests
+    s = kvs.query_sizes(kvs.make_config(batch=10, layers=1, context=4096, slots=512, topk=256,
+                                        fetch_groups=4))
+    assert s.fetch_groups == 4          # groups of 3, 3, 3, 1
+    s = kvs.query_sizes(kvs.make_config(batch=9, layers=1, context=4096, slots=512, topk=256,
+                                        fetch_groups=4))
+    assert s.fetch_groups == 3          # groups of 3: a fourth group would be empty

@@ -41,7 +41,8 @@ class kvs_config(ctypes.Structure):
         ("batch", ctypes.c_int32), ("layers", ctypes.c_int32), ("context", ctypes.c_int64),
         ("slots", ctypes.c_int32), ("topk", ctypes.c_int32), ("heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("scale", ctypes.c_float),
-        ("attn_splits", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("attn_splits", ctypes.c_int32), ("fetch_groups", ctypes.c_int32),
+        ("fetch_blocks", ctypes.c_int32), ("flags", ctypes.c_int32),
     ]
 
 
@@ -50,6 +51,7 @@ class kvs_sizes(ctypes.Structure):
         ("host_pool_bytes", ctypes.c_uint64), ("hot_bytes", ctypes.c_uint64),
         ("meta_bytes", ctypes.c_uint64), ("cbuf_bytes", ctypes.c_uint64),
         ("scratch_bytes", ctypes.c_uint64), ("attn_splits", ctypes.c_int32),
+        ("fetch_groups", ctypes.c_int32), ("fetch_blocks", ctypes.c_int32),
     ]
 
 
@@ -82,7 +84,8 @@ class kvs_unit_state(ctypes.Structure):
 
 
 class kvs_kernel_times(ctypes.Structure):
-    _fields_ = [("steps", ctypes.c_int32), ("ms_total", ctypes.c_float * len(KERNEL_NAMES))]
+    _fields_ = [("steps", ctypes.c_int32), ("launches", ctypes.c_int32 * len(KERNEL_NAMES)),
+                ("ms_total", ctypes.c_float * len(KERNEL_NAMES))]
 
 
 class KvsError(RuntimeError):
@@ -115,7 +118,7 @@ def lib() -> ctypes.CDLL:
         "kvs_free_request": [vp, i32, vp],
         "kvs_sync_status": [vp, vp, ctypes.POINTER(kvs_step_stats)],
         "kvs_debug_read_state": [vp, i32, i32, vp, ctypes.POINTER(kvs_unit_state)],
-        "kvs_profile_begin": [vp, i32],
+        "kvs_profile_begin": [vp, i32, ctypes.c_uint32],
         "kvs_profile_end": [vp, ctypes.POINTER(kvs_kernel_times)],
         "kvs_release": [vp],
     }
@@ -139,12 +142,16 @@ def _check(rc: int, what: str) -> int:
     return rc
 
 
-def make_config(batch, layers, context, slots, topk, scale=None, attn_splits=0, flags=0,
-                heads=HEADS, head_dim=HEAD_DIM, v_dim=V_DIM) -> kvs_config:
+KVS_FLAG_HIT_GATHER_FIRST = 1
+
+
+def make_config(batch, layers, context, slots, topk, scale=None, attn_splits=0, fetch_groups=0,
+                fetch_blocks=0, flags=0, heads=HEADS, head_dim=HEAD_DIM,
+                v_dim=V_DIM) -> kvs_config:
     if scale is None:
         scale = 1.0 / float(np.sqrt(head_dim))
     return kvs_config(batch, layers, context, slots, topk, heads, head_dim, v_dim, scale,
-                      attn_splits, flags)
+                      attn_splits, fetch_groups, fetch_blocks, flags)
 
 
 def query_sizes(cfg: kvs_config) -> kvs_sizes:
@@ -188,9 +195,11 @@ class Pool:
     """
 
     def __init__(self, batch, layers, context, slots, topk, scale=None, attn_splits=0,
-                 host: Optional[HostPool] = None, device=None, stream=None):
+                 fetch_groups=0, fetch_blocks=0, flags=0, host: Optional[HostPool] = None,
+                 device=None, stream=None):
         import torch
-        self.cfg = make_config(batch, layers, context, slots, topk, scale, attn_splits)
+        self.cfg = make_config(batch, layers, context, slots, topk, scale, attn_splits,
+                               fetch_groups, fetch_blocks, flags)
         self.sizes = query_sizes(self.cfg)
         self.B, self.L, self.N, self.S, self.K = batch, layers, context, slots, topk
         self.device = torch.device("cuda" if device is None else device)
@@ -259,13 +268,19 @@ class Pool:
         arr["step"] = int(st.step)
         return arr
 
-    def profile_begin(self, max_steps):
-        _check(lib().kvs_profile_begin(self.handle, max_steps), "kvs_profile_begin")
+    def profile_begin(self, max_steps, kernels=KERNEL_NAMES):
+        """Bracket every launch of the named kernels with HIP events."""
+        mask = 0
+        for k in kernels:
+            mask |= 1 << KERNEL_NAMES.index(k)
+        _check(lib().kvs_profile_begin(self.handle, max_steps, mask), "kvs_profile_begin")
 
     def profile_end(self) -> dict:
         t = kvs_kernel_times()
         _check(lib().kvs_profile_end(self.handle, ctypes.byref(t)), "kvs_profile_end")
-        return {"steps": t.steps, **{n: t.ms_total[i] for i, n in enumerate(KERNEL_NAMES)}}
+        return {"steps": t.steps,
+                "launches": {n: t.launches[i] for i, n in enumerate(KERNEL_NAMES)},
+                **{n: t.ms_total[i] for i, n in enumerate(KERNEL_NAMES)}}
 
     def release(self):
         if self.handle:

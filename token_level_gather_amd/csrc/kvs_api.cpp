@@ -27,22 +27,34 @@ int make_layout(const kvs_config* c, Layout* lay) {
   if (c->heads != KVS_HEADS || c->head_dim != KVS_HEAD_DIM || c->v_dim != KVS_V_DIM)
     return KVS_EINVAL;
   if (!(c->scale > 0.f) || !isfinite(c->scale)) return KVS_EINVAL;
-  if (c->attn_splits < 0 || c->attn_splits > 64 || c->flags != 0) return KVS_EINVAL;
+  if (c->attn_splits < 0 || c->attn_splits > 64) return KVS_EINVAL;
+  if (c->fetch_groups < 0 || c->fetch_groups > 64 || c->fetch_blocks < 0 ||
+      c->fetch_blocks > 65535)
+    return KVS_EINVAL;
+  if ((c->flags & ~KVS_FLAG_HIT_GATHER_FIRST) != 0) return KVS_EINVAL;
   if ((int64_t)c->batch * c->layers > 0x7fffffffLL) return KVS_EINVAL;
 
   const uint64_t B = c->batch, L = c->layers, N = c->context, S = c->slots, K = c->topk;
   const uint64_t U = B * L;
+  int groups = c->fetch_groups == 0 ? 1 : c->fetch_groups;
+  if (groups > c->batch) groups = c->batch;
+  const int group_size = (int)((B + groups - 1) / groups);
+  groups = (int)((B + group_size - 1) / group_size);   // no empty group
   const int ntiles = (int)((K + 63) / 64);
   int splits = c->attn_splits;
   if (splits == 0) {
-    // about two attention workgroups per compute unit (256 CUs), at least one tile each
-    splits = (int)((512 + B - 1) / B);
+    // about two attention workgroups per compute unit (256 CUs) for one group,
+    // at least one 64-token tile each
+    splits = (int)((512 + group_size - 1) / group_size);
     if (splits > ntiles) splits = ntiles;
     if (splits > 64) splits = 64;
     if (splits < 1) splits = 1;
   } else if (splits > ntiles) {
     return KVS_EINVAL;
   }
+  // 512 fetch workgroups per group (2 per CU) keep the host link saturated;
+  // more only adds outstanding PCIe reads that slow concurrent HBM traffic
+  int fetch_blocks = c->fetch_blocks == 0 ? 512 : c->fetch_blocks;
 
   lay->B = c->batch;
   lay->L = c->layers;
@@ -50,6 +62,10 @@ int make_layout(const kvs_config* c, Layout* lay) {
   lay->K = c->topk;
   lay->N = c->context;
   lay->splits = splits;
+  lay->groups = groups;
+  lay->group_size = group_size;
+  lay->fetch_blocks = fetch_blocks;
+  lay->flags = c->flags;
 
   uint64_t o = 0;
   auto take = [&](uint64_t bytes) {
@@ -89,11 +105,17 @@ struct kvs_pool {
   uint8_t* host_pool;       // host address of the pool (for kvs_publish)
   int device;
   hipStream_t side;         // miss fetch runs here, beside the hit gather
-  hipEvent_t ev_fork, ev_join;
-  // per-kernel timing: events [max_steps][KVS_NUM_KERNELS][2]
+  hipEvent_t ev_fork;       // main stream -> side stream (after diff_lru, or the hit gather)
+  hipEvent_t ev_group[64];  // side stream -> main stream, one per request group
+  hipEvent_t ev_join;       // last group's event: all side-stream work of the last step
+  // per-kernel timing: a pool of event pairs, one pair per recorded launch
   std::vector<hipEvent_t> prof_ev;
-  int prof_max;
-  int prof_n;
+  std::vector<int> prof_kernel;
+  int prof_cap;      // launches that can be recorded
+  int prof_used;     // launches recorded
+  int prof_steps;    // kvs_step calls recorded
+  int prof_max_steps;
+  uint32_t prof_mask;  // kernels recorded (1 << KVS_KERNEL_*)
 };
 
 static int hip_err(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP_BASE - (int)e; }
@@ -104,16 +126,25 @@ static int hip_err(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP_BA
     if (e_ != hipSuccess) return hip_err(e_);   \
   } while (0)
 
-static hipEvent_t* prof_slot(kvs_pool* p, int kernel) {
-  if (p->prof_n >= p->prof_max) return nullptr;
-  return &p->prof_ev[((size_t)p->prof_n * KVS_NUM_KERNELS + kernel) * 2];
+// Frees the pool's streams and events (handles left null by a failed create are skipped).
+static void destroy_pool(kvs_pool* p) {
+  for (hipEvent_t ev : p->prof_ev) (void)hipEventDestroy(ev);
+  if (p->ev_fork != nullptr) (void)hipEventDestroy(p->ev_fork);
+  for (int g = 0; g < 64; ++g)
+    if (p->ev_group[g] != nullptr) (void)hipEventDestroy(p->ev_group[g]);
+  if (p->side != nullptr) (void)hipStreamDestroy(p->side);
+  delete p;
 }
 
 // Launch `fn` on `s`, bracketed by timing events when profiling.
 template <typename F>
 static hipError_t timed(kvs_pool* p, int kernel, hipStream_t s, F fn) {
-  hipEvent_t* ev = prof_slot(p, kernel);
-  if (ev != nullptr) {
+  hipEvent_t* ev = nullptr;
+  if (p->prof_steps < p->prof_max_steps && p->prof_used < p->prof_cap &&
+      ((p->prof_mask >> kernel) & 1u)) {
+    ev = &p->prof_ev[(size_t)p->prof_used * 2];
+    p->prof_kernel[p->prof_used] = kernel;
+    ++p->prof_used;
     hipError_t e = hipEventRecord(ev[0], s);
     if (e != hipSuccess) return e;
   }
@@ -137,6 +168,8 @@ int kvs_query_sizes(const kvs_config* cfg, kvs_sizes* out) {
   out->cbuf_bytes = B * K * kRowBytes;
   out->scratch_bytes = lay.scratch_bytes;
   out->attn_splits = lay.splits;
+  out->fetch_groups = lay.groups;
+  out->fetch_blocks = lay.fetch_blocks;
   return KVS_OK;
 }
 
@@ -194,8 +227,10 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
   if (p == nullptr) return KVS_ENOMEM;
   p->cfg = *cfg;
   make_layout(cfg, &p->lay);
-  p->prof_max = 0;
-  p->prof_n = 0;
+  p->prof_cap = 0;
+  p->prof_used = 0;
+  p->prof_steps = 0;
+  p->prof_max_steps = 0;
   p->host_pool = (uint8_t*)const_cast<void*>(bufs->host_pool);
 
   uint8_t* meta = (uint8_t*)bufs->meta;
@@ -224,11 +259,13 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
   if (e == hipSuccess) e = prepare_kernels();
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming);
+  for (int g = 0; g < p->lay.groups && e == hipSuccess; ++g)
+    e = hipEventCreateWithFlags(&p->ev_group[g], hipEventDisableTiming);
+  if (e == hipSuccess) p->ev_join = p->ev_group[p->lay.groups - 1];
   if (e == hipSuccess)
     e = launch_init_units(L, d, 0, L.B * L.L, /*reset_counters=*/true, (hipStream_t)stream);
   if (e != hipSuccess) {
-    delete p;
+    destroy_pool(p);
     return hip_err(e);
   }
   *out = p;
@@ -252,19 +289,38 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
   const hipStream_t s = (hipStream_t)stream;
   const Layout& L = p->lay;
   const DevPtrs& d = p->d;
+  const bool hit_first = (L.flags & KVS_FLAG_HIT_GATHER_FIRST) != 0;
+  // lookup, diff, LRU and map update for every request of the layer
   KVS_TRY_HIP(timed(p, KVS_KERNEL_DIFF_LRU, s, [&] { return launch_diff_lru(L, d, layer, topk, s); }));
+  if (hit_first)
+    KVS_TRY_HIP(timed(p, KVS_KERNEL_HIT_GATHER, s,
+                      [&] { return launch_hit_gather(L, d, layer, 0, L.B, s); }));
+  // misses of each request group on the side stream, in group order
   KVS_TRY_HIP(hipEventRecord(p->ev_fork, s));
   KVS_TRY_HIP(hipStreamWaitEvent(p->side, p->ev_fork, 0));
-  KVS_TRY_HIP(timed(p, KVS_KERNEL_MISS_FETCH, p->side,
-                    [&] { return launch_miss_fetch(L, d, layer, topk, p->side); }));
-  KVS_TRY_HIP(hipEventRecord(p->ev_join, p->side));
-  KVS_TRY_HIP(timed(p, KVS_KERNEL_HIT_GATHER, s, [&] { return launch_hit_gather(L, d, layer, s); }));
-  KVS_TRY_HIP(hipStreamWaitEvent(s, p->ev_join, 0));
-  KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s,
-                    [&] { return launch_attention(L, d, (const uint16_t*)q, p->cfg.scale, s); }));
-  KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
-                    [&] { return launch_combine(L, d, (uint16_t*)out, lse, s); }));
-  if (p->prof_n < p->prof_max) ++p->prof_n;
+  for (int g = 0; g < L.groups; ++g) {
+    const int b0 = g * L.group_size;
+    const int nb = b0 + L.group_size <= L.B ? L.group_size : L.B - b0;
+    KVS_TRY_HIP(timed(p, KVS_KERNEL_MISS_FETCH, p->side,
+                      [&] { return launch_miss_fetch(L, d, layer, topk, b0, nb, p->side); }));
+    KVS_TRY_HIP(hipEventRecord(p->ev_group[g], p->side));
+  }
+  // hits of every request on the main stream, beside the fetch
+  if (!hit_first)
+    KVS_TRY_HIP(timed(p, KVS_KERNEL_HIT_GATHER, s,
+                      [&] { return launch_hit_gather(L, d, layer, 0, L.B, s); }));
+  // attention of group g as soon as its misses have landed
+  for (int g = 0; g < L.groups; ++g) {
+    const int b0 = g * L.group_size;
+    const int nb = b0 + L.group_size <= L.B ? L.group_size : L.B - b0;
+    KVS_TRY_HIP(hipStreamWaitEvent(s, p->ev_group[g], 0));
+    KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s, [&] {
+      return launch_attention(L, d, (const uint16_t*)q, p->cfg.scale, b0, nb, s);
+    }));
+    KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
+                      [&] { return launch_combine(L, d, (uint16_t*)out, lse, b0, nb, s); }));
+  }
+  if (p->prof_steps < p->prof_max_steps) ++p->prof_steps;
   return KVS_OK;
 }
 
@@ -338,46 +394,48 @@ int kvs_debug_read_state(kvs_pool* p, int32_t req, int32_t layer, void* stream,
   return KVS_OK;
 }
 
-int kvs_profile_begin(kvs_pool* p, int32_t max_steps) {
+int kvs_profile_begin(kvs_pool* p, int32_t max_steps, uint32_t kernel_mask) {
   if (p == nullptr || max_steps < 0) return KVS_EINVAL;
-  const size_t need = (size_t)max_steps * KVS_NUM_KERNELS * 2;
-  while (p->prof_ev.size() < need) {
+  if ((kernel_mask >> KVS_NUM_KERNELS) != 0) return KVS_EINVAL;
+  const int per_step = 2 + 3 * p->lay.groups;   // diff, hit, groups x (miss, attention, combine)
+  const size_t need = (size_t)max_steps * per_step;
+  while (p->prof_ev.size() < need * 2) {
     hipEvent_t e;
     KVS_TRY_HIP(hipEventCreate(&e));
     p->prof_ev.push_back(e);
   }
-  p->prof_max = max_steps;
-  p->prof_n = 0;
+  p->prof_kernel.assign(need, 0);
+  p->prof_cap = (int)need;
+  p->prof_used = 0;
+  p->prof_steps = 0;
+  p->prof_max_steps = max_steps;
+  p->prof_mask = kernel_mask;
   return KVS_OK;
 }
 
 int kvs_profile_end(kvs_pool* p, kvs_kernel_times* out) {
   if (p == nullptr || out == nullptr) return KVS_EINVAL;
   memset(out, 0, sizeof(*out));
-  const int n = p->prof_n;
-  p->prof_max = 0;   // stop recording
+  const int n = p->prof_used;
   for (int i = 0; i < n; ++i) {
-    for (int k = 0; k < KVS_NUM_KERNELS; ++k) {
-      hipEvent_t* ev = &p->prof_ev[((size_t)i * KVS_NUM_KERNELS + k) * 2];
-      KVS_TRY_HIP(hipEventSynchronize(ev[1]));
-      float ms = 0.f;
-      KVS_TRY_HIP(hipEventElapsedTime(&ms, ev[0], ev[1]));
-      out->ms_total[k] += ms;
-    }
+    hipEvent_t* ev = &p->prof_ev[(size_t)i * 2];
+    KVS_TRY_HIP(hipEventSynchronize(ev[1]));
+    float ms = 0.f;
+    KVS_TRY_HIP(hipEventElapsedTime(&ms, ev[0], ev[1]));
+    out->ms_total[p->prof_kernel[i]] += ms;
+    out->launches[p->prof_kernel[i]] += 1;
   }
-  out->steps = n;
-  p->prof_n = 0;
+  out->steps = p->prof_steps;
+  p->prof_max_steps = 0;   // stop recording
+  p->prof_used = 0;
+  p->prof_steps = 0;
   return KVS_OK;
 }
 
 int kvs_release(kvs_pool* p) {
   if (p == nullptr) return KVS_EINVAL;
-  hipError_t e = hipStreamSynchronize(p->side);
-  for (hipEvent_t ev : p->prof_ev) (void)hipEventDestroy(ev);
-  (void)hipEventDestroy(p->ev_fork);
-  (void)hipEventDestroy(p->ev_join);
-  (void)hipStreamDestroy(p->side);
-  delete p;
+  const hipError_t e = hipStreamSynchronize(p->side);
+  destroy_pool(p);
   return hip_err(e);
 }
 

@@ -296,8 +296,8 @@ static_assert(kCopyItems * kCopyThreads == kCopyRows * kRowChunks, "copy tiling"
 // Hits: cbuf[b][i] = hot[b][l][slot_of[b][i]] for every hit position i.
 __global__ __launch_bounds__(kCopyThreads) void hit_gather_kernel(
     const u32x4* __restrict__ hot, u32x4* __restrict__ cbuf, const int32_t* __restrict__ slot_of,
-    const int32_t* __restrict__ counts, int L, int layer, int S, int K) {
-  const int b = blockIdx.y;
+    const int32_t* __restrict__ counts, int L, int layer, int S, int K, int b0) {
+  const int b = b0 + blockIdx.y;
   if (counts[4 * b + 3] == 0) return;
   const long long u = (long long)b * L + layer;
   const int i0 = blockIdx.x * kCopyRows;
@@ -324,54 +324,57 @@ __global__ __launch_bounds__(kCopyThreads) void hit_gather_kernel(
 }
 
 // Misses: row = pool[b][l][tok_j]; cbuf[b][miss_pos_j] = row; hot[b][l][victim_j] = row.
-// The pool pointer is pinned host memory: every load crosses PCIe.
+// The pool pointer is pinned host memory: every load crosses PCIe.  Blocks
+// (x, y) serve request b0 + y, taking 32-row groups x, x + gridDim.x, ...
 __global__ __launch_bounds__(kCopyThreads) void miss_fetch_kernel(
     const u32x4* __restrict__ pool, u32x4* __restrict__ hot, u32x4* __restrict__ cbuf,
     const int32_t* __restrict__ topk, const int32_t* __restrict__ miss_pos,
     const int32_t* __restrict__ victims, const int32_t* __restrict__ counts, int L, int layer,
-    long long N, int S, int K) {
-  const int b = blockIdx.y;
+    long long N, int S, int K, int b0) {
+  const int b = b0 + blockIdx.y;
   if (counts[4 * b + 3] == 0) return;
   const int n = counts[4 * b + 1];
-  const int j0 = blockIdx.x * kCopyRows;
-  if (j0 >= n) return;
   const long long u = (long long)b * L + layer;
   const long long bk = (long long)b * K;
-  u32x4 v[kCopyItems];
-  long long dc[kCopyItems], dh[kCopyItems];
+  for (int j0 = blockIdx.x * kCopyRows; j0 < n; j0 += gridDim.x * kCopyRows) {
+    u32x4 v[kCopyItems];
+    long long dc[kCopyItems], dh[kCopyItems];
 #pragma unroll
-  for (int j = 0; j < kCopyItems; ++j) {
-    const int c = j * kCopyThreads + threadIdx.x;
-    const int r = c / kRowChunks;
-    const int col = c - r * kRowChunks;
-    const int jj = j0 + r;
-    dc[j] = -1;
-    if (jj < n) {
-      const int i = miss_pos[bk + jj];
-      const int tok = topk[bk + i];
-      v[j] = pool[(u * N + tok) * kRowChunks + col];
-      dc[j] = (bk + i) * kRowChunks + col;
-      dh[j] = (u * S + victims[bk + jj]) * kRowChunks + col;
+    for (int j = 0; j < kCopyItems; ++j) {
+      const int c = j * kCopyThreads + threadIdx.x;
+      const int r = c / kRowChunks;
+      const int col = c - r * kRowChunks;
+      const int jj = j0 + r;
+      dc[j] = -1;
+      if (jj < n) {
+        const int i = miss_pos[bk + jj];
+        const int tok = topk[bk + i];
+        v[j] = pool[(u * N + tok) * kRowChunks + col];
+        dc[j] = (bk + i) * kRowChunks + col;
+        dh[j] = (u * S + victims[bk + jj]) * kRowChunks + col;
+      }
     }
-  }
 #pragma unroll
-  for (int j = 0; j < kCopyItems; ++j) {
-    if (dc[j] >= 0) {
-      cbuf[dc[j]] = v[j];
-      hot[dh[j]] = v[j];
+    for (int j = 0; j < kCopyItems; ++j) {
+      if (dc[j] >= 0) {
+        cbuf[dc[j]] = v[j];
+        hot[dh[j]] = v[j];
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------ attention
-constexpr int kAttnThreads = 256;
-constexpr int kTile = 64;                       // tokens per LDS tile (16 per wave in Q.K^T)
+constexpr int kAttnThreads = 512;               // 8 waves
+constexpr int kTile = 64;                       // tokens per LDS tile
 constexpr int kLdsRow = kRowBytes + 16;         // padded row: 16-B aligned, spreads banks
-constexpr int kAttnItems = kTile * kRowChunks / kAttnThreads;   // 18 chunks / thread
+constexpr int kAttnItems = kTile * kRowChunks / kAttnThreads;   // 9 chunks / thread
 constexpr int kKSteps = kRowElems / 32;         // 18 MFMA k-steps over 576 dims
+constexpr int kKHalf = kKSteps / 2;             // each Q.K^T wave takes half of them
 constexpr int kPRow = kTile + 8;                // bf16 P row stride (144 B)
 constexpr int kMaxSplits = 64;
 static_assert(kAttnItems * kAttnThreads == kTile * kRowChunks, "attention tiling");
+static_assert(kKHalf * 2 == kKSteps, "k split");
 
 struct AttnArgs {
   const uint16_t* cbuf;   // [B][K][576]
@@ -379,7 +382,7 @@ struct AttnArgs {
   const int32_t* counts;  // [B][4]
   float* part_o;          // [B][splits][16][512]
   float* part_ml;         // [B][splits][16][2]
-  int K, splits;
+  int K, splits, b0;
   float scale_log2;       // softmax scale * log2(e): scores are kept in log2 units
 };
 
@@ -389,34 +392,42 @@ struct AttnArgs {
 // k-values selected by l / 16; the result lane l holds rows 4*(l/16)+j,
 // column l % 16.  Both operands of each product take their k-values through
 // the same (l/16, j) -> k assignment, so the sum is over the intended k.
+//
+// Wave roles per 64-token tile:
+//   Q.K^T   wave w: tokens 16*(w % 4) .. +16, k-steps 9*(w / 4) .. +9 (two
+//           partial score tiles per token block, summed in the softmax);
+//   softmax 32 threads per head, 2 tokens each;
+//   P.V     wave w: value columns 64*w .. +64 (4 MFMA column tiles).
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char kv[kTile * kLdsRow];
-  __shared__ float sc[kHeads * kTile];
+  __shared__ float sc[2 * kHeads * kTile];
   __shared__ __attribute__((aligned(16))) uint16_t pb[kHeads * kPRow];
   __shared__ float alpha_s[kHeads];
 
-  const int b = blockIdx.y, sp = blockIdx.x;
-  if (a.counts[4 * b + 3] == 0) return;
+  const int b = a.b0 + blockIdx.y, sp = blockIdx.x;
+  if (a.counts[4 * b + 3] == 0) return;   // combine writes the zero output
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
+  const int tt = wave & 3, kh = wave >> 2;
   const int K = a.K;
   const int ntiles = (K + kTile - 1) / kTile;
   const int tb = (int)((long long)sp * ntiles / a.splits);
   const int te = (int)((long long)(sp + 1) * ntiles / a.splits);
   const u32x4* rows = reinterpret_cast<const u32x4*>(a.cbuf + (long long)b * K * kRowElems);
 
-  // Q as A-operand fragments: head r16, dims ks*32 + g*8 .. +7
-  bf16x8 qf[kKSteps];
+  // Q as A-operand fragments: head r16, dims (kh*9 + ks)*32 + g*8 .. +7
+  bf16x8 qf[kKHalf];
   {
-    const u32x4* qh = reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
+    const u32x4* qh =
+        reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = as_bf16x8(qh[ks * 4 + g]);
+    for (int ks = 0; ks < kKHalf; ++ks) qf[ks] = as_bf16x8(qh[(kh * kKHalf + ks) * 4 + g]);
   }
 
-  float m_run = -INFINITY, l_run = 0.f;   // per head, replicated over its 16 softmax threads
-  f32x4 acc[8];
+  float m_run = -INFINITY, l_run = 0.f;   // per head, replicated over its 32 softmax threads
+  f32x4 acc[4];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 pre[kAttnItems];
   auto load_tile = [&](int tile) {
@@ -448,56 +459,53 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   for (int tile = tb; tile < te; ++tile) {
     if (tile + 1 < te) load_tile(tile + 1);   // next tile's rows in flight during compute
 
-    // scores: wave w takes tokens [16w, 16w + 16) of the tile, all 16 heads
+    // partial scores of 16 tokens over half of the 576 dims
     {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      const unsigned char* krow = kv + (wave * 16 + r16) * kLdsRow + g * 16;
+      const unsigned char* krow = kv + (tt * 16 + r16) * kLdsRow + kh * kKHalf * 64 + g * 16;
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
+      for (int ks = 0; ks < kKHalf; ++ks) {
         const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + ks * 64));
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kf, s, 0, 0, 0);
       }
-      const int col = wave * 16 + r16;
-      const bool valid = tile * kTile + col < K;
+      float* sck = sc + kh * kHeads * kTile;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sc[(4 * g + j) * kTile + col] = valid ? s[j] * a.scale_log2 : -INFINITY;
+      for (int j = 0; j < 4; ++j) sck[(4 * g + j) * kTile + tt * 16 + r16] = s[j];
     }
     __syncthreads();
 
-    // online softmax: head h = tid / 16, tokens 4*(tid % 16) .. +3
+    // online softmax: head h = tid / 32, tokens 2*(tid % 32) .. +1
     {
-      const int h = tid >> 4, c4 = (tid & 15) * 4;
-      const float x0 = sc[h * kTile + c4 + 0], x1 = sc[h * kTile + c4 + 1];
-      const float x2 = sc[h * kTile + c4 + 2], x3 = sc[h * kTile + c4 + 3];
-      float mx = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+      const int h = tid >> 5, c2 = (tid & 31) * 2;
+      const int tok0 = tile * kTile + c2;
+      const float* s0 = sc + h * kTile + c2;
+      const float* s1 = sc + kHeads * kTile + h * kTile + c2;
+      const float x0 = tok0 < K ? (s0[0] + s1[0]) * a.scale_log2 : -INFINITY;
+      const float x1 = tok0 + 1 < K ? (s0[1] + s1[1]) * a.scale_log2 : -INFINITY;
+      float mx = fmaxf(x0, x1);
 #pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);
       const float p0 = exp2f(x0 - m_new), p1 = exp2f(x1 - m_new);
-      const float p2 = exp2f(x2 - m_new), p3 = exp2f(x3 - m_new);
-      float ps = (p0 + p1) + (p2 + p3);
+      float ps = p0 + p1;
 #pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) ps += __shfl_xor(ps, o);
+      for (int o = 16; o >= 1; o >>= 1) ps += __shfl_xor(ps, o);
       l_run = l_run * alpha + ps;
       m_run = m_new;
-      uint16_t* prow = pb + h * kPRow + c4;
-      prow[0] = f32_to_bf16_rne(p0);
-      prow[1] = f32_to_bf16_rne(p1);
-      prow[2] = f32_to_bf16_rne(p2);
-      prow[3] = f32_to_bf16_rne(p3);
-      if ((tid & 15) == 0) alpha_s[h] = alpha;
+      *reinterpret_cast<uint32_t*>(pb + h * kPRow + c2) =
+          (uint32_t)f32_to_bf16_rne(p0) | ((uint32_t)f32_to_bf16_rne(p1) << 16);
+      if ((tid & 31) == 0) alpha_s[h] = alpha;
     }
     __syncthreads();
 
-    // P.V: wave w owns value columns [128w, 128w + 128) as 8 MFMA column tiles
+    // P.V: wave w owns value columns [64w, 64w + 64) as 4 MFMA column tiles
     {
       float al[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) al[j] = alpha_s[4 * g + j];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[nt][j] *= al[j];
 #pragma unroll
@@ -506,8 +514,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
             as_bf16x8(*reinterpret_cast<const u32x4*>(pb + r16 * kPRow + kk * 32 + g * 8));
         const unsigned char* vbase = kv + (kk * 32 + g * 8) * kLdsRow;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const int e = wave * 128 + nt * 16 + r16;
+        for (int nt = 0; nt < 4; ++nt) {
+          const int e = wave * 64 + nt * 16 + r16;
           u16x8 vv;
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj)
@@ -524,69 +532,72 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     }
   }
 
-  // partials: acc lane holds O[h = 4g + j][e = 128w + 16nt + r16]
+  // partials: acc lane holds O[h = 4g + j][e = 64w + 16nt + r16]
   const long long part = (long long)b * a.splits + sp;
   float* po = a.part_o + part * kHeads * kVDim;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
+  for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) po[(4 * g + j) * kVDim + wave * 128 + nt * 16 + r16] = acc[nt][j];
-  if ((tid & 15) == 0) {
-    const int h = tid >> 4;
+    for (int j = 0; j < 4; ++j) po[(4 * g + j) * kVDim + wave * 64 + nt * 16 + r16] = acc[nt][j];
+  if ((tid & 31) == 0) {
+    const int h = tid >> 5;
     a.part_ml[(part * kHeads + h) * 2 + 0] = m_run;
     a.part_ml[(part * kHeads + h) * 2 + 1] = l_run;
   }
 }
 
-// Merge of the split partials of request b: out = sum_s 2^(m_s - M) O_s / L,
-// L = sum_s 2^(m_s - M) l_s, lse = (M + log2 L) * ln 2.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
+// Merge of the split partials of (request b, head h):
+// out = sum_s 2^(m_s - M) O_s / L, L = sum_s 2^(m_s - M) l_s, lse = (M + log2 L) * ln 2.
+// One workgroup of 128 threads per (b, h), 4 outputs per thread.
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const int32_t* __restrict__ counts,
                                                       uint16_t* __restrict__ out,
-                                                      float* __restrict__ lse, int splits) {
-  __shared__ float w[kMaxSplits * kHeads];
-  __shared__ float inv_l[kHeads];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  u32x4* ob = reinterpret_cast<u32x4*>(out + (long long)b * kHeads * kVDim);
-  if (counts[4 * b + 3] == 0) {
-    for (int i = tid; i < kHeads * kVDim / 8; i += blockDim.x) ob[i] = u32x4{0u, 0u, 0u, 0u};
-    if (lse != nullptr && tid < kHeads) lse[b * kHeads + tid] = -INFINITY;
+                                                      float* __restrict__ lse, int splits,
+                                                      int b0) {
+  __shared__ float w[kMaxSplits];
+  __shared__ float inv_l;
+  const int b = b0 + blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+  uint2* ob = reinterpret_cast<uint2*>(out + ((long long)b * kHeads + h) * kVDim);
+  if (counts[4 * b + 3] == 0) {   // invalid Top-K: zero output, lse = -inf
+    ob[tid] = make_uint2(0u, 0u);
+    if (lse != nullptr && tid == 0) lse[b * kHeads + h] = -INFINITY;
     return;
   }
   const float* ml = part_ml + (long long)b * splits * kHeads * 2;
-  if (tid < kHeads) {
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(s * kHeads + tid) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float ws = exp2f(ml[(s * kHeads + tid) * 2] - M);
-      w[s * kHeads + tid] = ws;
-      L += ws * ml[(s * kHeads + tid) * 2 + 1];
+  if (tid < 64) {   // one wave: max and weighted sum over the splits
+    float m = -INFINITY;
+    for (int s = tid; s < splits; s += 64) m = fmaxf(m, ml[(s * kHeads + h) * 2]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float l = 0.f;
+    for (int s = tid; s < splits; s += 64) {
+      const float ws = exp2f(ml[(s * kHeads + h) * 2] - m);
+      w[s] = ws;
+      l += ws * ml[(s * kHeads + h) * 2 + 1];
     }
-    inv_l[tid] = 1.f / L;
-    if (lse != nullptr) lse[b * kHeads + tid] = (M + log2f(L)) * 0.69314718055994531f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+    if (tid == 0) {
+      inv_l = 1.f / l;
+      if (lse != nullptr) lse[b * kHeads + h] = (m + log2f(l)) * 0.69314718055994531f;
+    }
   }
   __syncthreads();
-  const float* pob = part_o + (long long)b * splits * kHeads * kVDim;
-  for (int i8 = tid; i8 < kHeads * kVDim / 8; i8 += blockDim.x) {
-    const int h = (i8 * 8) / kVDim;
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) {
-      const float ws = w[s * kHeads + h];
-      const float4* src = reinterpret_cast<const float4*>(pob + (long long)s * kHeads * kVDim + i8 * 8);
-      const float4 x = src[0], y = src[1];
-      o[0] += ws * x.x; o[1] += ws * x.y; o[2] += ws * x.z; o[3] += ws * x.w;
-      o[4] += ws * y.x; o[5] += ws * y.y; o[6] += ws * y.z; o[7] += ws * y.w;
-    }
-    const float il = inv_l[h];
-    u32x4 r;
-    r[0] = (uint32_t)f32_to_bf16_rne(o[0] * il) | ((uint32_t)f32_to_bf16_rne(o[1] * il) << 16);
-    r[1] = (uint32_t)f32_to_bf16_rne(o[2] * il) | ((uint32_t)f32_to_bf16_rne(o[3] * il) << 16);
-    r[2] = (uint32_t)f32_to_bf16_rne(o[4] * il) | ((uint32_t)f32_to_bf16_rne(o[5] * il) << 16);
-    r[3] = (uint32_t)f32_to_bf16_rne(o[6] * il) | ((uint32_t)f32_to_bf16_rne(o[7] * il) << 16);
-    ob[i8] = r;
+  const float* pob = part_o + (long long)b * splits * kHeads * kVDim + h * kVDim + tid * 4;
+  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float ws = w[s];
+    const float4 x = *reinterpret_cast<const float4*>(pob + (long long)s * kHeads * kVDim);
+    o0 += ws * x.x;
+    o1 += ws * x.y;
+    o2 += ws * x.z;
+    o3 += ws * x.w;
   }
+  const float il = inv_l;
+  ob[tid] = make_uint2(
+      (uint32_t)f32_to_bf16_rne(o0 * il) | ((uint32_t)f32_to_bf16_rne(o1 * il) << 16),
+      (uint32_t)f32_to_bf16_rne(o2 * il) | ((uint32_t)f32_to_bf16_rne(o3 * il) << 16));
 }
 
 }  // namespace
@@ -663,26 +674,32 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const
   return hipGetLastError();
 }
 
-hipError_t launch_hit_gather(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s) {
-  dim3 grid((lay.K + kCopyRows - 1) / kCopyRows, lay.B);
+hipError_t launch_hit_gather(const Layout& lay, const DevPtrs& d, int layer, int b0, int nb,
+                             hipStream_t s) {
+  dim3 grid((lay.K + kCopyRows - 1) / kCopyRows, nb);
   hipLaunchKernelGGL(hit_gather_kernel, grid, dim3(kCopyThreads), 0, s,
                      reinterpret_cast<const u32x4*>(d.hot), reinterpret_cast<u32x4*>(d.cbuf),
-                     d.slot_of, d.counts, lay.L, layer, lay.S, lay.K);
+                     d.slot_of, d.counts, lay.L, layer, lay.S, lay.K, b0);
   return hipGetLastError();
 }
 
 hipError_t launch_miss_fetch(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
-                             hipStream_t s) {
-  dim3 grid((lay.K + kCopyRows - 1) / kCopyRows, lay.B);
+                             int b0, int nb, hipStream_t s) {
+  // fetch_blocks workgroups per group, spread evenly over its requests
+  int per_req = (lay.fetch_blocks + nb - 1) / nb;
+  const int max_per_req = (lay.K + kCopyRows - 1) / kCopyRows;
+  if (per_req > max_per_req) per_req = max_per_req;
+  if (per_req < 1) per_req = 1;
+  dim3 grid(per_req, nb);
   hipLaunchKernelGGL(miss_fetch_kernel, grid, dim3(kCopyThreads), 0, s,
                      reinterpret_cast<const u32x4*>(d.pool), reinterpret_cast<u32x4*>(d.hot),
                      reinterpret_cast<u32x4*>(d.cbuf), topk, d.miss_pos, d.victims, d.counts,
-                     lay.L, layer, (long long)lay.N, lay.S, lay.K);
+                     lay.L, layer, (long long)lay.N, lay.S, lay.K, b0);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t* q, float scale,
-                            hipStream_t s) {
+                            int b0, int nb, hipStream_t s) {
   AttnArgs a;
   a.cbuf = d.cbuf;
   a.q = q;
@@ -691,15 +708,16 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t*
   a.part_ml = d.part_ml;
   a.K = lay.K;
   a.splits = lay.splits;
+  a.b0 = b0;
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attention_kernel, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
+  hipLaunchKernelGGL(attention_kernel, dim3(lay.splits, nb), dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
-                          hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(lay.B), dim3(256), 0, s, d.part_o, d.part_ml, d.counts,
-                     out, lse, lay.splits);
+hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse, int b0,
+                          int nb, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(kHeads, nb), dim3(128), 0, s, d.part_o, d.part_ml,
+                     d.counts, out, lse, lay.splits, b0);
   return hipGetLastError();
 }
 
