@@ -1,8 +1,10 @@
 """Benchmark of the per-decode-step sparse KV assembly path on one MI355X.
 
 A step is one decode step of the whole hot path for every request and layer of
-the workload: slot lookup + sparse diff + LRU (diff_lru), hit gather (HBM),
-miss fetch + write-back (PCIe), split-K sparse MLA attention and combine.
+the workload: slot lookup + sparse diff + LRU (diff_lru), the index copy
+(gather: misses fetched from pinned host memory over PCIe and written back to
+the hot buffer, hits copied within HBM), split-K sparse MLA attention and the
+merge of its partials (combine).
 Inputs (host pool rows, Top-K streams, queries) are seeded and synthetic and
 are resident (pool in pinned host memory, the rest in HBM) before timing.
 
@@ -48,11 +50,11 @@ def parse():
     p.add_argument("--no-profile", action="store_true", help="skip per-kernel HIP events")
     p.add_argument("--breakdown-steps", type=int, default=8,
                    help="extra steps after the timed region with events around every kernel")
-    p.add_argument("--fetch-groups", type=int, default=0, help="0 = library's choice")
     p.add_argument("--fetch-blocks", type=int, default=0, help="0 = library's choice")
     p.add_argument("--attn-splits", type=int, default=0, help="0 = library's choice")
-    p.add_argument("--hit-gather-first", action="store_true",
-                   help="finish the hit gather before the miss fetch starts")
+    p.add_argument("--hit-blocks", type=int, default=0, help="0 = library's choice")
+    p.add_argument("--hits-first", action="store_true",
+                   help="hit-copy workgroups take the first grid indices of the gather")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (the known-size "
                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -163,8 +165,8 @@ def main():
           f"steps {args.warmup}+{args.steps}+{breakdown}", file=sys.stderr, flush=True)
 
     pool = kvs.Pool(B, L, N, S, K, scale=wl.scale, attn_splits=args.attn_splits,
-                    fetch_groups=args.fetch_groups, fetch_blocks=args.fetch_blocks,
-                    flags=kvs.KVS_FLAG_HIT_GATHER_FIRST if args.hit_gather_first else 0)
+                    fetch_blocks=args.fetch_blocks, hit_blocks=args.hit_blocks,
+                    flags=kvs.KVS_FLAG_HITS_FIRST if args.hits_first else 0)
     W.fill_pool(pool.host.array, wl)
     topk_np = W.topk_streams(wl, total)
     topk = torch.from_numpy(topk_np).cuda()                         # [T][L][B][K]
@@ -181,7 +183,7 @@ def main():
 
     # warm-up; the last warm-up step is timed per kernel to find the dominant kernel
     cold = None
-    dominant = "miss_fetch"
+    dominant = "gather"
     for t in range(args.warmup):
         probe = (not args.no_profile) and t == args.warmup - 1 and t > 0
         if probe:
@@ -233,12 +235,16 @@ def main():
     part_bytes = B * splits * 16 * (512 + 2) * 4
 
     def algorithmic(hit_l, miss_l):
-        """Algorithmic bytes (and flops) of one kvs_step call, per kernel."""
+        """Algorithmic bytes (and flops) of one kvs_step call, per kernel.
+
+        The gather is bound by the host link: its roofline bytes are the miss
+        rows read over PCIe; its HBM traffic (hit rows read and written, miss
+        rows written twice) is listed beside them.
+        """
         return {
             "diff_lru": {"bound": "hbm", "bytes": B * (16 * K + 4 * S) + 32 * miss_l},
-            "hit_gather": {"bound": "hbm", "bytes": 2 * ROW * hit_l},
-            "miss_fetch": {"bound": "pcie", "bytes": ROW * miss_l,
-                           "hbm_write_bytes": 2 * ROW * miss_l},
+            "gather": {"bound": "pcie", "bytes": ROW * miss_l,
+                       "hbm_bytes": 2 * ROW * hit_l + 2 * ROW * miss_l},
             "attention": {"bound": "hbm", "bytes": B * (K * ROW + 16 * 576 * 2) + part_bytes,
                           "flop": B * 2 * 16 * K * (576 + 512)},
             "combine": {"bound": "hbm", "bytes": part_bytes + B * 16 * 512 * 2},
@@ -265,8 +271,9 @@ def main():
                 tf = a["flop"] / per_call / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
                 k["tflops"] = round(tf, 2)
                 k["mfma_frac"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 5)
-            if "hbm_write_bytes" in a:
-                k["hbm_write_gbs"] = round(a["hbm_write_bytes"] / per_call / (avg_ms * 1e-3) / 1e9, 2)
+            if "hbm_bytes" in a:
+                k["hbm_bytes_per_launch"] = int(a["hbm_bytes"] / per_call)
+                k["hbm_gbs"] = round(a["hbm_bytes"] / per_call / (avg_ms * 1e-3) / 1e9, 2)
             res[name] = k
         return res
 
@@ -288,6 +295,11 @@ def main():
                     "bytes_per_launch": dom["bytes_per_launch"]}
         if dom["bound"] == "pcie":
             roofline["frac_of_measured_h2d"] = round(dom["achieved_gbs"] / h2d, 4)
+        if "hbm_bytes" in alg[dominant]:
+            # what the HBM counters should read if nothing is re-read: the kernel's
+            # algorithmic HBM bytes plus the host rows it pulls through the L2
+            roofline["algorithmic_traffic"] = int((alg[dominant]["hbm_bytes"]
+                                                   + alg[dominant]["bytes"]) / dom["launches_per_call"])
 
     # parity of sampled requests against the oracle, plus the CPU baseline
     cpu = None
@@ -316,8 +328,8 @@ def main():
                   "attn_max_abs": round(max_abs, 6), "attn_max_rel_l2": round(max_rel, 6),
                   "pass": bool(state_ok and max_abs <= 2e-2 and max_rel <= 1e-2)}
 
-    hbm_bytes_step = (sum(alg[k]["bytes"] for k in ("diff_lru", "hit_gather", "attention", "combine"))
-                      + alg["miss_fetch"]["hbm_write_bytes"]) * L
+    hbm_bytes_step = (alg["diff_lru"]["bytes"] + alg["gather"]["hbm_bytes"]
+                      + alg["attention"]["bytes"] + alg["combine"]["bytes"]) * L
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -334,8 +346,8 @@ def main():
         "config": {"workload": wl.name, "batch": B, "layers": L, "context": N, "slots": S,
                    "topk": K, "fresh_rate": wl.fresh_rate, "fresh_dist": wl.dist,
                    "heads": 16, "head_dim": 576, "v_dim": 512, "attn_splits": splits,
-                   "fetch_groups": pool.sizes.fetch_groups, "fetch_blocks": pool.sizes.fetch_blocks,
-                   "hit_gather_first": bool(args.hit_gather_first)},
+                   "fetch_blocks": pool.sizes.fetch_blocks, "hit_blocks": args.hit_blocks,
+                   "hits_first": bool(args.hits_first)},
         "decode_steps_per_s": round(1e3 / ms_step, 2),
         "cold_step_ms": None if cold is None else round(cold, 4),
         "miss_rate": round(miss_rate, 5),

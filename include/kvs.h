@@ -73,11 +73,11 @@ extern "C" {
 
 /* Indices of the per-kernel times in kvs_kernel_times.ms_total. */
 #define KVS_KERNEL_DIFF_LRU 0   /* lookup + sparse diff + LRU + map update */
-#define KVS_KERNEL_HIT_GATHER 1 /* hot buffer -> compute buffer (HBM) */
-#define KVS_KERNEL_MISS_FETCH 2 /* host pool -> compute buffer + hot buffer (PCIe) */
-#define KVS_KERNEL_ATTENTION 3  /* split-K sparse MLA decode (MFMA) */
-#define KVS_KERNEL_COMBINE 4    /* merge of the split-K partials */
-#define KVS_NUM_KERNELS 5
+#define KVS_KERNEL_GATHER 1     /* index copy: misses host -> compute buffer + hot buffer
+                                   (PCIe) and hits hot buffer -> compute buffer (HBM) */
+#define KVS_KERNEL_ATTENTION 2  /* split-K sparse MLA decode (MFMA) */
+#define KVS_KERNEL_COMBINE 3    /* merge of the split-K partials */
+#define KVS_NUM_KERNELS 4
 
 /*
  * Shape of a pool.  B requests x L layers = B*L units; each unit has its own
@@ -94,16 +94,14 @@ typedef struct kvs_config {
   int32_t v_dim;        /* must be KVS_V_DIM */
   float scale;          /* softmax scale > 0, e.g. 1/sqrt(576) */
   int32_t attn_splits;  /* token splits per request in attention, 1..64; 0 = library's choice */
-  int32_t fetch_groups; /* request groups one step is pipelined over: the attention of group g
-                           runs while the misses of group g+1 are fetched; 1..64, 0 = library's
-                           choice */
-  int32_t fetch_blocks; /* workgroups of one group's miss fetch, 1..65535; 0 = library's choice */
-  int32_t flags;        /* KVS_FLAG_* bits, 0 = default schedule */
+  int32_t fetch_blocks; /* workgroups that fetch misses over PCIe, 1..65535; 0 = library's choice */
+  int32_t hit_blocks;   /* workgroups that copy hits within HBM, 1..65535; 0 = library's choice */
+  int32_t flags;        /* KVS_FLAG_* bits; 0 = default */
 } kvs_config;
 
-/* kvs_config.flags: run the hit gather to completion before the miss fetch
- * starts (default: the two run concurrently on two streams). */
-#define KVS_FLAG_HIT_GATHER_FIRST 1
+/* kvs_config.flags: give the hit-copy workgroups the first grid indices of the
+ * gather launch (default: the PCIe fetch workgroups come first). */
+#define KVS_FLAG_HITS_FIRST 1
 
 /* Bytes each caller buffer must hold (see kvs_buffers). */
 typedef struct kvs_sizes {
@@ -113,7 +111,6 @@ typedef struct kvs_sizes {
   uint64_t cbuf_bytes;      /* B*K*576*2: compute buffer of one step, device */
   uint64_t scratch_bytes;   /* per-step lists and attention partials, device */
   int32_t attn_splits;      /* the split count these sizes assume */
-  int32_t fetch_groups;     /* resolved kvs_config.fetch_groups */
   int32_t fetch_blocks;     /* resolved kvs_config.fetch_blocks */
 } kvs_sizes;
 
@@ -198,7 +195,8 @@ int kvs_publish(kvs_pool* pool, int32_t req, int32_t layer, int64_t first_tok,
                 int64_t n_tok, const void* rows);
 
 /* Lifecycle "fetch + write-back" and the Top-K attention of one layer for all
- * B requests.  Enqueued on `stream`; nothing is synchronised.
+ * B requests: four kernel launches on `stream`, no host synchronisation, no
+ * device-to-host copy, no other stream.
  *   topk [B][K] int32, device: request b's Top-K token indices, unique, in [0, N).
  *   q    [B][16][576] bf16, device: queries.
  *   out  [B][16][512] bf16, device: attention output.
@@ -214,9 +212,9 @@ int kvs_step(kvs_pool* pool, int32_t layer, const int32_t* topk, const void* q,
  * LRU order 0..S-1).  Its step counters keep running.  Enqueued on `stream`. */
 int kvs_free_request(kvs_pool* pool, int32_t req, void* stream);
 
-/* Synchronise `stream` and the pool's internal stream, then return the first
- * device-detected error (KVS_ERANGE / KVS_EDUP) since the last call, or KVS_OK,
- * and clear it.  `stats` (may be NULL) receives the running totals. */
+/* Synchronise `stream`, then return the first device-detected error
+ * (KVS_ERANGE / KVS_EDUP) since the last call, or KVS_OK, and clear it.
+ * `stats` (may be NULL) receives the running totals. */
 int kvs_sync_status(kvs_pool* pool, void* stream, kvs_step_stats* stats);
 
 /* Synchronising copy of unit (req, layer)'s state into host arrays (tests). */
@@ -231,7 +229,7 @@ int kvs_profile_begin(kvs_pool* pool, int32_t max_steps, uint32_t kernel_mask);
 /* Synchronise and report the recorded times; stops recording. */
 int kvs_profile_end(kvs_pool* pool, kvs_kernel_times* out);
 
-/* Destroy the pool's internal streams and events.  Caller buffers are untouched. */
+/* Destroy the pool's timing events and host-side state.  Caller buffers are untouched. */
 int kvs_release(kvs_pool* pool);
 
 /* Static description of a return code. */

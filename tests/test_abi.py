@@ -71,8 +71,8 @@ def test_query_sizes_arithmetic():
     # maps: tok2slot + slot2tok + last_used + order (+ small counters)
     assert s.meta_bytes >= 64 * (16384 * 4 + 4096 * 10)
     assert s.meta_bytes < 64 * (16384 * 4 + 4096 * 10) + 64 * 64 + 4096
-    assert s.attn_splits == 8
-    per = 4 * 64 * 2048 * 4 + 64 * 16 + 64 * 8 * 16 * (512 + 2) * 4
+    assert s.attn_splits == 4
+    per = 4 * 64 * 2048 * 4 + 64 * 16 + 64 * 4 * 16 * (512 + 2) * 4
     assert per <= s.scratch_bytes < per + 8 * 256
 
 
@@ -81,7 +81,7 @@ def test_query_sizes_arithmetic():
     dict(context=100, topk=200, slots=300), dict(slots=16385), dict(topk=8193, slots=9000),
     dict(heads=8), dict(head_dim=512), dict(v_dim=576), dict(scale=0.0),
     dict(scale=float("inf")), dict(attn_splits=65), dict(flags=2), dict(context=2**31),
-    dict(fetch_groups=65), dict(fetch_groups=-1), dict(fetch_blocks=-1), dict(fetch_blocks=65536),
+    dict(fetch_blocks=-1), dict(fetch_blocks=65536), dict(hit_blocks=-1), dict(hit_blocks=70000),
     dict(attn_splits=33),   # more splits than 64-token tiles (K = 2048 -> 32)
 ])
 def test_bad_configs_rejected(bad):
@@ -129,17 +129,9 @@ def test_strerror():
     assert "HIP" in kvs.strerror(kvs.KVS_EHIP_BASE - 2)
 
 
-def test_pipelining_knobs_resolve():
+def test_fetch_blocks_resolve():
+    s = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096, topk=2048))
+    assert s.fetch_blocks == 256
     s = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096, topk=2048,
-                                        fetch_groups=4, fetch_blocks=128))
-    assert (s.fetch_groups, s.fetch_blocks) == (4, 128)
-    assert s.attn_splits == 32          # sized for one 16-request group
-    s = kvs.query_sizes(kvs.make_config(batch=3, layers=1, context=4096, slots=512, topk=256,
-                                        fetch_groups=8))
-    assert s.fetch_groups == 3          # never more groups than requests
-    s = kvs.query_sizes(kvs.make_config(batch=10, layers=1, context=4096, slots=512, topk=256,
-                                        fetch_groups=4))
-    assert s.fetch_groups == 4          # groups of 3, 3, 3, 1
-    s = kvs.query_sizes(kvs.make_config(batch=9, layers=1, context=4096, slots=512, topk=256,
-                                        fetch_groups=4))
-    assert s.fetch_groups == 3          # groups of 3: a fourth group would be empty
+                                        fetch_blocks=128))
+    assert s.fetch_blocks == 128

@@ -26,7 +26,8 @@ KVS_EHIP_BASE = -1000
 
 HEADS, HEAD_DIM, V_DIM = 16, 576, 512
 ROW_BYTES = HEAD_DIM * 2
-KERNEL_NAMES = ("diff_lru", "hit_gather", "miss_fetch", "attention", "combine")
+KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine")
+KVS_FLAG_HITS_FIRST = 1
 
 # Every exported symbol of include/kvs.h.
 EXPORTS = (
@@ -41,8 +42,8 @@ class kvs_config(ctypes.Structure):
         ("batch", ctypes.c_int32), ("layers", ctypes.c_int32), ("context", ctypes.c_int64),
         ("slots", ctypes.c_int32), ("topk", ctypes.c_int32), ("heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("scale", ctypes.c_float),
-        ("attn_splits", ctypes.c_int32), ("fetch_groups", ctypes.c_int32),
-        ("fetch_blocks", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("attn_splits", ctypes.c_int32), ("fetch_blocks", ctypes.c_int32),
+        ("hit_blocks", ctypes.c_int32), ("flags", ctypes.c_int32),
     ]
 
 
@@ -51,7 +52,7 @@ class kvs_sizes(ctypes.Structure):
         ("host_pool_bytes", ctypes.c_uint64), ("hot_bytes", ctypes.c_uint64),
         ("meta_bytes", ctypes.c_uint64), ("cbuf_bytes", ctypes.c_uint64),
         ("scratch_bytes", ctypes.c_uint64), ("attn_splits", ctypes.c_int32),
-        ("fetch_groups", ctypes.c_int32), ("fetch_blocks", ctypes.c_int32),
+        ("fetch_blocks", ctypes.c_int32),
     ]
 
 
@@ -142,16 +143,12 @@ def _check(rc: int, what: str) -> int:
     return rc
 
 
-KVS_FLAG_HIT_GATHER_FIRST = 1
-
-
-def make_config(batch, layers, context, slots, topk, scale=None, attn_splits=0, fetch_groups=0,
-                fetch_blocks=0, flags=0, heads=HEADS, head_dim=HEAD_DIM,
-                v_dim=V_DIM) -> kvs_config:
+def make_config(batch, layers, context, slots, topk, scale=None, attn_splits=0, fetch_blocks=0,
+                hit_blocks=0, flags=0, heads=HEADS, head_dim=HEAD_DIM, v_dim=V_DIM) -> kvs_config:
     if scale is None:
         scale = 1.0 / float(np.sqrt(head_dim))
     return kvs_config(batch, layers, context, slots, topk, heads, head_dim, v_dim, scale,
-                      attn_splits, fetch_groups, fetch_blocks, flags)
+                      attn_splits, fetch_blocks, hit_blocks, flags)
 
 
 def query_sizes(cfg: kvs_config) -> kvs_sizes:
@@ -195,11 +192,11 @@ class Pool:
     """
 
     def __init__(self, batch, layers, context, slots, topk, scale=None, attn_splits=0,
-                 fetch_groups=0, fetch_blocks=0, flags=0, host: Optional[HostPool] = None,
+                 fetch_blocks=0, hit_blocks=0, flags=0, host: Optional[HostPool] = None,
                  device=None, stream=None):
         import torch
         self.cfg = make_config(batch, layers, context, slots, topk, scale, attn_splits,
-                               fetch_groups, fetch_blocks, flags)
+                               fetch_blocks, hit_blocks, flags)
         self.sizes = query_sizes(self.cfg)
         self.B, self.L, self.N, self.S, self.K = batch, layers, context, slots, topk
         self.device = torch.device("cuda" if device is None else device)

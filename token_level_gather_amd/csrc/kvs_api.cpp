@@ -1,7 +1,7 @@
 // Host runtime behind the C ABI in include/kvs.h: configuration and buffer
-// validation, host-pool allocation, launch orchestration of one decode step on
-// the caller's stream plus one internal stream (fork/join by events), status
-// and statistics readback, and per-kernel event timing.
+// validation, host-pool allocation, launch orchestration of one decode step
+// (four kernels on the caller's stream), status and statistics readback, and
+// per-kernel event timing.
 //
 // The request lifecycle follows "XM-Sparse" (HiSparse integration section):
 // publish = kvs_publish, fetch + write-back = kvs_step, free = kvs_free_request.
@@ -28,33 +28,28 @@ int make_layout(const kvs_config* c, Layout* lay) {
     return KVS_EINVAL;
   if (!(c->scale > 0.f) || !isfinite(c->scale)) return KVS_EINVAL;
   if (c->attn_splits < 0 || c->attn_splits > 64) return KVS_EINVAL;
-  if (c->fetch_groups < 0 || c->fetch_groups > 64 || c->fetch_blocks < 0 ||
-      c->fetch_blocks > 65535)
-    return KVS_EINVAL;
-  if ((c->flags & ~KVS_FLAG_HIT_GATHER_FIRST) != 0) return KVS_EINVAL;
+  if (c->fetch_blocks < 0 || c->fetch_blocks > 65535) return KVS_EINVAL;
+  if (c->hit_blocks < 0 || c->hit_blocks > 65535) return KVS_EINVAL;
+  if ((c->flags & ~KVS_FLAG_HITS_FIRST) != 0) return KVS_EINVAL;
   if ((int64_t)c->batch * c->layers > 0x7fffffffLL) return KVS_EINVAL;
 
   const uint64_t B = c->batch, L = c->layers, N = c->context, S = c->slots, K = c->topk;
   const uint64_t U = B * L;
-  int groups = c->fetch_groups == 0 ? 1 : c->fetch_groups;
-  if (groups > c->batch) groups = c->batch;
-  const int group_size = (int)((B + groups - 1) / groups);
-  groups = (int)((B + group_size - 1) / group_size);   // no empty group
   const int ntiles = (int)((K + 63) / 64);
   int splits = c->attn_splits;
   if (splits == 0) {
-    // about two attention workgroups per compute unit (256 CUs) for one group,
-    // at least one 64-token tile each
-    splits = (int)((512 + group_size - 1) / group_size);
+    // one attention workgroup per compute unit (256 CUs), at least one
+    // 64-token tile each
+    splits = (int)((256 + B - 1) / B);
     if (splits > ntiles) splits = ntiles;
     if (splits > 64) splits = 64;
     if (splits < 1) splits = 1;
   } else if (splits > ntiles) {
     return KVS_EINVAL;
   }
-  // 512 fetch workgroups per group (2 per CU) keep the host link saturated;
-  // more only adds outstanding PCIe reads that slow concurrent HBM traffic
-  int fetch_blocks = c->fetch_blocks == 0 ? 512 : c->fetch_blocks;
+  // 256 fetch workgroups (1 per CU) keep the host link saturated; more only
+  // add outstanding PCIe reads, which slow the HBM traffic beside them
+  const int fetch_blocks = c->fetch_blocks == 0 ? 256 : c->fetch_blocks;
 
   lay->B = c->batch;
   lay->L = c->layers;
@@ -62,9 +57,8 @@ int make_layout(const kvs_config* c, Layout* lay) {
   lay->K = c->topk;
   lay->N = c->context;
   lay->splits = splits;
-  lay->groups = groups;
-  lay->group_size = group_size;
   lay->fetch_blocks = fetch_blocks;
+  lay->hit_blocks = c->hit_blocks;
   lay->flags = c->flags;
 
   uint64_t o = 0;
@@ -104,10 +98,6 @@ struct kvs_pool {
   DevPtrs d;
   uint8_t* host_pool;       // host address of the pool (for kvs_publish)
   int device;
-  hipStream_t side;         // miss fetch runs here, beside the hit gather
-  hipEvent_t ev_fork;       // main stream -> side stream (after diff_lru, or the hit gather)
-  hipEvent_t ev_group[64];  // side stream -> main stream, one per request group
-  hipEvent_t ev_join;       // last group's event: all side-stream work of the last step
   // per-kernel timing: a pool of event pairs, one pair per recorded launch
   std::vector<hipEvent_t> prof_ev;
   std::vector<int> prof_kernel;
@@ -126,13 +116,9 @@ static int hip_err(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP_BA
     if (e_ != hipSuccess) return hip_err(e_);   \
   } while (0)
 
-// Frees the pool's streams and events (handles left null by a failed create are skipped).
+// Frees the pool's timing events and the pool itself.
 static void destroy_pool(kvs_pool* p) {
   for (hipEvent_t ev : p->prof_ev) (void)hipEventDestroy(ev);
-  if (p->ev_fork != nullptr) (void)hipEventDestroy(p->ev_fork);
-  for (int g = 0; g < 64; ++g)
-    if (p->ev_group[g] != nullptr) (void)hipEventDestroy(p->ev_group[g]);
-  if (p->side != nullptr) (void)hipStreamDestroy(p->side);
   delete p;
 }
 
@@ -168,7 +154,6 @@ int kvs_query_sizes(const kvs_config* cfg, kvs_sizes* out) {
   out->cbuf_bytes = B * K * kRowBytes;
   out->scratch_bytes = lay.scratch_bytes;
   out->attn_splits = lay.splits;
-  out->fetch_groups = lay.groups;
   out->fetch_blocks = lay.fetch_blocks;
   return KVS_OK;
 }
@@ -257,11 +242,6 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
 
   hipError_t e = hipGetDevice(&p->device);
   if (e == hipSuccess) e = prepare_kernels();
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming);
-  for (int g = 0; g < p->lay.groups && e == hipSuccess; ++g)
-    e = hipEventCreateWithFlags(&p->ev_group[g], hipEventDisableTiming);
-  if (e == hipSuccess) p->ev_join = p->ev_group[p->lay.groups - 1];
   if (e == hipSuccess)
     e = launch_init_units(L, d, 0, L.B * L.L, /*reset_counters=*/true, (hipStream_t)stream);
   if (e != hipSuccess) {
@@ -289,44 +269,22 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
   const hipStream_t s = (hipStream_t)stream;
   const Layout& L = p->lay;
   const DevPtrs& d = p->d;
-  const bool hit_first = (L.flags & KVS_FLAG_HIT_GATHER_FIRST) != 0;
-  // lookup, diff, LRU and map update for every request of the layer
+  // lookup, sparse diff, LRU and map update for every request of the layer
   KVS_TRY_HIP(timed(p, KVS_KERNEL_DIFF_LRU, s, [&] { return launch_diff_lru(L, d, layer, topk, s); }));
-  if (hit_first)
-    KVS_TRY_HIP(timed(p, KVS_KERNEL_HIT_GATHER, s,
-                      [&] { return launch_hit_gather(L, d, layer, 0, L.B, s); }));
-  // misses of each request group on the side stream, in group order
-  KVS_TRY_HIP(hipEventRecord(p->ev_fork, s));
-  KVS_TRY_HIP(hipStreamWaitEvent(p->side, p->ev_fork, 0));
-  for (int g = 0; g < L.groups; ++g) {
-    const int b0 = g * L.group_size;
-    const int nb = b0 + L.group_size <= L.B ? L.group_size : L.B - b0;
-    KVS_TRY_HIP(timed(p, KVS_KERNEL_MISS_FETCH, p->side,
-                      [&] { return launch_miss_fetch(L, d, layer, topk, b0, nb, p->side); }));
-    KVS_TRY_HIP(hipEventRecord(p->ev_group[g], p->side));
-  }
-  // hits of every request on the main stream, beside the fetch
-  if (!hit_first)
-    KVS_TRY_HIP(timed(p, KVS_KERNEL_HIT_GATHER, s,
-                      [&] { return launch_hit_gather(L, d, layer, 0, L.B, s); }));
-  // attention of group g as soon as its misses have landed
-  for (int g = 0; g < L.groups; ++g) {
-    const int b0 = g * L.group_size;
-    const int nb = b0 + L.group_size <= L.B ? L.group_size : L.B - b0;
-    KVS_TRY_HIP(hipStreamWaitEvent(s, p->ev_group[g], 0));
-    KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s, [&] {
-      return launch_attention(L, d, (const uint16_t*)q, p->cfg.scale, b0, nb, s);
-    }));
-    KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
-                      [&] { return launch_combine(L, d, (uint16_t*)out, lse, b0, nb, s); }));
-  }
+  // index copy: misses over PCIe (fetch + write-back) and hits within HBM
+  KVS_TRY_HIP(timed(p, KVS_KERNEL_GATHER, s, [&] { return launch_gather(L, d, layer, topk, s); }));
+  // Top-K sparse attention over the compute buffer
+  KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s, [&] {
+    return launch_attention(L, d, (const uint16_t*)q, p->cfg.scale, s);
+  }));
+  KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
+                    [&] { return launch_combine(L, d, (uint16_t*)out, lse, s); }));
   if (p->prof_steps < p->prof_max_steps) ++p->prof_steps;
   return KVS_OK;
 }
 
 int kvs_free_request(kvs_pool* p, int32_t req, void* stream) {
   if (p == nullptr || req < 0 || req >= p->lay.B) return KVS_EINVAL;
-  KVS_TRY_HIP(hipStreamWaitEvent((hipStream_t)stream, p->ev_join, 0));
   return hip_err(launch_init_units(p->lay, p->d, req * p->lay.L, p->lay.L, false,
                                    (hipStream_t)stream));
 }
@@ -334,7 +292,6 @@ int kvs_free_request(kvs_pool* p, int32_t req, void* stream) {
 int kvs_sync_status(kvs_pool* p, void* stream, kvs_step_stats* stats) {
   if (p == nullptr) return KVS_EINVAL;
   const hipStream_t s = (hipStream_t)stream;
-  KVS_TRY_HIP(hipStreamSynchronize(p->side));
   KVS_TRY_HIP(hipStreamSynchronize(s));
   int32_t status[4];
   KVS_TRY_HIP(hipMemcpyAsync(status, p->d.status, sizeof(status), hipMemcpyDeviceToHost, s));
@@ -370,7 +327,6 @@ int kvs_debug_read_state(kvs_pool* p, int32_t req, int32_t layer, void* stream,
   const Layout& L = p->lay;
   const DevPtrs& d = p->d;
   const long long u = (long long)req * L.L + layer;
-  KVS_TRY_HIP(hipStreamSynchronize(p->side));
   auto get = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
     if (dst == nullptr) return hipSuccess;
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
@@ -397,8 +353,7 @@ int kvs_debug_read_state(kvs_pool* p, int32_t req, int32_t layer, void* stream,
 int kvs_profile_begin(kvs_pool* p, int32_t max_steps, uint32_t kernel_mask) {
   if (p == nullptr || max_steps < 0) return KVS_EINVAL;
   if ((kernel_mask >> KVS_NUM_KERNELS) != 0) return KVS_EINVAL;
-  const int per_step = 2 + 3 * p->lay.groups;   // diff, hit, groups x (miss, attention, combine)
-  const size_t need = (size_t)max_steps * per_step;
+  const size_t need = (size_t)max_steps * KVS_NUM_KERNELS;
   while (p->prof_ev.size() < need * 2) {
     hipEvent_t e;
     KVS_TRY_HIP(hipEventCreate(&e));
@@ -434,9 +389,8 @@ int kvs_profile_end(kvs_pool* p, kvs_kernel_times* out) {
 
 int kvs_release(kvs_pool* p) {
   if (p == nullptr) return KVS_EINVAL;
-  const hipError_t e = hipStreamSynchronize(p->side);
   destroy_pool(p);
-  return hip_err(e);
+  return KVS_OK;
 }
 
 const char* kvs_strerror(int code) {

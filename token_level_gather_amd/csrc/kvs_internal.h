@@ -18,9 +18,8 @@ constexpr int kVDim = KVS_V_DIM;                 // 512
 // Byte offsets of every array inside the caller's meta and scratch buffers.
 struct Layout {
   int32_t B, L, S, K, splits;
-  int32_t groups;        // request groups a step is pipelined over
-  int32_t group_size;    // requests per group (the last group may be smaller)
-  int32_t fetch_blocks;  // workgroups of one group's miss fetch
+  int32_t fetch_blocks;  // miss-fetch workgroups of the gather launch
+  int32_t hit_blocks;    // hit-copy workgroups of the gather launch (0 = one per 32 positions)
   int32_t flags;
   int64_t N;
   // meta (persistent state)
@@ -77,15 +76,12 @@ hipError_t launch_init_units(const Layout& lay, const DevPtrs& d, int unit_begin
                              int unit_count, bool reset_counters, hipStream_t s);
 hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer,
                            const int32_t* topk, hipStream_t s);
-// The gather, attention and combine launchers cover requests [b0, b0 + nb).
-hipError_t launch_hit_gather(const Layout& lay, const DevPtrs& d, int layer, int b0, int nb,
-                             hipStream_t s);
-hipError_t launch_miss_fetch(const Layout& lay, const DevPtrs& d, int layer,
-                             const int32_t* topk, int b0, int nb, hipStream_t s);
+hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
+                         hipStream_t s);
 hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t* q,
-                            float scale, int b0, int nb, hipStream_t s);
-hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out,
-                          float* lse, int b0, int nb, hipStream_t s);
+                            float scale, hipStream_t s);
+hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
+                          hipStream_t s);
 hipError_t launch_clear_status(const DevPtrs& d, hipStream_t s);
 
 }  // namespace kvs

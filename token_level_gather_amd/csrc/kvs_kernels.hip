@@ -1,16 +1,16 @@
 // gfx950 (MI355X) kernels of the per-decode-step sparse KV assembly path.
 //
-// One kvs_step of layer l runs, for the B units (b, l):
-//   diff_lru    one workgroup per unit: slot lookup + validation, sparse diff
-//               (misses compacted in Top-K order with wave ballots and a
-//               workgroup prefix sum), hit touch, LRU victim choice from an
-//               LDS copy of the unit's LRU order array, map update.
-//   hit_gather  hot buffer -> compute buffer for the hits (HBM to HBM).
-//   miss_fetch  host pool -> compute buffer and hot buffer for the misses,
-//               by direct loads from pinned host memory over PCIe.
-//   attention   split-K sparse MLA decode over the K gathered rows:
-//               v_mfma_f32_16x16x32_bf16 for Q.K^T and P.V, fp32 online softmax.
-//   combine     merges the split partials, writes bf16 out and fp32 lse.
+// One kvs_step of layer l runs four launches for the B units (b, l):
+//   diff_lru   one workgroup per unit: slot lookup + validation, sparse diff
+//              (misses compacted in Top-K order with wave ballots and a
+//              workgroup prefix sum), hit touch, LRU victim choice from an
+//              LDS copy of the unit's LRU order array, map update.
+//   gather     the index copy: miss rows read from pinned host memory over
+//              PCIe into the compute buffer and the victim slots, hit rows
+//              copied from the hot buffer to the compute buffer, in one grid.
+//   attention  split-K sparse MLA decode over the K gathered rows:
+//              v_mfma_f32_16x16x32_bf16 for Q.K^T and P.V, fp32 online softmax.
+//   combine    merges the split partials, writes bf16 out and fp32 lse.
 //
 // Passages: index mapping / host pool / device cache / index-copy assembly
 // ("Sparse Attention-Driven KVCache Management for Domestic AI Supernodes",
@@ -287,80 +287,108 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ gathers
+// ------------------------------------------------------------------ gather
 constexpr int kCopyThreads = 256;
-constexpr int kCopyRows = 32;                                   // rows per block
-constexpr int kCopyItems = kCopyRows * kRowChunks / kCopyThreads;  // 9 chunks / thread
-static_assert(kCopyItems * kCopyThreads == kCopyRows * kRowChunks, "copy tiling");
+constexpr int kCopyRows = 32;                                   // rows per block iteration
+constexpr int kCopyItems = kRowChunks / 8;                      // 9 chunks / thread
+static_assert(kCopyRows * 8 == kCopyThreads && kCopyItems * 8 == kRowChunks, "copy tiling");
 
-// Hits: cbuf[b][i] = hot[b][l][slot_of[b][i]] for every hit position i.
-__global__ __launch_bounds__(kCopyThreads) void hit_gather_kernel(
-    const u32x4* __restrict__ hot, u32x4* __restrict__ cbuf, const int32_t* __restrict__ slot_of,
-    const int32_t* __restrict__ counts, int L, int layer, int S, int K, int b0) {
-  const int b = b0 + blockIdx.y;
-  if (counts[4 * b + 3] == 0) return;
-  const long long u = (long long)b * L + layer;
-  const int i0 = blockIdx.x * kCopyRows;
-  u32x4 v[kCopyItems];
-  long long dst[kCopyItems];
+struct GatherArgs {
+  const u32x4* pool;       // host pool (pinned, GPU-mapped) [B][L][N] rows
+  u32x4* hot;              // [B][L][S] rows
+  u32x4* cbuf;             // [B][K] rows
+  const int32_t* topk;     // [B][K]
+  const int32_t* slot_of;  // [B][K]
+  const int32_t* miss_pos; // [B][K]
+  const int32_t* victims;  // [B][K]
+  const int32_t* counts;   // [B][4]
+  long long N;
+  int S, K, L, B, layer;
+  int fetch_per_req;       // miss-role workgroups per request
+  int fetch_wgs;           // fetch_per_req * B
+  int hit_wgs;             // hit-role workgroups (each loops over 32-position groups)
+  int hits_first;          // 0: fetch workgroups take the first grid indices; 1: hit ones do
+};
+
+// The index copy of one layer.  Workgroups [0, fetch_wgs) fetch misses: row =
+// pool[b][l][tok_j] read straight from pinned host memory over PCIe, written to
+// cbuf[b][miss_pos_j] and to the victim slot hot[b][l][v_j].  The remaining
+// workgroups copy hits hot[b][l][slot_of_i] -> cbuf[b][i] within HBM.  One
+// launch keeps both on one stream; the fetch workgroups come first so the host
+// link starts as early as possible.  Hit slots and victim slots are disjoint,
+// so the two roles never touch the same hot row.
+__global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
+  const int K = a.K;
+  const int id = a.hits_first ? ((int)blockIdx.x + a.fetch_wgs) % (a.fetch_wgs + a.hit_wgs)
+                              : (int)blockIdx.x;
+  if (id < a.fetch_wgs) {
+    // fetch role: 32 rows per workgroup pass; chunk c = 256 j + thread of the
+    // pass's 32 x 72 chunks, so each wave instruction reads 1 KB of
+    // consecutive host memory (1-2 rows); the host link is measurably faster
+    // with this order than with one row per 8 threads
+    const int b = id / a.fetch_per_req;
+    const int x = id - b * a.fetch_per_req;
+    if (a.counts[4 * b + 3] == 0) return;
+    const int n = a.counts[4 * b + 1];
+    const long long u = (long long)b * a.L + a.layer;
+    const long long bk = (long long)b * K;
+    for (int j0 = x * kCopyRows; j0 < n; j0 += a.fetch_per_req * kCopyRows) {
+      // per chunk only the Top-K position and the victim slot are kept (32-bit)
+      // while the host loads are in flight; addresses are rebuilt for the stores
+      u32x4 v[kCopyItems];
+      int pos[kCopyItems], vic[kCopyItems];
 #pragma unroll
-  for (int j = 0; j < kCopyItems; ++j) {
-    const int c = j * kCopyThreads + threadIdx.x;
-    const int r = c / kRowChunks;
-    const int col = c - r * kRowChunks;
-    const int i = i0 + r;
-    dst[j] = -1;
-    if (i < K) {
-      const int s = slot_of[(long long)b * K + i];
-      if (s >= 0) {
-        v[j] = hot[(u * S + s) * kRowChunks + col];
-        dst[j] = ((long long)b * K + i) * kRowChunks + col;
+      for (int j = 0; j < kCopyItems; ++j) {
+        const int c = j * kCopyThreads + threadIdx.x;
+        const int r = c / kRowChunks;
+        const int col = c - r * kRowChunks;
+        const int jj = j0 + r;
+        pos[j] = -1;
+        if (jj < n) {
+          const int i = a.miss_pos[bk + jj];
+          const int tok = a.topk[bk + i];
+          v[j] = a.pool[(u * a.N + tok) * kRowChunks + col];
+          pos[j] = i;
+          vic[j] = a.victims[bk + jj];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kCopyItems; ++j) {
+        if (pos[j] >= 0) {
+          const int c = j * kCopyThreads + threadIdx.x;
+          const int col = c - (c / kRowChunks) * kRowChunks;
+          a.cbuf[(bk + pos[j]) * kRowChunks + col] = v[j];
+          a.hot[(u * a.S + vic[j]) * kRowChunks + col] = v[j];
+        }
       }
     }
+    return;
   }
-#pragma unroll
-  for (int j = 0; j < kCopyItems; ++j)
-    if (dst[j] >= 0) cbuf[dst[j]] = v[j];
-}
-
-// Misses: row = pool[b][l][tok_j]; cbuf[b][miss_pos_j] = row; hot[b][l][victim_j] = row.
-// The pool pointer is pinned host memory: every load crosses PCIe.  Blocks
-// (x, y) serve request b0 + y, taking 32-row groups x, x + gridDim.x, ...
-__global__ __launch_bounds__(kCopyThreads) void miss_fetch_kernel(
-    const u32x4* __restrict__ pool, u32x4* __restrict__ hot, u32x4* __restrict__ cbuf,
-    const int32_t* __restrict__ topk, const int32_t* __restrict__ miss_pos,
-    const int32_t* __restrict__ victims, const int32_t* __restrict__ counts, int L, int layer,
-    long long N, int S, int K, int b0) {
-  const int b = b0 + blockIdx.y;
-  if (counts[4 * b + 3] == 0) return;
-  const int n = counts[4 * b + 1];
-  const long long u = (long long)b * L + layer;
-  const long long bk = (long long)b * K;
-  for (int j0 = blockIdx.x * kCopyRows; j0 < n; j0 += gridDim.x * kCopyRows) {
+  // hit role: 8 threads per row, 32 rows per pass; thread (row, sub) moves the
+  // 16-byte chunks sub, sub + 8, ..., sub + 64 of its row, so each wave
+  // instruction covers eight whole 128-byte lines
+  const int rsub = threadIdx.x >> 3;
+  const int sub = threadIdx.x & 7;
+  // hit role: workgroup h copies 32-position groups h, h + hit_wgs, ... over all
+  // requests' Top-K positions (request-major)
+  const int groups_per_req = (K + kCopyRows - 1) / kCopyRows;
+  const long long n_groups = (long long)groups_per_req * a.B;
+  for (long long grp = id - a.fetch_wgs; grp < n_groups; grp += a.hit_wgs) {
+    const int b = (int)(grp / groups_per_req);
+    const int x = (int)(grp - (long long)b * groups_per_req);
+    if (a.counts[4 * b + 3] == 0) continue;
+    const int i = x * kCopyRows + rsub;
+    if (i >= K) continue;
+    const int s = a.slot_of[(long long)b * K + i];
+    if (s < 0) continue;
+    const long long u = (long long)b * a.L + a.layer;
+    const u32x4* src = a.hot + (u * a.S + s) * kRowChunks + sub;
+    u32x4* dst = a.cbuf + ((long long)b * K + i) * kRowChunks + sub;
     u32x4 v[kCopyItems];
-    long long dc[kCopyItems], dh[kCopyItems];
 #pragma unroll
-    for (int j = 0; j < kCopyItems; ++j) {
-      const int c = j * kCopyThreads + threadIdx.x;
-      const int r = c / kRowChunks;
-      const int col = c - r * kRowChunks;
-      const int jj = j0 + r;
-      dc[j] = -1;
-      if (jj < n) {
-        const int i = miss_pos[bk + jj];
-        const int tok = topk[bk + i];
-        v[j] = pool[(u * N + tok) * kRowChunks + col];
-        dc[j] = (bk + i) * kRowChunks + col;
-        dh[j] = (u * S + victims[bk + jj]) * kRowChunks + col;
-      }
-    }
+    for (int j = 0; j < kCopyItems; ++j) v[j] = src[8 * j];
 #pragma unroll
-    for (int j = 0; j < kCopyItems; ++j) {
-      if (dc[j] >= 0) {
-        cbuf[dc[j]] = v[j];
-        hot[dh[j]] = v[j];
-      }
-    }
+    for (int j = 0; j < kCopyItems; ++j) dst[8 * j] = v[j];
   }
 }
 
@@ -368,12 +396,12 @@ __global__ __launch_bounds__(kCopyThreads) void miss_fetch_kernel(
 constexpr int kAttnThreads = 512;               // 8 waves
 constexpr int kTile = 64;                       // tokens per LDS tile
 constexpr int kLdsRow = kRowBytes + 16;         // padded row: 16-B aligned, spreads banks
-constexpr int kAttnItems = kTile * kRowChunks / kAttnThreads;   // 9 chunks / thread
+constexpr int kAttnItems = kRowChunks / 8;      // 9 chunks / thread, 8 threads per row
 constexpr int kKSteps = kRowElems / 32;         // 18 MFMA k-steps over 576 dims
 constexpr int kKHalf = kKSteps / 2;             // each Q.K^T wave takes half of them
 constexpr int kPRow = kTile + 8;                // bf16 P row stride (144 B)
 constexpr int kMaxSplits = 64;
-static_assert(kAttnItems * kAttnThreads == kTile * kRowChunks, "attention tiling");
+static_assert(kTile * 8 == kAttnThreads && kAttnItems * 8 == kRowChunks, "attention tiling");
 static_assert(kKHalf * 2 == kKSteps, "k split");
 
 struct AttnArgs {
@@ -382,7 +410,7 @@ struct AttnArgs {
   const int32_t* counts;  // [B][4]
   float* part_o;          // [B][splits][16][512]
   float* part_ml;         // [B][splits][16][2]
-  int K, splits, b0;
+  int K, splits;
   float scale_log2;       // softmax scale * log2(e): scores are kept in log2 units
 };
 
@@ -404,7 +432,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t pb[kHeads * kPRow];
   __shared__ float alpha_s[kHeads];
 
-  const int b = a.b0 + blockIdx.y, sp = blockIdx.x;
+  const int b = blockIdx.y, sp = blockIdx.x;
   if (a.counts[4 * b + 3] == 0) return;   // combine writes the zero output
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -429,36 +457,27 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 pre[kAttnItems];
-  auto load_tile = [&](int tile) {
+  // two register buffers: the rows of the next two tiles are in flight while a
+  // tile is consumed from LDS
+  u32x4 ra[kAttnItems], rb[kAttnItems];
+  // 8 threads per row: thread (row tid / 8, sub tid % 8) moves chunks sub + 8j
+  const int lrow = tid >> 3, lsub = tid & 7;
+  auto load_tile = [&](u32x4 (&dst)[kAttnItems], int tile) {
+    const int tok = tile * kTile + lrow;
+    const u32x4* src = rows + (long long)tok * kRowChunks + lsub;
 #pragma unroll
-    for (int j = 0; j < kAttnItems; ++j) {
-      const int c = j * kAttnThreads + tid;
-      const int r = c / kRowChunks;
-      const int col = c - r * kRowChunks;
-      const int tok = tile * kTile + r;
-      pre[j] = tok < K ? rows[(long long)tok * kRowChunks + col] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int j = 0; j < kAttnItems; ++j)
+      dst[j] = tok < K ? src[8 * j] : u32x4{0u, 0u, 0u, 0u};
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const u32x4 (&src)[kAttnItems]) {
+    unsigned char* d = kv + lrow * kLdsRow + lsub * 16;
 #pragma unroll
-    for (int j = 0; j < kAttnItems; ++j) {
-      const int c = j * kAttnThreads + tid;
-      const int r = c / kRowChunks;
-      const int col = c - r * kRowChunks;
-      *reinterpret_cast<u32x4*>(kv + r * kLdsRow + col * 16) = pre[j];
-    }
+    for (int j = 0; j < kAttnItems; ++j) *reinterpret_cast<u32x4*>(d + j * 128) = src[j];
   };
 
-  if (tb < te) {
-    load_tile(tb);
-    store_tile();
-  }
-  __syncthreads();
-
-  for (int tile = tb; tile < te; ++tile) {
-    if (tile + 1 < te) load_tile(tile + 1);   // next tile's rows in flight during compute
-
+  // one tile from LDS: scores, online softmax, P.V; ends with a barrier after
+  // which the LDS tile may be overwritten
+  auto compute = [&](int tile) {
     // partial scores of 16 tokens over half of the 576 dims
     {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -526,9 +545,28 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
+  };
+
+  // tiles two at a time so the register buffers alternate without copies:
+  // at the top of each iteration LDS holds `tile` and rb holds tile + 1
+  if (tb < te) {
+    load_tile(ra, tb);
+    if (tb + 1 < te) load_tile(rb, tb + 1);
+    store_tile(ra);
+  }
+  __syncthreads();
+  for (int tile = tb; tile < te; tile += 2) {
+    if (tile + 2 < te) load_tile(ra, tile + 2);
+    compute(tile);
     if (tile + 1 < te) {
-      store_tile();
+      store_tile(rb);
       __syncthreads();
+      if (tile + 3 < te) load_tile(rb, tile + 3);
+      compute(tile + 1);
+      if (tile + 2 < te) {
+        store_tile(ra);
+        __syncthreads();
+      }
     }
   }
 
@@ -544,20 +582,20 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     a.part_ml[(part * kHeads + h) * 2 + 0] = m_run;
     a.part_ml[(part * kHeads + h) * 2 + 1] = l_run;
   }
+
 }
 
 // Merge of the split partials of (request b, head h):
-// out = sum_s 2^(m_s - M) O_s / L, L = sum_s 2^(m_s - M) l_s, lse = (M + log2 L) * ln 2.
-// One workgroup of 128 threads per (b, h), 4 outputs per thread.
+// out = sum_s 2^(m_s - M) O_s / L, L = sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2.
+// One workgroup of 128 threads per (h, b), 4 outputs per thread.
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const int32_t* __restrict__ counts,
                                                       uint16_t* __restrict__ out,
-                                                      float* __restrict__ lse, int splits,
-                                                      int b0) {
+                                                      float* __restrict__ lse, int splits) {
   __shared__ float w[kMaxSplits];
   __shared__ float inv_l;
-  const int b = b0 + blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   uint2* ob = reinterpret_cast<uint2*>(out + ((long long)b * kHeads + h) * kVDim);
   if (counts[4 * b + 3] == 0) {   // invalid Top-K: zero output, lse = -inf
     ob[tid] = make_uint2(0u, 0u);
@@ -674,32 +712,38 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const
   return hipGetLastError();
 }
 
-hipError_t launch_hit_gather(const Layout& lay, const DevPtrs& d, int layer, int b0, int nb,
-                             hipStream_t s) {
-  dim3 grid((lay.K + kCopyRows - 1) / kCopyRows, nb);
-  hipLaunchKernelGGL(hit_gather_kernel, grid, dim3(kCopyThreads), 0, s,
-                     reinterpret_cast<const u32x4*>(d.hot), reinterpret_cast<u32x4*>(d.cbuf),
-                     d.slot_of, d.counts, lay.L, layer, lay.S, lay.K, b0);
-  return hipGetLastError();
-}
-
-hipError_t launch_miss_fetch(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
-                             int b0, int nb, hipStream_t s) {
-  // fetch_blocks workgroups per group, spread evenly over its requests
-  int per_req = (lay.fetch_blocks + nb - 1) / nb;
-  const int max_per_req = (lay.K + kCopyRows - 1) / kCopyRows;
-  if (per_req > max_per_req) per_req = max_per_req;
-  if (per_req < 1) per_req = 1;
-  dim3 grid(per_req, nb);
-  hipLaunchKernelGGL(miss_fetch_kernel, grid, dim3(kCopyThreads), 0, s,
-                     reinterpret_cast<const u32x4*>(d.pool), reinterpret_cast<u32x4*>(d.hot),
-                     reinterpret_cast<u32x4*>(d.cbuf), topk, d.miss_pos, d.victims, d.counts,
-                     lay.L, layer, (long long)lay.N, lay.S, lay.K, b0);
+hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
+                         hipStream_t s) {
+  GatherArgs a;
+  a.pool = reinterpret_cast<const u32x4*>(d.pool);
+  a.hot = reinterpret_cast<u32x4*>(d.hot);
+  a.cbuf = reinterpret_cast<u32x4*>(d.cbuf);
+  a.topk = topk;
+  a.slot_of = d.slot_of;
+  a.miss_pos = d.miss_pos;
+  a.victims = d.victims;
+  a.counts = d.counts;
+  a.N = lay.N;
+  a.S = lay.S;
+  a.K = lay.K;
+  a.L = lay.L;
+  a.layer = layer;
+  a.B = lay.B;
+  const int groups_per_req = (lay.K + kCopyRows - 1) / kCopyRows;
+  int per_req = (lay.fetch_blocks + lay.B - 1) / lay.B;   // fetch workgroups spread over requests
+  if (per_req > groups_per_req) per_req = groups_per_req;
+  a.fetch_per_req = per_req;
+  a.fetch_wgs = per_req * lay.B;
+  const long long all_groups = (long long)groups_per_req * lay.B;
+  a.hit_wgs = (int)(lay.hit_blocks > 0 && lay.hit_blocks < all_groups ? lay.hit_blocks : all_groups);
+  a.hits_first = (lay.flags & KVS_FLAG_HITS_FIRST) != 0;
+  const long long grid = (long long)a.fetch_wgs + (long long)a.hit_wgs;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t* q, float scale,
-                            int b0, int nb, hipStream_t s) {
+                            hipStream_t s) {
   AttnArgs a;
   a.cbuf = d.cbuf;
   a.q = q;
@@ -708,16 +752,15 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t*
   a.part_ml = d.part_ml;
   a.K = lay.K;
   a.splits = lay.splits;
-  a.b0 = b0;
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attention_kernel, dim3(lay.splits, nb), dim3(kAttnThreads), 0, s, a);
+  hipLaunchKernelGGL(attention_kernel, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse, int b0,
-                          int nb, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(kHeads, nb), dim3(128), 0, s, d.part_o, d.part_ml,
-                     d.counts, out, lse, lay.splits, b0);
+hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(kHeads, lay.B), dim3(128), 0, s, d.part_o, d.part_ml,
+                     d.counts, out, lse, lay.splits);
   return hipGetLastError();
 }
 
