@@ -29,11 +29,6 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
 
-__device__ __forceinline__ unsigned long long lanemask_lt() {
-  const int lane = threadIdx.x & 63;
-  return lane ? (~0ull >> (64 - lane)) : 0ull;
-}
-
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;   // NaN stays NaN
@@ -79,7 +74,8 @@ __global__ void clear_status_kernel(int32_t* status) {
 // ------------------------------------------------------------------ diff + LRU
 constexpr int kDiffThreads = 1024;
 constexpr int kDiffWaves = kDiffThreads / 64;
-constexpr int kDiffItems = KVS_MAX_TOPK / kDiffThreads;   // Top-K entries per thread
+constexpr int kDiffItems = KVS_MAX_TOPK / kDiffThreads;   // Top-K entries per thread, at most
+constexpr int kDiffSlots = KVS_MAX_SLOTS / kDiffThreads;  // slots per thread, at most
 
 struct DiffArgs {
   const int32_t* topk;     // [B][K]
@@ -99,27 +95,34 @@ struct DiffArgs {
   int S, K, L, layer, hash_bits;
 };
 
-// Rank of this thread among the threads of the workgroup whose `pred` holds,
-// counted in thread order; `total` receives the number of such threads.
-// Must be reached by every thread of the workgroup.
-__device__ __forceinline__ int wg_rank(bool pred, int* wtot, int& total) {
+// Exclusive prefix sum of `v` over the workgroup in thread order; `total`
+// receives the workgroup sum.  Must be reached by every thread.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* wtot, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(pred);
-  const int in_wave = __popcll(m & lanemask_lt());
-  if (lane == 0) wtot[wave] = __popcll(m);
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wtot[wave] = x;
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kDiffWaves; ++w) {
-    const int v = wtot[w];
-    off += (w < wave) ? v : 0;
-    tot += v;
+    const int y = wtot[w];
+    off += (w < wave) ? y : 0;
+    tot += y;
   }
   __syncthreads();
   total = tot;
-  return off + in_wave;
+  return off + x - v;
 }
 
+// Thread t owns the contiguous Top-K entries [t*kpt, t*kpt + kpt) and the
+// contiguous order positions / slots [t*spt, t*spt + spt), so every
+// order-preserving compaction is one local count, one workgroup scan and one
+// local write-out.
 __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int wtot[kDiffWaves];
@@ -131,6 +134,10 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   const int b = blockIdx.x;
   const long long u = (long long)b * a.L + a.layer;
   const int H = 1 << a.hash_bits;
+  const int kpt = (K + kDiffThreads - 1) / kDiffThreads;   // <= kDiffItems
+  const int spt = (S + kDiffThreads - 1) / kDiffThreads;   // <= kDiffSlots
+  const int i0 = tid * kpt;
+  const int p0 = tid * spt;
 
   // LDS: LRU order copy [S] u16 | per-slot flag [S] u8 (1 = hit, 2 = victim) |
   //      token hash set [H] i32, reused after validation as miss list [K] + victims [K]
@@ -148,9 +155,13 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   const long long bk = (long long)b * K;
   const int t = a.stepctr[u];
 
-  for (int s = tid; s < S; s += kDiffThreads) {
-    ord[s] = gorder[s];
-    flag[s] = 0;
+#pragma unroll
+  for (int q = 0; q < kDiffSlots; ++q) {
+    const int p = p0 + q;
+    if (q < spt && p < S) {
+      ord[p] = gorder[p];
+      flag[p] = 0;
+    }
   }
   for (int h = tid; h < H; h += kDiffThreads) hash[h] = -1;
   if (tid == 0) {
@@ -160,13 +171,12 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   __syncthreads();
 
   // 1. lookup + validation (range, duplicates via an LDS open-addressing set)
-  const int items = (K + kDiffThreads - 1) / kDiffThreads;
   int my_slot[kDiffItems];
 #pragma unroll
   for (int j = 0; j < kDiffItems; ++j) {
     my_slot[j] = -1;
-    const int i = tid + j * kDiffThreads;
-    if (j < items && i < K) {
+    const int i = i0 + j;
+    if (j < kpt && i < K) {
       const int tok = topk[i];
       if (tok < 0 || (long long)tok >= a.N) {
         atomicOr(&err_bits, 1);
@@ -202,58 +212,67 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   }
 
   // 2. sparse diff: record slot_of, touch hits, compact misses in Top-K order
-  int running = 0;
+  int cnt = 0;
 #pragma unroll
   for (int j = 0; j < kDiffItems; ++j) {
-    if (j < items) {
-      const int i = tid + j * kDiffThreads;
-      const bool in = i < K;
-      const bool miss = in && my_slot[j] < 0;
-      if (in) {
-        a.slot_of[bk + i] = my_slot[j];
-        if (!miss) lu[my_slot[j]] = t;
-      }
-      int total;
-      const int r = wg_rank(miss, wtot, total);
-      if (miss) lmiss[running + r] = i;
-      running += total;
+    const int i = i0 + j;
+    if (j < kpt && i < K) {
+      a.slot_of[bk + i] = my_slot[j];
+      if (my_slot[j] >= 0) lu[my_slot[j]] = t;
+      else ++cnt;
     }
   }
-  const int m = running;
+  int m;
+  int r = wg_exclusive_scan(cnt, wtot, m);
+#pragma unroll
+  for (int j = 0; j < kDiffItems; ++j) {
+    const int i = i0 + j;
+    if (j < kpt && i < K && my_slot[j] < 0) lmiss[r++] = i;
+  }
   const int n_hit = K - m;
 
   // 3. victims: the first m non-hit slots of the LRU order; the other non-hit
   //    slots keep their relative order at the front of the new order
-  running = 0;
-  for (int c = 0; c < S; c += kDiffThreads) {
-    const int p = c + tid;
-    const bool in = p < S;
-    const int s = in ? ord[p] : 0;
-    const bool nonhit = in && flag[s] == 0;
-    int total;
-    const int r = running + wg_rank(nonhit, wtot, total);
-    if (nonhit) {
-      if (r < m) {
-        lvict[r] = s;
-        flag[s] = 2;
-      } else {
-        gorder[r - m] = (uint16_t)s;
+  cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kDiffSlots; ++q) {
+    const int p = p0 + q;
+    if (q < spt && p < S && flag[ord[p]] == 0) ++cnt;
+  }
+  int n_nonhit;
+  r = wg_exclusive_scan(cnt, wtot, n_nonhit);
+#pragma unroll
+  for (int q = 0; q < kDiffSlots; ++q) {
+    const int p = p0 + q;
+    if (q < spt && p < S) {
+      const int s = ord[p];
+      if (flag[s] == 0) {
+        if (r < m) {
+          lvict[r] = s;
+          flag[s] = 2;
+        } else {
+          gorder[r - m] = (uint16_t)s;
+        }
+        ++r;
       }
     }
-    running += total;
   }
   __syncthreads();
 
   // 4. the K touched slots (hits and victims, all stamped t) close the order,
   //    ascending by slot
-  running = 0;
-  for (int c = 0; c < S; c += kDiffThreads) {
-    const int s = c + tid;
-    const bool touched = s < S && flag[s] != 0;
-    int total;
-    const int r = running + wg_rank(touched, wtot, total);
-    if (touched) gorder[S - K + r] = (uint16_t)s;
-    running += total;
+  cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kDiffSlots; ++q) {
+    const int s = p0 + q;
+    if (q < spt && s < S && flag[s] != 0) ++cnt;
+  }
+  int n_touched;
+  r = S - K + wg_exclusive_scan(cnt, wtot, n_touched);
+#pragma unroll
+  for (int q = 0; q < kDiffSlots; ++q) {
+    const int s = p0 + q;
+    if (q < spt && s < S && flag[s] != 0) gorder[r++] = (uint16_t)s;
   }
 
   // 5. map update: the j-th miss takes the j-th victim
