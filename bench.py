@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--fetch-blocks", type=int, default=0, help="0 = library's choice")
     p.add_argument("--attn-splits", type=int, default=0, help="0 = library's choice")
     p.add_argument("--hit-blocks", type=int, default=0, help="0 = library's choice")
+    p.add_argument("--graph", action="store_true",
+                   help="launch every (step, layer) as a captured HIP graph (inputs in place)")
     p.add_argument("--hits-first", action="store_true",
                    help="hit-copy workgroups take the first grid indices of the gather")
     p.add_argument("--copy-calibration", action="store_true",
@@ -177,9 +179,19 @@ def main():
     print(f"# inputs ready, pool {pool.host.nbytes / 1e9:.2f} GB pinned", file=sys.stderr,
           flush=True)
 
+    graphs = None
+    if args.graph:
+        # one graph per (step, layer) over that step's own buffers: the inputs are
+        # where a selector would have written them, so a replay is the whole step
+        graphs = [[pool.capture(l, topk[t, l], q[t, l], out[t, l], lse[t, l]) for l in range(L)]
+                  for t in range(total)]
+
     def run_step(t):
         for l in range(L):
-            pool.step(l, topk[t, l], q[t, l], out[t, l], lse[t, l])
+            if graphs is not None:
+                graphs[t][l].launch()
+            else:
+                pool.step(l, topk[t, l], q[t, l], out[t, l], lse[t, l])
 
     # warm-up; the last warm-up step is timed per kernel to find the dominant kernel
     cold = None
@@ -347,7 +359,7 @@ def main():
                    "topk": K, "fresh_rate": wl.fresh_rate, "fresh_dist": wl.dist,
                    "heads": 16, "head_dim": 576, "v_dim": 512, "attn_splits": splits,
                    "fetch_blocks": pool.sizes.fetch_blocks, "hit_blocks": args.hit_blocks,
-                   "hits_first": bool(args.hits_first)},
+                   "hits_first": bool(args.hits_first), "hip_graph": bool(args.graph)},
         "decode_steps_per_s": round(1e3 / ms_step, 2),
         "cold_step_ms": None if cold is None else round(cold, 4),
         "miss_rate": round(miss_rate, 5),
@@ -362,6 +374,10 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
     }
+    if graphs is not None:
+        for row in graphs:
+            for g in row:
+                g.destroy()
     pool.release()
     pool.host.free()
     print(json.dumps(line), flush=True)

@@ -229,6 +229,24 @@ int kvs_profile_begin(kvs_pool* pool, int32_t max_steps, uint32_t kernel_mask);
 /* Synchronise and report the recorded times; stops recording. */
 int kvs_profile_end(kvs_pool* pool, kvs_kernel_times* out);
 
+/* A captured kvs_step (HIP graph), for callers that replay the decode step
+ * with fixed buffers: the selector writes each step's Top-K into the same
+ * `topk` buffer and the queries into the same `q` buffer, and the graph is
+ * relaunched.  The graph holds no host synchronisation, no memset and no
+ * host-side state: the step counters live in device memory, so every launch
+ * is one more decode step of `layer` ("XM-Sparse", HiSparse integration: the
+ * same path supports CUDA Graph on the pages' hardware). */
+typedef struct kvs_graph kvs_graph;
+
+/* Capture one kvs_step(pool, layer, topk, q, out, lse) into an executable
+ * graph.  Nothing runs at capture time.  The buffers must stay valid while the
+ * graph exists.  Errors as kvs_step, plus KVS_EHIP_* for graph API failures. */
+int kvs_graph_capture(kvs_pool* pool, int32_t layer, const int32_t* topk, const void* q,
+                      void* out, float* lse, kvs_graph** out_graph);
+/* Enqueue one replay on `stream`. */
+int kvs_graph_launch(kvs_graph* graph, void* stream);
+int kvs_graph_destroy(kvs_graph* graph);
+
 /* Destroy the pool's timing events and host-side state.  Caller buffers are untouched. */
 int kvs_release(kvs_pool* pool);
 

@@ -135,3 +135,11 @@ def test_fetch_blocks_resolve():
     s = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096, topk=2048,
                                         fetch_blocks=128))
     assert s.fetch_blocks == 128
+
+
+def test_graph_calls_reject_null():
+    lib = kvs.lib()
+    g = ctypes.c_void_p()
+    assert lib.kvs_graph_capture(None, 0, None, None, None, None, ctypes.byref(g)) == kvs.KVS_EINVAL
+    assert lib.kvs_graph_launch(None, None) == kvs.KVS_EINVAL
+    assert lib.kvs_graph_destroy(None) == kvs.KVS_EINVAL

@@ -34,6 +34,7 @@ EXPORTS = (
     "kvs_query_sizes", "kvs_host_alloc", "kvs_host_free", "kvs_create_pool", "kvs_publish",
     "kvs_step", "kvs_free_request", "kvs_sync_status", "kvs_debug_read_state",
     "kvs_profile_begin", "kvs_profile_end", "kvs_release", "kvs_strerror",
+    "kvs_graph_capture", "kvs_graph_launch", "kvs_graph_destroy",
 )
 
 
@@ -122,6 +123,9 @@ def lib() -> ctypes.CDLL:
         "kvs_profile_begin": [vp, i32, ctypes.c_uint32],
         "kvs_profile_end": [vp, ctypes.POINTER(kvs_kernel_times)],
         "kvs_release": [vp],
+        "kvs_graph_capture": [vp, i32, vp, vp, vp, vp, ctypes.POINTER(vp)],
+        "kvs_graph_launch": [vp, vp],
+        "kvs_graph_destroy": [vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -279,6 +283,19 @@ class Pool:
                 "launches": {n: t.launches[i] for i, n in enumerate(KERNEL_NAMES)},
                 **{n: t.ms_total[i] for i, n in enumerate(KERNEL_NAMES)}}
 
+    def capture(self, layer, topk, q, out, lse=None) -> "StepGraph":
+        """Capture one step of `layer` over these fixed buffers into a HIP graph."""
+        self._check_dev(topk, (self.B, self.K), 4)
+        self._check_dev(q, (self.B, HEADS, HEAD_DIM), 2)
+        self._check_dev(out, (self.B, HEADS, V_DIM), 2)
+        if lse is not None:
+            self._check_dev(lse, (self.B, HEADS), 4)
+        g = ctypes.c_void_p()
+        _check(lib().kvs_graph_capture(self.handle, layer, topk.data_ptr(), q.data_ptr(),
+                                       out.data_ptr(), None if lse is None else lse.data_ptr(),
+                                       ctypes.byref(g)), "kvs_graph_capture")
+        return StepGraph(g, (topk, q, out, lse))
+
     def release(self):
         if self.handle:
             _check(lib().kvs_release(self.handle), "kvs_release")
@@ -290,3 +307,19 @@ class Pool:
                 or not t.is_contiguous():
             raise ValueError(f"expected a contiguous device tensor {shape} of {itemsize}-byte "
                              f"elements, got {tuple(t.shape)} {t.dtype} on {t.device}")
+
+
+class StepGraph:
+    """A captured kvs_step; launch() replays it on a stream."""
+
+    def __init__(self, handle, keep_alive):
+        self.handle = handle
+        self._keep = keep_alive
+
+    def launch(self, stream=None):
+        _check(lib().kvs_graph_launch(self.handle, _stream_ptr(stream)), "kvs_graph_launch")
+
+    def destroy(self):
+        if self.handle:
+            _check(lib().kvs_graph_destroy(self.handle), "kvs_graph_destroy")
+            self.handle = None

@@ -18,6 +18,9 @@ namespace kvs {
 
 static uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
+// Attention workgroups resident at once: one per compute unit of an MI355X.
+constexpr int kAttnWorkgroupsPerRound = 256;
+
 int make_layout(const kvs_config* c, Layout* lay) {
   if (c == nullptr || lay == nullptr) return KVS_EINVAL;
   if (c->batch < 1 || c->batch > 65535 || c->layers < 1) return KVS_EINVAL;
@@ -38,12 +41,21 @@ int make_layout(const kvs_config* c, Layout* lay) {
   const int ntiles = (int)((K + 63) / 64);
   int splits = c->attn_splits;
   if (splits == 0) {
-    // one attention workgroup per compute unit (256 CUs), at least one
-    // 64-token tile each
-    splits = (int)((256 + B - 1) / B);
-    if (splits > ntiles) splits = ntiles;
-    if (splits > 64) splits = 64;
-    if (splits < 1) splits = 1;
+    // An attention workgroup holds one CU (its LDS tile), so a launch runs in
+    // rounds of 256 workgroups.  Pick the split count with the fewest
+    // tile-times: rounds x tiles per split; ties go to fewer splits (less to
+    // merge).
+    long long best = -1;
+    const int max_s = ntiles < 64 ? ntiles : 64;
+    for (int sp = 1; sp <= max_s; ++sp) {
+      const long long rounds = ((long long)B * sp + kAttnWorkgroupsPerRound - 1) /
+                               kAttnWorkgroupsPerRound;
+      const long long cost = rounds * ((ntiles + sp - 1) / sp);
+      if (best < 0 || cost < best) {
+        best = cost;
+        splits = sp;
+      }
+    }
   } else if (splits > ntiles) {
     return KVS_EINVAL;
   }
@@ -385,6 +397,62 @@ int kvs_profile_end(kvs_pool* p, kvs_kernel_times* out) {
   p->prof_used = 0;
   p->prof_steps = 0;
   return KVS_OK;
+}
+
+struct kvs_graph {
+  hipGraphExec_t exec;
+};
+
+int kvs_graph_capture(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, void* out,
+                      float* lse, kvs_graph** out_graph) {
+  if (out_graph == nullptr) return KVS_EINVAL;
+  *out_graph = nullptr;
+  if (p == nullptr || topk == nullptr || q == nullptr || out == nullptr) return KVS_EINVAL;
+  if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
+  hipStream_t cs = nullptr;
+  KVS_TRY_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  // no timing events inside the graph
+  const int saved_max = p->prof_max_steps;
+  p->prof_max_steps = 0;
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  int rc = KVS_OK;
+  hipGraph_t g = nullptr;
+  if (e == hipSuccess) {
+    rc = kvs_step(p, layer, topk, q, out, lse, cs);
+    const hipError_t e2 = hipStreamEndCapture(cs, &g);   // always end the capture
+    if (rc == KVS_OK && e2 != hipSuccess) rc = hip_err(e2);
+  } else {
+    rc = hip_err(e);
+  }
+  p->prof_max_steps = saved_max;
+  hipGraphExec_t exec = nullptr;
+  if (rc == KVS_OK) {
+    e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) rc = hip_err(e);
+  }
+  if (g != nullptr) (void)hipGraphDestroy(g);
+  (void)hipStreamDestroy(cs);
+  if (rc != KVS_OK) return rc;
+  kvs_graph* kg = new (std::nothrow) kvs_graph();
+  if (kg == nullptr) {
+    (void)hipGraphExecDestroy(exec);
+    return KVS_ENOMEM;
+  }
+  kg->exec = exec;
+  *out_graph = kg;
+  return KVS_OK;
+}
+
+int kvs_graph_launch(kvs_graph* g, void* stream) {
+  if (g == nullptr) return KVS_EINVAL;
+  return hip_err(hipGraphLaunch(g->exec, (hipStream_t)stream));
+}
+
+int kvs_graph_destroy(kvs_graph* g) {
+  if (g == nullptr) return KVS_EINVAL;
+  const hipError_t e = hipGraphExecDestroy(g->exec);
+  delete g;
+  return hip_err(e);
 }
 
 int kvs_release(kvs_pool* p) {

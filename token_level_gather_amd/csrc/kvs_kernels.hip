@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
 // ------------------------------------------------------------------ attention
 constexpr int kAttnThreads = 512;               // 8 waves
 constexpr int kTile = 64;                       // tokens per LDS tile
-constexpr int kLdsRow = kRowBytes + 16;         // padded row: 16-B aligned, spreads banks
+constexpr int kLdsRow = kRowBytes;              // LDS row stride; chunks are XOR-swizzled
 constexpr int kAttnItems = kRowChunks / 8;      // 9 chunks / thread, 8 threads per row
 constexpr int kKSteps = kRowElems / 32;         // 18 MFMA k-steps over 576 dims
 constexpr int kKHalf = kKSteps / 2;             // each Q.K^T wave takes half of them
@@ -422,6 +422,17 @@ constexpr int kPRow = kTile + 8;                // bf16 P row stride (144 B)
 constexpr int kMaxSplits = 64;
 static_assert(kTile * 8 == kAttnThreads && kAttnItems * 8 == kRowChunks, "attention tiling");
 static_assert(kKHalf * 2 == kKSteps, "k split");
+
+// LDS placement of the 16-byte chunk c of tile row r: chunk c ^ sw(r) of the
+// row (the XOR stays inside c's aligned group of 8 chunks).  With 1152-byte rows
+// (288 dwords, so odd rows start half-way round the 64 banks) this spreads
+//  - a wave's row stores (8 rows x 128 B) and the Q.K^T operand reads (16 rows
+//    x 4 chunks) evenly over the banks, and
+//  - the P.V operand reads (2-byte values of 4 rows 8 apart, 16 columns each)
+//    over distinct banks.
+__device__ __forceinline__ int lds_swz(int r) {
+  return (((r >> 3) & 3) << 1) ^ (((r >> 1) & 1) << 2);
+}
 
 struct AttnArgs {
   const uint16_t* cbuf;   // [B][K][576]
@@ -488,8 +499,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     for (int j = 0; j < kAttnItems; ++j)
       dst[j] = tok < K ? src[8 * j] : u32x4{0u, 0u, 0u, 0u};
   };
+  const int lsw = lds_swz(lrow);
   auto store_tile = [&](const u32x4 (&src)[kAttnItems]) {
-    unsigned char* d = kv + lrow * kLdsRow + lsub * 16;
+    unsigned char* d = kv + lrow * kLdsRow + ((lsub ^ lsw) * 16);
 #pragma unroll
     for (int j = 0; j < kAttnItems; ++j) *reinterpret_cast<u32x4*>(d + j * 128) = src[j];
   };
@@ -500,10 +512,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     // partial scores of 16 tokens over half of the 576 dims
     {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      const unsigned char* krow = kv + (tt * 16 + r16) * kLdsRow + kh * kKHalf * 64 + g * 16;
+      const int krow_i = tt * 16 + r16;
+      const unsigned char* krow = kv + krow_i * kLdsRow;
+      const int ksw = lds_swz(krow_i);
 #pragma unroll
       for (int ks = 0; ks < kKHalf; ++ks) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + ks * 64));
+        const int chunk = (kh * kKHalf + ks) * 4 + g;   // dims chunk*8 .. +7
+        const bf16x8 kf =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(krow + (chunk ^ ksw) * 16));
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kf, s, 0, 0, 0);
       }
       float* sck = sc + kh * kHeads * kTile;
@@ -550,14 +566,17 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
       for (int kk = 0; kk < kTile / 32; ++kk) {
         const bf16x8 pf =
             as_bf16x8(*reinterpret_cast<const u32x4*>(pb + r16 * kPRow + kk * 32 + g * 8));
-        const unsigned char* vbase = kv + (kk * 32 + g * 8) * kLdsRow;
+        const int vrow0 = kk * 32 + g * 8;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const int e = wave * 64 + nt * 16 + r16;
           u16x8 vv;
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            vv[jj] = *reinterpret_cast<const uint16_t*>(vbase + jj * kLdsRow + e * 2);
+          for (int jj = 0; jj < 8; ++jj) {
+            const int vr = vrow0 + jj;
+            vv[jj] = *reinterpret_cast<const uint16_t*>(
+                kv + vr * kLdsRow + (((e >> 3) ^ lds_swz(vr)) * 16) + (e & 7) * 2);
+          }
           acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               pf, __builtin_bit_cast(bf16x8, vv), acc[nt], 0, 0, 0);
         }
