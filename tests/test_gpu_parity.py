@@ -246,3 +246,50 @@ def test_full_size_16k_sampled(name, reqs):
 def test_full_size_long_context_sampled(name, reqs, steps):
     wl = W.WORKLOADS[name]
     _case(wl, steps, reqs, fill="checked")
+
+
+def test_publish_rows_then_fetch():
+    """Lifecycle "publish": rows written with kvs_publish are what later misses fetch."""
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(batch=2, layers=2, context=3000, slots=400,
+                                                  topk=200, steps=6, fresh_rate=0.5)
+    h = Harness(wl, wl.steps, range(2))
+    try:
+        for t in range(2):
+            for l in range(wl.layers):
+                h.check(t, l, *h.device_step(t, l))
+        rng = np.random.default_rng(7)
+        published = {}
+        for b in range(2):
+            for l in range(wl.layers):
+                resident = set(h.oracle[(b, l)].resident())
+                free = [x for x in range(wl.context) if x not in resident]
+                start = int(rng.choice(free[: len(free) - 40]))
+                n = 1
+                while n < 32 and start + n not in resident and start + n < wl.context:
+                    n += 1
+                rows = W.f32_to_bf16_bits(rng.standard_normal((n, 576)).astype(np.float32))
+                h.pool.publish(b, l, start, rows)
+                assert np.array_equal(h.pool.host.array[b, l, start:start + n], rows)
+                # make the next step select the first published token (a miss)
+                if start not in h.topk[2, l, b]:
+                    h.topk[2, l, b, 0] = start
+                published[(b, l)] = (start, rows[0])
+        # the next step fetches the published bytes
+        for l in range(wl.layers):
+            h.check(2, l, *h.device_step(2, l))
+            row = wl.topk * 1152
+            for b in range(2):
+                start, first = published[(b, l)]
+                pos = int(np.flatnonzero(h.topk[2, l, b] == start)[0])
+                got = h.pool.cbuf[b * row:(b + 1) * row].view(torch.int16).cpu().numpy()
+                assert np.array_equal(got.view(np.uint16).reshape(wl.topk, 576)[pos], first)
+        for t in range(3, wl.steps):
+            for l in range(wl.layers):
+                h.check(t, l, *h.device_step(t, l))
+        for bad in ((2, 0, 0, 1), (0, 2, 0, 1), (0, 0, -1, 1), (0, 0, wl.context - 1, 2)):
+            with pytest.raises(kvs.KvsError):
+                h.pool.publish(bad[0], bad[1], bad[2], np.zeros((bad[3], 576), np.uint16))
+    finally:
+        h.close()

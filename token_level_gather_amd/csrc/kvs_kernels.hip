@@ -2,9 +2,9 @@
 //
 // One kvs_step of layer l runs four launches for the B units (b, l):
 //   diff_lru   one workgroup per unit: slot lookup + validation, sparse diff
-//              (misses compacted in Top-K order with wave ballots and a
-//              workgroup prefix sum), hit touch, LRU victim choice from an
-//              LDS copy of the unit's LRU order array, map update.
+//              (misses compacted in Top-K order by a workgroup prefix sum),
+//              hit touch, LRU victim choice from the unit's LRU order array,
+//              eviction and map update.
 //   gather     the index copy: miss rows read from pinned host memory over
 //              PCIe into the compute buffer and the victim slots, hit rows
 //              copied from the hot buffer to the compute buffer, in one grid.
@@ -122,7 +122,10 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wtot, int& total) {
 // Thread t owns the contiguous Top-K entries [t*kpt, t*kpt + kpt) and the
 // contiguous order positions / slots [t*spt, t*spt + spt), so every
 // order-preserving compaction is one local count, one workgroup scan and one
-// local write-out.
+// local write-out.  Global loads are issued as early as their inputs allow:
+// the Top-K entries, the LRU order and the step counter at entry, then the
+// token-to-slot lookups and, for every order position, the token its slot
+// holds (so the thread that picks a victim already knows what it evicts).
 __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int wtot[kDiffWaves];
@@ -139,11 +142,10 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   const int i0 = tid * kpt;
   const int p0 = tid * spt;
 
-  // LDS: LRU order copy [S] u16 | per-slot flag [S] u8 (1 = hit, 2 = victim) |
-  //      token hash set [H] i32, reused after validation as miss list [K] + victims [K]
-  uint16_t* ord = reinterpret_cast<uint16_t*>(smem);
-  uint8_t* flag = smem + ((S * 2 + 15) & ~15);
-  int32_t* hash = reinterpret_cast<int32_t*>(smem + ((S * 2 + 15) & ~15) + ((S + 15) & ~15));
+  // LDS: per-slot flag [S] u8 (1 = hit, 2 = victim) | token hash set [H] i32,
+  //      reused after validation as miss list [K] + victims [K]
+  uint8_t* flag = smem;
+  int32_t* hash = reinterpret_cast<int32_t*>(smem + ((S + 15) & ~15));
   int32_t* lmiss = hash;
   int32_t* lvict = hash + K;
 
@@ -153,15 +155,36 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   uint16_t* gorder = a.order + u * S;
   const int32_t* topk = a.topk + (long long)b * K;
   const long long bk = (long long)b * K;
-  const int t = a.stepctr[u];
 
+  // 0. independent loads first: Top-K entries, LRU order, step counter
+  int my_tok[kDiffItems];
+#pragma unroll
+  for (int j = 0; j < kDiffItems; ++j) {
+    const int i = i0 + j;
+    my_tok[j] = (j < kpt && i < K) ? topk[i] : 0;
+  }
+  int my_ord[kDiffSlots];
 #pragma unroll
   for (int q = 0; q < kDiffSlots; ++q) {
     const int p = p0 + q;
-    if (q < spt && p < S) {
-      ord[p] = gorder[p];
-      flag[p] = 0;
-    }
+    my_ord[q] = (q < spt && p < S) ? (int)gorder[p] : 0;
+  }
+  const int t = a.stepctr[u];
+  // the token held by the slot at each of this thread's order positions
+  int my_old[kDiffSlots];
+#pragma unroll
+  for (int q = 0; q < kDiffSlots; ++q) {
+    const int p = p0 + q;
+    my_old[q] = (q < spt && p < S) ? slot2tok[my_ord[q]] : -1;
+    if (q < spt && p < S) flag[p] = 0;
+  }
+  // 1a. slot lookup of every in-range entry, issued before the first barrier
+  int my_slot[kDiffItems];
+#pragma unroll
+  for (int j = 0; j < kDiffItems; ++j) {
+    const int i = i0 + j;
+    const int tok = my_tok[j];
+    my_slot[j] = (j < kpt && i < K && tok >= 0 && (long long)tok < a.N) ? tok2slot[tok] : -1;
   }
   for (int h = tid; h < H; h += kDiffThreads) hash[h] = -1;
   if (tid == 0) {
@@ -170,14 +193,12 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   }
   __syncthreads();
 
-  // 1. lookup + validation (range, duplicates via an LDS open-addressing set)
-  int my_slot[kDiffItems];
+  // 1b. validation (range, duplicates via an LDS open-addressing set); hit flags
 #pragma unroll
   for (int j = 0; j < kDiffItems; ++j) {
-    my_slot[j] = -1;
     const int i = i0 + j;
     if (j < kpt && i < K) {
-      const int tok = topk[i];
+      const int tok = my_tok[j];
       if (tok < 0 || (long long)tok >= a.N) {
         atomicOr(&err_bits, 1);
       } else {
@@ -191,11 +212,8 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
           }
           h = (h + 1) & (unsigned)(H - 1);
         }
-        const int s = tok2slot[tok];
-        if (s >= 0 && s < S) {
-          my_slot[j] = s;
-          flag[s] = 1;
-        }
+        if (my_slot[j] >= S) my_slot[j] = -1;
+        if (my_slot[j] >= 0) flag[my_slot[j]] = 1;
       }
     }
   }
@@ -231,25 +249,32 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   }
   const int n_hit = K - m;
 
-  // 3. victims: the first m non-hit slots of the LRU order; the other non-hit
-  //    slots keep their relative order at the front of the new order
+  // 3. victims: the first m non-hit slots of the LRU order, evicted here; the
+  //    other non-hit slots keep their relative order at the front of the new order
   cnt = 0;
 #pragma unroll
   for (int q = 0; q < kDiffSlots; ++q) {
     const int p = p0 + q;
-    if (q < spt && p < S && flag[ord[p]] == 0) ++cnt;
+    if (q < spt && p < S && flag[my_ord[q]] == 0) ++cnt;
   }
   int n_nonhit;
   r = wg_exclusive_scan(cnt, wtot, n_nonhit);
+  int my_evict = 0;
 #pragma unroll
   for (int q = 0; q < kDiffSlots; ++q) {
     const int p = p0 + q;
     if (q < spt && p < S) {
-      const int s = ord[p];
+      const int s = my_ord[q];
       if (flag[s] == 0) {
         if (r < m) {
           lvict[r] = s;
           flag[s] = 2;
+          const int old = my_old[q];
+          a.evicted[bk + r] = old;
+          if (old >= 0) {
+            tok2slot[old] = -1;   // evicted tokens are outside the Top-K set
+            ++my_evict;
+          }
         } else {
           gorder[r - m] = (uint16_t)s;
         }
@@ -257,6 +282,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
       }
     }
   }
+  if (my_evict) atomicAdd(&n_evict, my_evict);
   __syncthreads();
 
   // 4. the K touched slots (hits and victims, all stamped t) close the order,
@@ -274,35 +300,29 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     const int s = p0 + q;
     if (q < spt && s < S && flag[s] != 0) gorder[r++] = (uint16_t)s;
   }
+  if (tid == 0) {   // n_evict is final after the barriers inside the scan
+    a.counts[4 * b + 0] = n_hit;
+    a.counts[4 * b + 1] = m;
+    a.counts[4 * b + 2] = n_evict;
+    a.counts[4 * b + 3] = 1;
+    unsigned long long* st = reinterpret_cast<unsigned long long*>(a.stats + 4 * u);
+    atomicAdd(st + 0, 1ull);   // no return value is used: the adds do not stall
+    atomicAdd(st + 1, (unsigned long long)n_hit);
+    atomicAdd(st + 2, (unsigned long long)m);
+    atomicAdd(st + 3, (unsigned long long)n_evict);
+    a.stepctr[u] = t + 1;
+  }
 
   // 5. map update: the j-th miss takes the j-th victim
   for (int j = tid; j < m; j += kDiffThreads) {
     const int i = lmiss[j];
     const int tok = topk[i];
     const int v = lvict[j];
-    const int old = slot2tok[v];
-    if (old >= 0) {
-      tok2slot[old] = -1;
-      atomicAdd(&n_evict, 1);
-    }
     slot2tok[v] = tok;
     tok2slot[tok] = v;
     lu[v] = t;
     a.miss_pos[bk + j] = i;
     a.victims[bk + j] = v;
-    a.evicted[bk + j] = old;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    a.counts[4 * b + 0] = n_hit;
-    a.counts[4 * b + 1] = m;
-    a.counts[4 * b + 2] = n_evict;
-    a.counts[4 * b + 3] = 1;
-    a.stats[4 * u + 0] += 1;
-    a.stats[4 * u + 1] += n_hit;
-    a.stats[4 * u + 2] += m;
-    a.stats[4 * u + 3] += n_evict;
-    a.stepctr[u] = t + 1;
   }
 }
 
@@ -682,7 +702,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
 size_t diff_lds_bytes(int S, int K) {
   int hb = 1;
   while ((1 << hb) < 2 * K) ++hb;
-  return (size_t)((S * 2 + 15) & ~15) + (size_t)((S + 15) & ~15) + (size_t)4 * (1u << hb);
+  return (size_t)((S + 15) & ~15) + (size_t)4 * (1u << hb);
 }
 
 static int hash_bits_for(int K) {
@@ -717,7 +737,7 @@ hipError_t launch_clear_status(const DevPtrs& d, hipStream_t s) {
 }
 
 hipError_t prepare_kernels() {
-  // the diff kernel's dynamic LDS can exceed the 64 KiB default (up to 112 KiB)
+  // the diff kernel's dynamic LDS can exceed the 64 KiB default (up to 80 KiB)
   return hipFuncSetAttribute(reinterpret_cast<const void*>(diff_lru_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)diff_lds_bytes(KVS_MAX_SLOTS, KVS_MAX_TOPK));
