@@ -74,8 +74,6 @@ __global__ void clear_status_kernel(int32_t* status) {
 // ------------------------------------------------------------------ diff + LRU
 constexpr int kDiffThreads = 1024;
 constexpr int kDiffWaves = kDiffThreads / 64;
-constexpr int kDiffItems = KVS_MAX_TOPK / kDiffThreads;   // Top-K entries per thread, at most
-constexpr int kDiffSlots = KVS_MAX_SLOTS / kDiffThreads;  // slots per thread, at most
 
 struct DiffArgs {
   const int32_t* topk;     // [B][K]
@@ -126,6 +124,9 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wtot, int& total) {
 // the Top-K entries, the LRU order and the step counter at entry, then the
 // token-to-slot lookups and, for every order position, the token its slot
 // holds (so the thread that picks a victim already knows what it evicts).
+// KPT / SPT: compile-time upper bounds of the Top-K entries and slots per
+// thread (powers of two), so the per-thread loops carry no dead iterations.
+template <int KPT, int SPT>
 __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int wtot[kDiffWaves];
@@ -137,8 +138,8 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   const int b = blockIdx.x;
   const long long u = (long long)b * a.L + a.layer;
   const int H = 1 << a.hash_bits;
-  const int kpt = (K + kDiffThreads - 1) / kDiffThreads;   // <= kDiffItems
-  const int spt = (S + kDiffThreads - 1) / kDiffThreads;   // <= kDiffSlots
+  const int kpt = (K + kDiffThreads - 1) / kDiffThreads;   // <= KPT
+  const int spt = (S + kDiffThreads - 1) / kDiffThreads;   // <= SPT
   const int i0 = tid * kpt;
   const int p0 = tid * spt;
 
@@ -157,31 +158,31 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   const long long bk = (long long)b * K;
 
   // 0. independent loads first: Top-K entries, LRU order, step counter
-  int my_tok[kDiffItems];
+  int my_tok[KPT];
 #pragma unroll
-  for (int j = 0; j < kDiffItems; ++j) {
+  for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
     my_tok[j] = (j < kpt && i < K) ? topk[i] : 0;
   }
-  int my_ord[kDiffSlots];
+  int my_ord[SPT];
 #pragma unroll
-  for (int q = 0; q < kDiffSlots; ++q) {
+  for (int q = 0; q < SPT; ++q) {
     const int p = p0 + q;
     my_ord[q] = (q < spt && p < S) ? (int)gorder[p] : 0;
   }
   const int t = a.stepctr[u];
   // the token held by the slot at each of this thread's order positions
-  int my_old[kDiffSlots];
+  int my_old[SPT];
 #pragma unroll
-  for (int q = 0; q < kDiffSlots; ++q) {
+  for (int q = 0; q < SPT; ++q) {
     const int p = p0 + q;
     my_old[q] = (q < spt && p < S) ? slot2tok[my_ord[q]] : -1;
     if (q < spt && p < S) flag[p] = 0;
   }
   // 1a. slot lookup of every in-range entry, issued before the first barrier
-  int my_slot[kDiffItems];
+  int my_slot[KPT];
 #pragma unroll
-  for (int j = 0; j < kDiffItems; ++j) {
+  for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
     const int tok = my_tok[j];
     my_slot[j] = (j < kpt && i < K && tok >= 0 && (long long)tok < a.N) ? tok2slot[tok] : -1;
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
 
   // 1b. validation (range, duplicates via an LDS open-addressing set); hit flags
 #pragma unroll
-  for (int j = 0; j < kDiffItems; ++j) {
+  for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
     if (j < kpt && i < K) {
       const int tok = my_tok[j];
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   // 2. sparse diff: record slot_of, touch hits, compact misses in Top-K order
   int cnt = 0;
 #pragma unroll
-  for (int j = 0; j < kDiffItems; ++j) {
+  for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
     if (j < kpt && i < K) {
       a.slot_of[bk + i] = my_slot[j];
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   int m;
   int r = wg_exclusive_scan(cnt, wtot, m);
 #pragma unroll
-  for (int j = 0; j < kDiffItems; ++j) {
+  for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
     if (j < kpt && i < K && my_slot[j] < 0) lmiss[r++] = i;
   }
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   //    other non-hit slots keep their relative order at the front of the new order
   cnt = 0;
 #pragma unroll
-  for (int q = 0; q < kDiffSlots; ++q) {
+  for (int q = 0; q < SPT; ++q) {
     const int p = p0 + q;
     if (q < spt && p < S && flag[my_ord[q]] == 0) ++cnt;
   }
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   r = wg_exclusive_scan(cnt, wtot, n_nonhit);
   int my_evict = 0;
 #pragma unroll
-  for (int q = 0; q < kDiffSlots; ++q) {
+  for (int q = 0; q < SPT; ++q) {
     const int p = p0 + q;
     if (q < spt && p < S) {
       const int s = my_ord[q];
@@ -289,14 +290,14 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   //    ascending by slot
   cnt = 0;
 #pragma unroll
-  for (int q = 0; q < kDiffSlots; ++q) {
+  for (int q = 0; q < SPT; ++q) {
     const int s = p0 + q;
     if (q < spt && s < S && flag[s] != 0) ++cnt;
   }
   int n_touched;
   r = S - K + wg_exclusive_scan(cnt, wtot, n_touched);
 #pragma unroll
-  for (int q = 0; q < kDiffSlots; ++q) {
+  for (int q = 0; q < SPT; ++q) {
     const int s = p0 + q;
     if (q < spt && s < S && flag[s] != 0) gorder[r++] = (uint16_t)s;
   }
@@ -736,11 +737,37 @@ hipError_t launch_clear_status(const DevPtrs& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The instantiation of diff_lru_kernel whose per-thread bounds cover K and S.
+template <int KPT>
+static const void* diff_kernel_spt(int spt) {
+  if (spt <= 1) return reinterpret_cast<const void*>(diff_lru_kernel<KPT, 1>);
+  if (spt <= 2) return reinterpret_cast<const void*>(diff_lru_kernel<KPT, 2>);
+  if (spt <= 4) return reinterpret_cast<const void*>(diff_lru_kernel<KPT, 4>);
+  if (spt <= 8) return reinterpret_cast<const void*>(diff_lru_kernel<KPT, 8>);
+  return reinterpret_cast<const void*>(diff_lru_kernel<KPT, 16>);
+}
+static const void* diff_kernel_for(int K, int S) {
+  const int kpt = (K + kDiffThreads - 1) / kDiffThreads;
+  const int spt = (S + kDiffThreads - 1) / kDiffThreads;
+  if (kpt <= 1) return diff_kernel_spt<1>(spt);
+  if (kpt <= 2) return diff_kernel_spt<2>(spt);
+  if (kpt <= 4) return diff_kernel_spt<4>(spt);
+  return diff_kernel_spt<8>(spt);
+}
+static_assert(KVS_MAX_TOPK <= 8 * kDiffThreads && KVS_MAX_SLOTS <= 16 * kDiffThreads,
+              "diff_lru instantiations cover the limits");
+
 hipError_t prepare_kernels() {
   // the diff kernel's dynamic LDS can exceed the 64 KiB default (up to 80 KiB)
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(diff_lru_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)diff_lds_bytes(KVS_MAX_SLOTS, KVS_MAX_TOPK));
+  const int max_lds = (int)diff_lds_bytes(KVS_MAX_SLOTS, KVS_MAX_TOPK);
+  for (int kpt = 1; kpt <= 8; kpt *= 2)
+    for (int spt = 1; spt <= 16; spt *= 2) {
+      const hipError_t e = hipFuncSetAttribute(
+          diff_kernel_for(kpt * kDiffThreads, spt * kDiffThreads),
+          hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
 }
 
 hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
@@ -766,8 +793,9 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const
   a.L = lay.L;
   a.layer = layer;
   a.hash_bits = hash_bits_for(lay.K);
-  hipLaunchKernelGGL(diff_lru_kernel, dim3(lay.B), dim3(kDiffThreads), lds, s, a);
-  return hipGetLastError();
+  const void* fn = diff_kernel_for(lay.K, lay.S);
+  void* args[] = {&a};
+  return hipLaunchKernel(fn, dim3(lay.B), dim3(kDiffThreads), args, lds, s);
 }
 
 hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
