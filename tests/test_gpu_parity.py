@@ -30,10 +30,10 @@ def _torch():
     return torch
 
 
-def _pool(wl, host=None):
+def _pool(wl, host=None, **kw):
     import token_level_gather_amd as kvs
     return kvs.Pool(wl.batch, wl.layers, wl.context, wl.slots, wl.topk, scale=wl.scale,
-                    host=host)
+                    host=host, **kw)
 
 
 def _u16(t):
@@ -48,11 +48,11 @@ def _bf16_to_f64(bits):
 class Harness:
     """Drives one pool through a workload and checks sampled units each step."""
 
-    def __init__(self, wl, steps, check_reqs, fill="all"):
+    def __init__(self, wl, steps, check_reqs, fill="all", **pool_kw):
         torch = _torch()
         self.wl, self.steps = wl, steps
         self.check_reqs = list(check_reqs)
-        self.pool = _pool(wl)
+        self.pool = _pool(wl, **pool_kw)
         host = self.pool.host.array
         if fill == "all":
             W.fill_pool(host, wl)
@@ -130,8 +130,8 @@ class Harness:
         self.pool.host.free()
 
 
-def _case(wl, steps, reqs, fill="all"):
-    h = Harness(wl, steps, reqs, fill)
+def _case(wl, steps, reqs, fill="all", **pool_kw):
+    h = Harness(wl, steps, reqs, fill, **pool_kw)
     try:
         stats = h.run()
         print(f"{wl.name}: steps {steps} max_abs {h.max_abs:.3g} max_rel {h.max_rel:.3g} "
@@ -159,6 +159,21 @@ def test_4k_context_single_request_all_steps():
 def test_small_shapes_every_unit(shape):
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="small", steps=6, **shape)
     _case(wl, wl.steps, range(wl.batch))
+
+
+@pytest.mark.parametrize("topk,splits", [
+    (300, 1),    # 5 tiles in one split: two full pairs and an odd tail
+    (300, 2),    # 2 + 3 tiles
+    (300, 5),    # one tile per split (no full pair, tail only)
+    (1025, 4),   # 4, 4, 4, 5 tiles: even splits and a ragged last tile
+    (1025, 17),  # every split a single tile, the last one a 1-token tile
+])
+def test_attention_split_counts(topk, splits):
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="splits", batch=3, context=4000,
+                                                  slots=1100, topk=topk, steps=3,
+                                                  fresh_rate=0.3)
+    h, _ = _case(wl, wl.steps, range(wl.batch), attn_splits=splits)
+    assert h.pool.sizes.attn_splits == splits
 
 
 def test_zipf_stream_small():

@@ -441,6 +441,10 @@ constexpr int kKSteps = kRowElems / 32;         // 18 MFMA k-steps over 576 dims
 constexpr int kKHalf = kKSteps / 2;             // each Q.K^T wave takes half of them
 constexpr int kPRow = kTile + 8;                // bf16 P row stride (144 B)
 constexpr int kMaxSplits = 64;
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: data format
+// 32 bits, everything else zero.  Untyped loads ignore the format, but a zero
+// format would mark the resource invalid.
+constexpr int kBufRsrcWord3 = 0x00020000;
 static_assert(kTile * 8 == kAttnThreads && kAttnItems * 8 == kRowChunks, "attention tiling");
 static_assert(kKHalf * 2 == kKSteps, "k split");
 
@@ -494,15 +498,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   const int te = (int)((long long)(sp + 1) * ntiles / a.splits);
   const u32x4* rows = reinterpret_cast<const u32x4*>(a.cbuf + (long long)b * K * kRowElems);
 
-  // Q as A-operand fragments: head r16, dims (kh*9 + ks)*32 + g*8 .. +7
   bf16x8 qf[kKHalf];
-  {
-    const u32x4* qh =
-        reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
-#pragma unroll
-    for (int ks = 0; ks < kKHalf; ++ks) qf[ks] = as_bf16x8(qh[(kh * kKHalf + ks) * 4 + g]);
-  }
-
   float m_run = -INFINITY, l_run = 0.f;   // per head, replicated over its 32 softmax threads
   f32x4 acc[4];
 #pragma unroll
@@ -511,14 +507,23 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   // two register buffers: the rows of the next two tiles are in flight while a
   // tile is consumed from LDS
   u32x4 ra[kAttnItems], rb[kAttnItems];
-  // 8 threads per row: thread (row tid / 8, sub tid % 8) moves chunks sub + 8j
+  // 8 threads per row: thread (row tid / 8, sub tid % 8) moves chunks sub + 8j.
+  // The rows are read through a buffer resource that spans this request's K
+  // rows: the hardware range check returns zeros for rows >= K and for the
+  // out-of-range offset given for tiles past te.  So every load is issued
+  // unconditionally, every path through the loop has the same number of loads
+  // in flight, and the wait before a tile's LDS store covers only that tile's
+  // own loads (a branch per load would make the count path-dependent and the
+  // compiler would then drain everything before each use).
   const int lrow = tid >> 3, lsub = tid & 7;
+  const int rec_bytes = K * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, rec_bytes, kBufRsrcWord3);
   auto load_tile = [&](u32x4 (&dst)[kAttnItems], int tile) {
-    const int tok = tile * kTile + lrow;
-    const u32x4* src = rows + (long long)tok * kRowChunks + lsub;
+    const int off = tile < te ? (tile * kTile + lrow) * kRowBytes + lsub * 16 : rec_bytes;
 #pragma unroll
     for (int j = 0; j < kAttnItems; ++j)
-      dst[j] = tok < K ? src[8 * j] : u32x4{0u, 0u, 0u, 0u};
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + j * 128, 0, 0);
   };
   const int lsw = lds_swz(lrow);
   auto store_tile = [&](const u32x4 (&src)[kAttnItems]) {
@@ -609,24 +614,30 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   // tiles two at a time so the register buffers alternate without copies:
   // at the top of each iteration LDS holds `tile` and rb holds tile + 1
   if (tb < te) {
+    // Q as A-operand fragments: head r16, dims (kh*9 + ks)*32 + g*8 .. +7
+    const u32x4* qh =
+        reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
+#pragma unroll
+    for (int ks = 0; ks < kKHalf; ++ks) qf[ks] = as_bf16x8(qh[(kh * kKHalf + ks) * 4 + g]);
     load_tile(ra, tb);
-    if (tb + 1 < te) load_tile(rb, tb + 1);
+    load_tile(rb, tb + 1);
     store_tile(ra);
-  }
-  __syncthreads();
-  for (int tile = tb; tile < te; tile += 2) {
-    if (tile + 2 < te) load_tile(ra, tile + 2);
-    compute(tile);
-    if (tile + 1 < te) {
+    __syncthreads();
+    // full pairs; one exit, so the loads in flight are the same (rb's) on the
+    // back edge and at the exit.  The last pair's ra load and store are of the
+    // tile past te: the range check makes them zeros that nothing reads.
+    int tile = tb;
+    for (; tile + 1 < te; tile += 2) {
+      load_tile(ra, tile + 2);
+      compute(tile);
       store_tile(rb);
       __syncthreads();
-      if (tile + 3 < te) load_tile(rb, tile + 3);
+      load_tile(rb, tile + 3);
       compute(tile + 1);
-      if (tile + 2 < te) {
-        store_tile(ra);
-        __syncthreads();
-      }
+      store_tile(ra);
+      __syncthreads();
     }
+    if (tile < te) compute(tile);   // odd tile count: LDS holds the last tile
   }
 
   // partials: acc lane holds O[h = 4g + j][e = 64w + 16nt + r16]
