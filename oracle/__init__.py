@@ -5,6 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 its Python binding) never calls it; it shares no code with it.
 """
 from .kvs_oracle import (  # noqa: F401
+    PAD,
+    SLOT_PAD,
     KvsError,
     OracleUnit,
     StepRecord,

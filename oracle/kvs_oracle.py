@@ -32,6 +32,15 @@ The pages leave the exact rules open; this oracle reads them as follows:
   slots and newly filled slots get ``last_used = t``.
 * KV rows are MLA rows of 576 bf16 values; scores use all 576 dims, values are
   dims 0..511, scale 1/sqrt(576); softmax and sums in float64 here.
+* Padded Top-K (``padded=True``): a selector may return fewer than K tokens
+  (a sequence shorter than K); the value -1 marks an empty entry.  An empty
+  entry is neither a hit nor a miss: it reads no map, takes no slot, does not
+  count as "a token of the current Top-K set" for the LRU, gathers a zero row
+  and is left out of the softmax.  A step whose entries are all empty still
+  counts as a step; its output is zero and its log-sum-exp -inf.
+* Lifecycle "publish" of a decode step's new row (``append``): the row
+  replaces the token's row in the host pool and, if the token is resident in
+  the hot buffer, that slot's copy too, so hot copies always equal the pool.
 
 There is no approximation in the method: every step is an exact definition,
 so the oracle is that definition written out.  The LRU victim choice sorts the
@@ -47,6 +56,10 @@ import numpy as np
 
 ROW_DIM = 576
 V_DIM = 512
+
+
+PAD = -1         # an empty Top-K entry when the step is padded
+SLOT_PAD = -2    # slot_of of an empty entry (-1 = miss, >= 0 = hit slot)
 
 
 class KvsError(ValueError):
@@ -65,8 +78,12 @@ def attention_fp64(q_bits: np.ndarray, rows_bits: np.ndarray, scale: float,
 
     q_bits: [H][D] bf16 bits; rows_bits: [K][D] bf16 bits (keys are the whole
     rows, values their first ``v_dim`` dims).  Returns (out [H][v_dim], lse [H])
-    with lse the natural-log log-sum-exp of the scaled scores.
+    with lse the natural-log log-sum-exp of the scaled scores.  Over no rows at
+    all (every entry of a padded step empty) the output is zero and lse -inf.
     """
+    if rows_bits.shape[0] == 0:
+        h = q_bits.shape[0]
+        return np.zeros((h, v_dim)), np.full(h, -np.inf)
     q = bf16_bits_to_f64(q_bits)
     kv = bf16_bits_to_f64(rows_bits)
     z = (q @ kv.T) * scale                      # [H][K]
@@ -84,7 +101,7 @@ class StepRecord:
     """Everything one unit-step produces, for comparison with the device."""
 
     t: int
-    slot_of: np.ndarray      # [K] slot of topk[i] before the step, -1 = miss
+    slot_of: np.ndarray      # [K] slot of topk[i] before the step, -1 = miss, -2 = empty
     miss_pos: np.ndarray     # [n_miss] Top-K positions of the misses, ascending
     victims: np.ndarray      # [n_miss] slot given to the j-th miss
     evicted: np.ndarray      # [n_miss] token that slot held before (-1 = empty)
@@ -98,7 +115,11 @@ class StepRecord:
 
     @property
     def n_hit(self) -> int:
-        return int(self.slot_of.size - self.miss_pos.size)
+        return int((self.slot_of >= 0).sum())
+
+    @property
+    def n_pad(self) -> int:
+        return int((self.slot_of == SLOT_PAD).sum())
 
 
 class OracleUnit:
@@ -123,27 +144,31 @@ class OracleUnit:
     # -- one decode step ---------------------------------------------------
     def step(self, topk: np.ndarray, pool_rows: np.ndarray,
              q_bits: Optional[np.ndarray] = None, scale: float = 1.0 / 24.0,
-             v_dim: int = V_DIM) -> StepRecord:
+             v_dim: int = V_DIM, padded: bool = False) -> StepRecord:
         """Run one step for this unit.
 
         topk: [K] token indices; pool_rows: [N][576] bf16 bits of this unit's
         host pool; q_bits: [H][576] bf16 bits or None to skip attention.
+        padded: entries equal to PAD (-1) are empty.
         """
         topk = np.asarray(topk, dtype=np.int64)
         K = self.K
         if topk.shape != (K,):
             raise KvsError("topk has the wrong length")
+        valid = (topk != PAD) if padded else np.ones(K, dtype=bool)
+        vt = topk[valid]
         # 1. validate (unique, in range); invalid input leaves the state alone
-        if topk.min() < 0 or topk.max() >= self.N:
+        if vt.size and (vt.min() < 0 or vt.max() >= self.N):
             raise KvsError("Top-K index out of range")
-        if np.unique(topk).size != K:
+        if np.unique(vt).size != vt.size:
             raise KvsError("duplicate Top-K index")
         t = self.t
 
         # 2. lookup + diff: hit iff the token maps to a slot; misses in array order
-        slot_of = self.tok2slot[topk].copy()
+        slot_of = np.full(K, SLOT_PAD, dtype=np.int64)
+        slot_of[valid] = self.tok2slot[vt]
         hit = slot_of >= 0
-        miss_pos = np.flatnonzero(~hit)
+        miss_pos = np.flatnonzero(slot_of == -1)
         n_miss = miss_pos.size
 
         # 3. touch the hit slots
@@ -170,11 +195,11 @@ class OracleUnit:
 
         # 6. index copy: hits from the hot copy (before write-back), misses from the
         #    pool; then write the misses back into their victim slots
-        cbuf = np.empty((K, ROW_DIM), dtype=np.uint16)
+        cbuf = np.zeros((K, ROW_DIM), dtype=np.uint16)   # empty entries stay zero
         for i in range(K):
             if hit[i]:
                 cbuf[i] = self.hot[slot_of[i]] if self.keep_hot else pool_rows[topk[i]]
-            else:
+            elif valid[i]:
                 cbuf[i] = pool_rows[topk[i]]
         if self.keep_hot:
             for j in range(n_miss):
@@ -183,11 +208,22 @@ class OracleUnit:
         # 7. Top-K attention over the gathered rows
         out = lse = None
         if q_bits is not None:
-            out, lse = attention_fp64(q_bits, cbuf, scale, v_dim)
+            out, lse = attention_fp64(q_bits, cbuf[valid], scale, v_dim)
 
         self.t = t + 1
         return StepRecord(t=t, slot_of=slot_of, miss_pos=miss_pos, victims=victims,
                           evicted=evicted, cbuf=cbuf, out=out, lse=lse)
+
+    # -- lifecycle "publish" of one new row --------------------------------
+    def append(self, pool_rows: np.ndarray, pos: int, row: np.ndarray) -> None:
+        """Write ``row`` ([576] bf16 bits) as token ``pos`` of this unit's host pool
+        (``pool_rows``, modified in place) and into its hot slot if it is resident."""
+        if not 0 <= pos < self.N:
+            raise KvsError("append position out of range")
+        pool_rows[pos] = row
+        s = self.tok2slot[pos]
+        if s >= 0 and self.keep_hot:
+            self.hot[s] = row
 
     # -- views ------------------------------------------------------------
     def resident(self) -> set:
@@ -196,11 +232,11 @@ class OracleUnit:
 
 def run_unit(context: int, slots: int, topk_stream: np.ndarray, pool_rows: np.ndarray,
              q_stream: Optional[np.ndarray] = None, scale: float = 1.0 / 24.0,
-             keep_hot: bool = True) -> List[StepRecord]:
+             keep_hot: bool = True, padded: bool = False) -> List[StepRecord]:
     """Replay a whole Top-K stream ([T][K]) through one fresh unit."""
     unit = OracleUnit(context, slots, topk_stream.shape[1], keep_hot=keep_hot)
     recs = []
     for t in range(topk_stream.shape[0]):
         q = None if q_stream is None else q_stream[t]
-        recs.append(unit.step(topk_stream[t], pool_rows, q, scale))
+        recs.append(unit.step(topk_stream[t], pool_rows, q, scale, padded=padded))
     return recs

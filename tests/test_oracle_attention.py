@@ -120,3 +120,47 @@ def test_step_attention_uses_gathered_rows():
         out, lse = attention_fp64(q, pool[topk], SCALE)
         np.testing.assert_array_equal(rec.out, out)
         np.testing.assert_array_equal(rec.lse, lse)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_padded_step_equals_dense_masked_softmax(seed):
+    # empty entries are masked out of the softmax (as tokens outside the Top-K
+    # set are in the dense form), not scored as zero rows
+    rng = np.random.default_rng(40 + seed)
+    n_ctx, slots, k = 300, 64, 48
+    pool = _bf16(rng, n_ctx, 576)
+    q = _bf16(rng, 16, 576)
+    topk = rng.choice(n_ctx, size=k, replace=False).astype(np.int64)
+    topk[rng.random(k) < 0.4] = -1
+    sel = topk[topk >= 0]
+    rec = OracleUnit(n_ctx, slots, k).step(topk, pool, q, SCALE, padded=True)
+    qf, kv = bf16_bits_to_f64(q), bf16_bits_to_f64(pool)
+    z = qf @ kv.T * SCALE
+    zm = z + np.where(np.isin(np.arange(n_ctx), sel), 0.0, -np.inf)
+    w = np.exp(zm - zm.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(rec.out, w @ kv[:, :512], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(rec.lse, logsumexp(z[:, sel], axis=1), rtol=1e-12)
+
+
+def test_padded_single_valid_entry_gives_that_row():
+    rng = np.random.default_rng(44)
+    pool = _bf16(rng, 50, 576)
+    q = _bf16(rng, 16, 576)
+    topk = np.array([-1, -1, 17, -1, -1])
+    rec = OracleUnit(50, 8, 5).step(topk, pool, q, SCALE, padded=True)
+    assert np.array_equal(rec.out, np.broadcast_to(bf16_bits_to_f64(pool[17])[:512], (16, 512)))
+    np.testing.assert_allclose(rec.lse, bf16_bits_to_f64(q) @ bf16_bits_to_f64(pool[17]) * SCALE,
+                               rtol=1e-13)
+
+
+def test_all_empty_step_gives_zero_output_and_minus_inf_lse():
+    rng = np.random.default_rng(45)
+    pool = _bf16(rng, 50, 576)
+    u = OracleUnit(50, 8, 4)
+    u.step(np.array([1, 2, 3, 4]), pool)
+    t2s = u.tok2slot.copy()
+    rec = u.step(np.full(4, -1), pool, _bf16(rng, 16, 576), SCALE, padded=True)
+    assert not rec.out.any() and np.all(rec.lse == -np.inf)
+    assert rec.t == 1 and u.t == 2 and np.array_equal(u.tok2slot, t2s)
+    assert rec.n_miss == 0 and rec.n_hit == 0 and rec.n_pad == 4

@@ -15,6 +15,8 @@ import pytest
 from oracle import KvsError, OracleUnit, run_unit
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "lru_trace_n8_s4_k2.json")
+GOLDEN_PADDED = os.path.join(os.path.dirname(__file__), "golden",
+                             "lru_trace_padded_n8_s4_k3.json")
 
 
 def _tagged_pool(n_ctx: int) -> np.ndarray:
@@ -241,3 +243,102 @@ def test_free_then_cold_refill():
     assert u.t == 3 and not u.resident()
     rec = u.step(np.array([1, 2, 3, 4]), pool)
     assert rec.t == 3 and rec.n_miss == 4 and rec.victims.tolist() == [0, 1, 2, 3]
+
+
+# ---------------------------------------------------------------- padded Top-K
+
+def test_golden_padded_trace_worked_by_hand():
+    g = json.load(open(GOLDEN_PADDED))
+    pool = _tagged_pool(g["context"])
+    u = OracleUnit(g["context"], g["slots"], g["topk"])
+    for st in g["steps"]:
+        rec = u.step(np.array(st["topk"]), pool, padded=True)
+        assert rec.t == st["t"]
+        assert rec.slot_of.tolist() == st["slot_of"]
+        assert rec.miss_pos.tolist() == st["miss_pos"]
+        assert rec.victims.tolist() == st["victims"]
+        assert rec.evicted.tolist() == st["evicted"]
+        assert u.last_used.tolist() == st["last_used"]
+        assert u.slot2tok.tolist() == st["slot2tok"]
+        for i, src in enumerate(st["cbuf_src"]):
+            if src == "z":
+                assert not rec.cbuf[i].any()
+            else:
+                assert int(rec.cbuf[i, 0]) == st["topk"][i] + 1
+                if src[0] == "h":
+                    assert rec.slot_of[i] == int(src[1:])
+    assert u.tok2slot.tolist() == g["final_tok2slot"]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_padded_matches_order_array_model_on_valid_tokens(seed):
+    # the list model knows nothing of padding: it sees only each step's valid tokens
+    rng = np.random.default_rng(300 + seed)
+    n_ctx = int(rng.integers(2, 50))
+    slots = int(rng.integers(1, 17))
+    k = int(rng.integers(1, min(slots, n_ctx) + 1))
+    width = int(rng.integers(k, n_ctx + 1))
+    stream = []
+    for _ in range(25):
+        row = rng.choice(width, size=k, replace=False).astype(np.int64)
+        row[rng.random(k) < rng.choice([0.0, 0.3, 1.0])] = -1
+        stream.append(row)
+    pool = _tagged_pool(n_ctx)
+    recs = run_unit(n_ctx, slots, np.array(stream), pool, padded=True)
+    model = order_array_model(n_ctx, slots, [[int(x) for x in r if x >= 0] for r in stream])
+    u = OracleUnit(n_ctx, slots, k)
+    for row, rec, (victims, slot2tok) in zip(stream, recs, model):
+        assert rec.victims.tolist() == victims
+        assert rec.n_hit + rec.n_miss + rec.n_pad == k and rec.n_pad == int((row < 0).sum())
+        assert (rec.slot_of[row < 0] == -2).all()
+        assert not rec.cbuf[row < 0].any()
+        assert np.array_equal(rec.cbuf[row >= 0], pool[row[row >= 0]])
+        u.step(row, pool, padded=True)
+        assert u.slot2tok.tolist() == slot2tok
+
+
+def test_padded_without_pads_is_the_unpadded_step():
+    rng = np.random.default_rng(5)
+    pool = rng.integers(0, 65536, size=(60, 576), dtype=np.uint16)
+    a, b = OracleUnit(60, 20, 8), OracleUnit(60, 20, 8)
+    for _ in range(12):
+        topk = rng.choice(40, size=8, replace=False)
+        ra, rb = a.step(topk, pool), b.step(topk, pool, padded=True)
+        for f in ("slot_of", "miss_pos", "victims", "evicted", "cbuf"):
+            assert np.array_equal(getattr(ra, f), getattr(rb, f))
+    assert np.array_equal(a.last_used, b.last_used) and np.array_equal(a.tok2slot, b.tok2slot)
+
+
+def test_padded_invalid_entries_still_raise():
+    pool = _tagged_pool(16)
+    u = OracleUnit(16, 8, 4)
+    u.step(np.array([1, -1, 3, -1]), pool, padded=True)
+    snap = (u.tok2slot.copy(), u.last_used.copy(), u.t)
+    for bad in ([-2, 2, 3, 4], [1, -1, 16, -1], [5, -1, 5, 7]):
+        with pytest.raises(KvsError):
+            u.step(np.array(bad), pool, padded=True)
+        assert np.array_equal(u.tok2slot, snap[0]) and np.array_equal(u.last_used, snap[1])
+        assert u.t == snap[2]
+    with pytest.raises(KvsError):          # without padding, -1 is out of range
+        u.step(np.array([1, -1, 3, 4]), pool)
+
+
+# ---------------------------------------------------------------- append (publish of a new row)
+
+def test_append_updates_pool_and_resident_hot_copy():
+    rng = np.random.default_rng(9)
+    pool = rng.integers(0, 65536, size=(32, 576), dtype=np.uint16)
+    u = OracleUnit(32, 8, 4)
+    u.step(np.array([3, 9, 12, 20]), pool)
+    new_res = rng.integers(0, 65536, size=576, dtype=np.uint16)     # token 9: resident
+    new_cold = rng.integers(0, 65536, size=576, dtype=np.uint16)    # token 30: not resident
+    slot9 = int(u.tok2slot[9])
+    u.append(pool, 9, new_res)
+    u.append(pool, 30, new_cold)
+    assert np.array_equal(pool[9], new_res) and np.array_equal(pool[30], new_cold)
+    assert np.array_equal(u.hot[slot9], new_res)
+    rec = u.step(np.array([9, 30, 3, 12]), pool)
+    assert rec.slot_of[0] == slot9                      # served from the hot copy
+    assert np.array_equal(rec.cbuf[0], new_res) and np.array_equal(rec.cbuf[1], new_cold)
+    with pytest.raises(KvsError):
+        u.append(pool, 32, new_res)
