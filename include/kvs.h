@@ -102,6 +102,16 @@ typedef struct kvs_config {
 /* kvs_config.flags: give the hit-copy workgroups the first grid indices of the
  * gather launch (default: the PCIe fetch workgroups come first). */
 #define KVS_FLAG_HITS_FIRST 1
+/* kvs_config.flags: padded Top-K.  A selector may return fewer than K tokens
+ * (a sequence shorter than K); a Top-K entry equal to -1 is then empty.  An
+ * empty entry is neither a hit nor a miss: it reads no map, takes no slot,
+ * does not shield any slot from eviction, gathers a zero row into cbuf and is
+ * left out of the softmax.  A step whose entries are all empty still advances
+ * the unit's step counter; its out row is zero and its lse -inf.  Without this
+ * flag -1 is out of range (KVS_ERANGE).  The pages do not describe padding:
+ * it completes the request lifecycle of "XM-Sparse", HiSparse integration
+ * section, for requests shorter than K. */
+#define KVS_FLAG_PADDED_TOPK 2
 
 /* Bytes each caller buffer must hold (see kvs_buffers). */
 typedef struct kvs_sizes {
@@ -153,7 +163,8 @@ typedef struct kvs_unit_state {
   int32_t* slot2tok;    /* [S]: token in slot s, -1 if empty */
   int32_t* last_used;   /* [S]: step stamp of slot s, -1 if never used */
   int32_t* lru_order;   /* [S]: slots in ascending (last_used, slot) order */
-  int32_t* slot_of;     /* [K]: last step of request b: slot of topk[i] before it, -1 = miss */
+  int32_t* slot_of;     /* [K]: last step of request b: slot of topk[i] before it, -1 = miss,
+                           -2 = empty entry (KVS_FLAG_PADDED_TOPK) */
   int32_t* miss_pos;    /* [K]: Top-K positions of the misses, first n_miss valid */
   int32_t* victims;     /* [K]: slot given to the j-th miss, first n_miss valid */
   int32_t* evicted;     /* [K]: token that slot held, -1 if empty, first n_miss valid */
@@ -194,10 +205,36 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
 int kvs_publish(kvs_pool* pool, int32_t req, int32_t layer, int64_t first_tok,
                 int64_t n_tok, const void* rows);
 
+/* Lifecycle "publish" from device memory (a prefill's KV rows): enqueue on
+ * `stream` a device-to-host copy of `n_tok` rows (device, [n_tok][576] bf16,
+ * 1152 B each) into the host pool of unit (req, layer) from token `first_tok`.
+ * The same rule as kvs_publish: the tokens must not be resident in the hot
+ * buffer (use kvs_append for a token that may be).  KVS_EINVAL for bad
+ * arguments; nothing is enqueued then. */
+int kvs_publish_device(kvs_pool* pool, int32_t req, int32_t layer, int64_t first_tok,
+                       int64_t n_tok, const void* rows, void* stream);
+
+/* Lifecycle "publish" of one decode step's new KV rows, one per request
+ * ("XM-Sparse", HiSparse integration section: publish -> fetch -> write-back
+ * -> free; the new token of a decode step is published before later steps can
+ * select it).  Enqueued on `stream`, one small kernel:
+ *   rows [B][576] bf16, device: request b's new row for `layer`.
+ *   pos  [B] int64, device: its token index in [0, N), or -1 for a request that
+ *        appends nothing this step.
+ * The row is written over PCIe into the host pool at (b, layer, pos[b]) and,
+ * when that token is resident in the hot buffer, into its slot too, so hot
+ * copies always equal the pool; no map or LRU state changes.  A position
+ * outside [-1, N) skips that request and latches KVS_ERANGE for
+ * kvs_sync_status.  Stream order makes the rows visible to later kvs_step
+ * calls on the same stream and, after synchronisation, to the host. */
+int kvs_append(kvs_pool* pool, int32_t layer, const void* rows, const int64_t* pos,
+               void* stream);
+
 /* Lifecycle "fetch + write-back" and the Top-K attention of one layer for all
  * B requests: four kernel launches on `stream`, no host synchronisation, no
  * device-to-host copy, no other stream.
- *   topk [B][K] int32, device: request b's Top-K token indices, unique, in [0, N).
+ *   topk [B][K] int32, device: request b's Top-K token indices, unique, in [0, N)
+ *        (with KVS_FLAG_PADDED_TOPK also -1 = empty entry; see there).
  *   q    [B][16][576] bf16, device: queries.
  *   out  [B][16][512] bf16, device: attention output.
  *   lse  [B][16] fp32, device, or NULL: natural-log log-sum-exp of the scores.

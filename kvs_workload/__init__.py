@@ -272,3 +272,36 @@ def topk_streams(wl: Workload, steps: Optional[int] = None,
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(run, jobs))
     return out
+
+
+PAD_PATTERNS = ("tail", "scatter", "empty", "none")
+
+
+def pad_topk_streams(streams: np.ndarray, seed: int, patterns=PAD_PATTERNS) -> np.ndarray:
+    """Padded copies of Top-K streams ([T][L][B][K]) for a selector that returns
+    fewer than K tokens: request b uses ``patterns[b % len(patterns)]``:
+
+    * ``tail``: only the first ``v`` entries are tokens, the rest -1, with ``v``
+      drawn per step uniformly from [0, K] (a sequence shorter than K; v = 0
+      and v = K included);
+    * ``scatter``: each entry is -1 with probability 0.3;
+    * ``empty``: every entry -1 on odd steps, no padding on even ones;
+    * ``none``: no padding.
+    """
+    out = streams.copy()
+    T, L, B, K = out.shape
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 3]))
+    for t in range(T):
+        for l in range(L):
+            for b in range(B):
+                kind = patterns[b % len(patterns)]
+                row = out[t, l, b]
+                if kind == "tail":
+                    v = int(rng.integers(0, K + 1))
+                    row[v:] = -1
+                elif kind == "scatter":
+                    row[rng.random(K) < 0.3] = -1
+                elif kind == "empty":
+                    if t % 2 == 1:
+                        row[:] = -1
+    return out

@@ -80,7 +80,7 @@ def test_query_sizes_arithmetic():
     dict(batch=0), dict(layers=0), dict(topk=0), dict(slots=100, topk=200),
     dict(context=100, topk=200, slots=300), dict(slots=16385), dict(topk=8193, slots=9000),
     dict(heads=8), dict(head_dim=512), dict(v_dim=576), dict(scale=0.0),
-    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=2), dict(context=2**31),
+    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=4), dict(context=2**31),
     dict(fetch_blocks=-1), dict(fetch_blocks=65536), dict(hit_blocks=-1), dict(hit_blocks=70000),
     dict(attn_splits=33),   # more splits than 64-token tiles (K = 2048 -> 32)
 ])
@@ -119,7 +119,16 @@ def test_null_pool_calls_are_rejected():
     assert lib.kvs_free_request(None, 0, None) == kvs.KVS_EINVAL
     assert lib.kvs_release(None) == kvs.KVS_EINVAL
     assert lib.kvs_publish(None, 0, 0, 0, 0, None) == kvs.KVS_EINVAL
+    assert lib.kvs_publish_device(None, 0, 0, 0, 0, None, None) == kvs.KVS_EINVAL
+    assert lib.kvs_append(None, 0, None, None, None) == kvs.KVS_EINVAL
     assert lib.kvs_profile_begin(None, 1, 1) == kvs.KVS_EINVAL
+
+
+def test_padded_flag_accepted():
+    cfg = kvs.make_config(batch=2, layers=1, context=4096, slots=512, topk=256,
+                          flags=kvs.KVS_FLAG_PADDED_TOPK | kvs.KVS_FLAG_HITS_FIRST)
+    out = kvs.kvs_sizes()
+    assert kvs.lib().kvs_query_sizes(ctypes.byref(cfg), ctypes.byref(out)) == kvs.KVS_OK
 
 
 def test_strerror():

@@ -48,10 +48,14 @@ def _bf16_to_f64(bits):
 class Harness:
     """Drives one pool through a workload and checks sampled units each step."""
 
-    def __init__(self, wl, steps, check_reqs, fill="all", **pool_kw):
+    def __init__(self, wl, steps, check_reqs, fill="all", padded=False, **pool_kw):
+        import token_level_gather_amd as kvs
         torch = _torch()
         self.wl, self.steps = wl, steps
         self.check_reqs = list(check_reqs)
+        self.padded = padded
+        if padded:
+            pool_kw["flags"] = pool_kw.get("flags", 0) | kvs.KVS_FLAG_PADDED_TOPK
         self.pool = _pool(wl, **pool_kw)
         host = self.pool.host.array
         if fill == "all":
@@ -61,6 +65,8 @@ class Harness:
                 for l in range(wl.layers):
                     W.fill_unit_rows(host[b, l], wl, b, l)
         self.topk = W.topk_streams(wl, steps)
+        if padded:
+            self.topk = W.pad_topk_streams(self.topk, wl.seed)
         self.oracle = {(b, l): OracleUnit(wl.context, wl.slots, wl.topk)
                        for b in self.check_reqs for l in range(wl.layers)}
         self.out = torch.empty((wl.batch, 16, 512), dtype=torch.bfloat16, device="cuda")
@@ -84,7 +90,7 @@ class Harness:
         lse = self.lse.cpu().numpy()
         for b in self.check_reqs:
             u = self.oracle[(b, l)]
-            rec = u.step(tk[b], self.pool.host.array[b, l], q[b], wl.scale)
+            rec = u.step(tk[b], self.pool.host.array[b, l], q[b], wl.scale, padded=self.padded)
             st = self.pool.read_state(b, l)
             n = rec.n_miss
             tag = f"step {t} layer {l} req {b}"
@@ -108,6 +114,9 @@ class Harness:
             occ = u.slot2tok >= 0
             assert np.array_equal(hot[occ], u.hot[occ]), tag + " hot bytes"
             got = _bf16_to_f64(out[b])
+            if rec.n_hit + rec.n_miss == 0:   # every entry empty: zero output, lse -inf
+                assert not got.any() and np.all(lse[b] == -np.inf), tag
+                continue
             err = got - rec.out
             max_abs = float(np.abs(err).max())
             rel = float(np.linalg.norm(err) / np.linalg.norm(rec.out))
@@ -130,8 +139,8 @@ class Harness:
         self.pool.host.free()
 
 
-def _case(wl, steps, reqs, fill="all", **pool_kw):
-    h = Harness(wl, steps, reqs, fill, **pool_kw)
+def _case(wl, steps, reqs, fill="all", padded=False, **pool_kw):
+    h = Harness(wl, steps, reqs, fill, padded, **pool_kw)
     try:
         stats = h.run()
         print(f"{wl.name}: steps {steps} max_abs {h.max_abs:.3g} max_rel {h.max_rel:.3g} "
@@ -174,6 +183,25 @@ def test_attention_split_counts(topk, splits):
                                                   fresh_rate=0.3)
     h, _ = _case(wl, wl.steps, range(wl.batch), attn_splits=splits)
     assert h.pool.sizes.attn_splits == splits
+
+
+@pytest.mark.parametrize("shape", [
+    dict(batch=4, layers=1, context=3000, slots=700, topk=300, fresh_rate=0.3),
+    dict(batch=8, layers=2, context=5000, slots=1100, topk=1025, fresh_rate=0.2),
+    dict(batch=4, layers=1, context=200, slots=64, topk=64, fresh_rate=0.5),
+])
+def test_padded_topk_every_unit(shape):
+    # requests cycle through tail / scatter / all-empty / no padding
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="padded", steps=6, **shape)
+    _case(wl, wl.steps, range(wl.batch), padded=True)
+
+
+def test_padded_topk_explicit_splits():
+    # whole tiles and whole splits of empty entries (tail padding, 4 splits)
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="padded_splits", batch=4, context=5000,
+                                                  slots=1100, topk=1025, steps=5,
+                                                  fresh_rate=0.3)
+    _case(wl, wl.steps, range(wl.batch), padded=True, attn_splits=4)
 
 
 def test_zipf_stream_small():
@@ -306,5 +334,84 @@ def test_publish_rows_then_fetch():
         for bad in ((2, 0, 0, 1), (0, 2, 0, 1), (0, 0, -1, 1), (0, 0, wl.context - 1, 2)):
             with pytest.raises(kvs.KvsError):
                 h.pool.publish(bad[0], bad[1], bad[2], np.zeros((bad[3], 576), np.uint16))
+    finally:
+        h.close()
+
+
+# ---------------------------------------------------------------- device-side publish
+
+def _bf16_rows(rng, n):
+    return W.f32_to_bf16_bits(rng.standard_normal((n, 576)).astype(np.float32))
+
+
+def test_append_rows_then_hit_and_fetch():
+    # one new row per request: a token resident in the hot buffer (the next
+    # step hits it and must read the new bytes from the hot copy), a token that
+    # is not (the next step fetches it from the pool), and two requests with
+    # nothing to append
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="append", batch=4, layers=2, context=3000,
+                                                  slots=400, topk=200, steps=6, fresh_rate=0.3)
+    h = Harness(wl, wl.steps, range(wl.batch))
+    try:
+        for t in range(2):
+            for l in range(wl.layers):
+                h.check(t, l, *h.device_step(t, l))
+        rng = np.random.default_rng(77)
+        host = h.pool.host.array
+        for l in range(wl.layers):
+            st0, st1 = h.pool.read_state(0, l), h.pool.read_state(1, l)
+            res_tok = next(int(x) for x in h.topk[2, l, 0] if st0["tok2slot"][x] >= 0)
+            cold_tok = next(int(x) for x in h.topk[2, l, 1] if st1["tok2slot"][x] < 0)
+            rows = _bf16_rows(rng, wl.batch)
+            pos = np.array([res_tok, cold_tok, -1, -1], dtype=np.int64)
+            before = host[2:, l].copy()
+            h.pool.append(l, torch.from_numpy(rows.view(np.int16)).cuda(),
+                          torch.from_numpy(pos).cuda())
+            torch.cuda.synchronize()
+            assert np.array_equal(host[0, l, res_tok], rows[0])
+            assert np.array_equal(host[1, l, cold_tok], rows[1])
+            assert np.array_equal(host[2:, l], before)
+            slot = int(st0["tok2slot"][res_tok])
+            hrow = wl.slots * 1152
+            hot0 = _u16(h.pool.hot[l * hrow:(l + 1) * hrow]).reshape(wl.slots, 576)
+            assert np.array_equal(hot0[slot], rows[0])
+            h.oracle[(0, l)].append(host[0, l], res_tok, rows[0])
+            h.oracle[(1, l)].append(host[1, l], cold_tok, rows[1])
+        for t in range(2, wl.steps):
+            for l in range(wl.layers):
+                h.check(t, l, *h.device_step(t, l))
+        rc, _ = h.pool.sync_status()
+        assert rc == 0
+        # out-of-range positions: nothing written, KVS_ERANGE latched
+        snap = host[:, 0].copy()
+        bad = np.array([wl.context, -2, -1, -1], dtype=np.int64)
+        h.pool.append(0, torch.from_numpy(_bf16_rows(rng, wl.batch).view(np.int16)).cuda(),
+                      torch.from_numpy(bad).cuda())
+        import token_level_gather_amd as kvs
+        rc, _ = h.pool.sync_status()
+        assert rc == kvs.KVS_ERANGE
+        assert np.array_equal(host[:, 0], snap)
+    finally:
+        h.close()
+
+
+def test_publish_device_rows_then_fetch():
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="publish_dev", batch=2, layers=2,
+                                                  context=3000, slots=400, topk=200, steps=3,
+                                                  fresh_rate=0.3)
+    h = Harness(wl, wl.steps, range(wl.batch))
+    try:
+        rng = np.random.default_rng(78)
+        rows = _bf16_rows(rng, 50)
+        h.pool.publish_device(1, 1, 1000, torch.from_numpy(rows.view(np.int16)).cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(h.pool.host.array[1, 1, 1000:1050], rows)
+        # step 0 of unit (1, 1) selects all 50 published tokens
+        row = h.topk[0, 1, 1]
+        keep = [int(x) for x in row if not 1000 <= x < 1050][: wl.topk - 50]
+        h.topk[0, 1, 1] = np.array(list(range(1000, 1050)) + keep, dtype=np.int32)
+        h.run()
     finally:
         h.close()

@@ -28,13 +28,15 @@ HEADS, HEAD_DIM, V_DIM = 16, 576, 512
 ROW_BYTES = HEAD_DIM * 2
 KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine")
 KVS_FLAG_HITS_FIRST = 1
+KVS_FLAG_PADDED_TOPK = 2
 
 # Every exported symbol of include/kvs.h.
 EXPORTS = (
     "kvs_query_sizes", "kvs_host_alloc", "kvs_host_free", "kvs_create_pool", "kvs_publish",
     "kvs_step", "kvs_free_request", "kvs_sync_status", "kvs_debug_read_state",
     "kvs_profile_begin", "kvs_profile_end", "kvs_release", "kvs_strerror",
-    "kvs_graph_capture", "kvs_graph_launch", "kvs_graph_destroy",
+    "kvs_graph_capture", "kvs_graph_launch", "kvs_graph_destroy", "kvs_publish_device",
+    "kvs_append",
 )
 
 
@@ -116,6 +118,8 @@ def lib() -> ctypes.CDLL:
         "kvs_create_pool": [ctypes.POINTER(kvs_config), ctypes.POINTER(kvs_buffers), vp,
                             ctypes.POINTER(vp)],
         "kvs_publish": [vp, i32, i32, i64, i64, vp],
+        "kvs_publish_device": [vp, i32, i32, i64, i64, vp, vp],
+        "kvs_append": [vp, i32, vp, vp, vp],
         "kvs_step": [vp, i32, vp, vp, vp, vp, vp],
         "kvs_free_request": [vp, i32, vp],
         "kvs_sync_status": [vp, vp, ctypes.POINTER(kvs_step_stats)],
@@ -231,6 +235,22 @@ class Pool:
         assert rows.ndim == 2 and rows.shape[1] == HEAD_DIM
         _check(lib().kvs_publish(self.handle, req, layer, first_tok, rows.shape[0],
                                  rows.ctypes.data), "kvs_publish")
+
+    def publish_device(self, req, layer, first_tok, rows, stream=None):
+        """rows: contiguous device tensor [n][576] of 2-byte elements."""
+        if not rows.is_cuda or rows.dim() != 2 or rows.shape[1] != HEAD_DIM \
+                or rows.element_size() != 2 or not rows.is_contiguous():
+            raise ValueError("expected a contiguous device tensor [n][576] of bf16")
+        _check(lib().kvs_publish_device(self.handle, req, layer, first_tok, rows.shape[0],
+                                        rows.data_ptr(), _stream_ptr(stream)),
+               "kvs_publish_device")
+
+    def append(self, layer, rows, pos, stream=None):
+        """rows [B][576] bf16 and pos [B] int64 (-1 = nothing to append), device."""
+        self._check_dev(rows, (self.B, HEAD_DIM), 2)
+        self._check_dev(pos, (self.B,), 8)
+        _check(lib().kvs_append(self.handle, layer, rows.data_ptr(), pos.data_ptr(),
+                                _stream_ptr(stream)), "kvs_append")
 
     def step(self, layer, topk, q, out, lse=None, stream=None):
         """topk [B][K] int32, q [B][16][576] bf16/uint16, out [B][16][512] bf16 (device)."""

@@ -33,7 +33,7 @@ int make_layout(const kvs_config* c, Layout* lay) {
   if (c->attn_splits < 0 || c->attn_splits > 64) return KVS_EINVAL;
   if (c->fetch_blocks < 0 || c->fetch_blocks > 65535) return KVS_EINVAL;
   if (c->hit_blocks < 0 || c->hit_blocks > 65535) return KVS_EINVAL;
-  if ((c->flags & ~KVS_FLAG_HITS_FIRST) != 0) return KVS_EINVAL;
+  if ((c->flags & ~(KVS_FLAG_HITS_FIRST | KVS_FLAG_PADDED_TOPK)) != 0) return KVS_EINVAL;
   if ((int64_t)c->batch * c->layers > 0x7fffffffLL) return KVS_EINVAL;
 
   const uint64_t B = c->batch, L = c->layers, N = c->context, S = c->slots, K = c->topk;
@@ -272,6 +272,25 @@ int kvs_publish(kvs_pool* p, int32_t req, int32_t layer, int64_t first_tok, int6
   const uint64_t row0 = ((uint64_t)req * p->lay.L + layer) * (uint64_t)p->lay.N + first_tok;
   memcpy(p->host_pool + row0 * kRowBytes, rows, (size_t)n_tok * kRowBytes);
   return KVS_OK;
+}
+
+int kvs_publish_device(kvs_pool* p, int32_t req, int32_t layer, int64_t first_tok,
+                       int64_t n_tok, const void* rows, void* stream) {
+  if (p == nullptr || rows == nullptr) return KVS_EINVAL;
+  if (req < 0 || req >= p->lay.B || layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
+  if (first_tok < 0 || n_tok < 0 || first_tok + n_tok > p->lay.N) return KVS_EINVAL;
+  if (n_tok == 0) return KVS_OK;
+  const uint64_t row0 = ((uint64_t)req * p->lay.L + layer) * (uint64_t)p->lay.N + first_tok;
+  return hip_err(hipMemcpyAsync(p->host_pool + row0 * kRowBytes, rows, (size_t)n_tok * kRowBytes,
+                                hipMemcpyDeviceToHost, (hipStream_t)stream));
+}
+
+int kvs_append(kvs_pool* p, int32_t layer, const void* rows, const int64_t* pos, void* stream) {
+  if (p == nullptr || rows == nullptr || pos == nullptr) return KVS_EINVAL;
+  if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
+  if (((uintptr_t)rows & 15) != 0 || ((uintptr_t)pos & 7) != 0) return KVS_EINVAL;
+  return hip_err(launch_append(p->lay, p->d, layer, (const uint16_t*)rows, pos,
+                               (hipStream_t)stream));
 }
 
 int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, void* out,

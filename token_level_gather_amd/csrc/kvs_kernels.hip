@@ -91,6 +91,7 @@ struct DiffArgs {
   int32_t* counts;         // [B][4]
   long long N;
   int S, K, L, layer, hash_bits;
+  int padded;              // 1: a Top-K entry of -1 is empty
 };
 
 // Exclusive prefix sum of `v` over the workgroup in thread order; `total`
@@ -194,13 +195,16 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   }
   __syncthreads();
 
-  // 1b. validation (range, duplicates via an LDS open-addressing set); hit flags
+  // 1b. validation (range, duplicates via an LDS open-addressing set); hit flags.
+  //     my_slot: >= 0 hit slot, -1 miss, -2 empty entry of a padded Top-K
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
     if (j < kpt && i < K) {
       const int tok = my_tok[j];
-      if (tok < 0 || (long long)tok >= a.N) {
+      if (a.padded && tok == -1) {
+        my_slot[j] = -2;
+      } else if (tok < 0 || (long long)tok >= a.N) {
         atomicOr(&err_bits, 1);
       } else {
         unsigned h = ((unsigned)tok * 2654435761u) >> (32 - a.hash_bits);
@@ -230,7 +234,9 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     return;
   }
 
-  // 2. sparse diff: record slot_of, touch hits, compact misses in Top-K order
+  // 2. sparse diff: record slot_of, touch hits, compact misses in Top-K order.
+  //    One scan counts misses (low 16 bits) and empty entries (high bits):
+  //    K <= 8192, so the low field never carries into the high one.
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -238,17 +244,18 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     if (j < kpt && i < K) {
       a.slot_of[bk + i] = my_slot[j];
       if (my_slot[j] >= 0) lu[my_slot[j]] = t;
-      else ++cnt;
+      else cnt += my_slot[j] == -1 ? 1 : (1 << 16);
     }
   }
-  int m;
-  int r = wg_exclusive_scan(cnt, wtot, m);
+  int packed;
+  int r = wg_exclusive_scan(cnt, wtot, packed) & 0xffff;
+  const int m = packed & 0xffff;
+  const int n_hit = K - m - (packed >> 16);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
-    if (j < kpt && i < K && my_slot[j] < 0) lmiss[r++] = i;
+    if (j < kpt && i < K && my_slot[j] == -1) lmiss[r++] = i;
   }
-  const int n_hit = K - m;
 
   // 3. victims: the first m non-hit slots of the LRU order, evicted here; the
   //    other non-hit slots keep their relative order at the front of the new order
@@ -286,8 +293,8 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   if (my_evict) atomicAdd(&n_evict, my_evict);
   __syncthreads();
 
-  // 4. the K touched slots (hits and victims, all stamped t) close the order,
-  //    ascending by slot
+  // 4. the n_hit + m touched slots (hits and victims, all stamped t) close the
+  //    order, ascending by slot
   cnt = 0;
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     if (q < spt && s < S && flag[s] != 0) ++cnt;
   }
   int n_touched;
-  r = S - K + wg_exclusive_scan(cnt, wtot, n_touched);
+  r = S - (n_hit + m) + wg_exclusive_scan(cnt, wtot, n_touched);
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
     const int s = p0 + q;
@@ -420,10 +427,15 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
     const int i = x * kCopyRows + rsub;
     if (i >= K) continue;
     const int s = a.slot_of[(long long)b * K + i];
-    if (s < 0) continue;
+    if (s == -1) continue;   // a miss: the fetch role writes it
+    u32x4* dst = a.cbuf + ((long long)b * K + i) * kRowChunks + sub;
+    if (s < 0) {             // an empty entry of a padded Top-K gathers a zero row
+#pragma unroll
+      for (int j = 0; j < kCopyItems; ++j) dst[8 * j] = u32x4{0u, 0u, 0u, 0u};
+      continue;
+    }
     const long long u = (long long)b * a.L + a.layer;
     const u32x4* src = a.hot + (u * a.S + s) * kRowChunks + sub;
-    u32x4* dst = a.cbuf + ((long long)b * K + i) * kRowChunks + sub;
     u32x4 v[kCopyItems];
 #pragma unroll
     for (int j = 0; j < kCopyItems; ++j) v[j] = src[8 * j];
@@ -462,10 +474,12 @@ __device__ __forceinline__ int lds_swz(int r) {
 struct AttnArgs {
   const uint16_t* cbuf;   // [B][K][576]
   const uint16_t* q;      // [B][16][576]
+  const int32_t* slot_of; // [B][K]: -2 marks an empty entry of a padded Top-K
   const int32_t* counts;  // [B][4]
   float* part_o;          // [B][splits][16][512]
   float* part_ml;         // [B][splits][16][2]
   int K, splits;
+  int padded;             // 1: mask the entries whose slot_of is -2
   float scale_log2;       // softmax scale * log2(e): scores are kept in log2 units
 };
 
@@ -488,7 +502,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   __shared__ float alpha_s[kHeads];
 
   const int b = blockIdx.y, sp = blockIdx.x;
-  if (a.counts[4 * b + 3] == 0) return;   // combine writes the zero output
+  // invalid input, or no entry at all (padded): combine writes the zero output
+  if (a.counts[4 * b + 3] == 0 || a.counts[4 * b + 0] + a.counts[4 * b + 1] == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int tt = wave & 3, kh = wave >> 2;
@@ -507,6 +522,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   // two register buffers: the rows of the next two tiles are in flight while a
   // tile is consumed from LDS
   u32x4 ra[kAttnItems], rb[kAttnItems];
+  int va[2], vb[2], cv[2];   // slot_of of this thread's two softmax tokens: next tiles, current
   // 8 threads per row: thread (row tid / 8, sub tid % 8) moves chunks sub + 8j.
   // The rows are read through a buffer resource that spans this request's K
   // rows: the hardware range check returns zeros for rows >= K and for the
@@ -519,11 +535,19 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   const int rec_bytes = K * kRowBytes;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, rec_bytes, kBufRsrcWord3);
-  auto load_tile = [&](u32x4 (&dst)[kAttnItems], int tile) {
+  // The slot_of entries of the softmax tokens travel with their tile.  Without
+  // padding the resource is empty: the loads return 0 (valid) and read nothing.
+  const __amdgpu_buffer_rsrc_t vsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.slot_of + (long long)b * K), (short)0, a.padded ? K * 4 : 0, kBufRsrcWord3);
+  const int c2 = (tid & 31) * 2;   // softmax tokens c2, c2 + 1 of a tile
+  auto load_tile = [&](u32x4 (&dst)[kAttnItems], int (&dv)[2], int tile) {
     const int off = tile < te ? (tile * kTile + lrow) * kRowBytes + lsub * 16 : rec_bytes;
 #pragma unroll
     for (int j = 0; j < kAttnItems; ++j)
       dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + j * 128, 0, 0);
+    const int voff = tile < te ? (tile * kTile + c2) * 4 : K * 4;
+    dv[0] = __builtin_amdgcn_raw_buffer_load_b32(vsrc, voff, 0, 0);
+    dv[1] = __builtin_amdgcn_raw_buffer_load_b32(vsrc, voff + 4, 0, 0);
   };
   const int lsw = lds_swz(lrow);
   auto store_tile = [&](const u32x4 (&src)[kAttnItems]) {
@@ -554,20 +578,25 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     }
     __syncthreads();
 
-    // online softmax: head h = tid / 32, tokens 2*(tid % 32) .. +1
+    // online softmax: head h = tid / 32, tokens c2 = 2*(tid % 32) .. +1; tokens
+    // past K and empty entries score -inf
     {
-      const int h = tid >> 5, c2 = (tid & 31) * 2;
+      const int h = tid >> 5;
       const int tok0 = tile * kTile + c2;
       const float* s0 = sc + h * kTile + c2;
       const float* s1 = sc + kHeads * kTile + h * kTile + c2;
-      const float x0 = tok0 < K ? (s0[0] + s1[0]) * a.scale_log2 : -INFINITY;
-      const float x1 = tok0 + 1 < K ? (s0[1] + s1[1]) * a.scale_log2 : -INFINITY;
+      const float x0 =
+          tok0 < K && cv[0] != -2 ? (s0[0] + s1[0]) * a.scale_log2 : -INFINITY;
+      const float x1 =
+          tok0 + 1 < K && cv[1] != -2 ? (s0[1] + s1[1]) * a.scale_log2 : -INFINITY;
       float mx = fmaxf(x0, x1);
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
-      const float p0 = exp2f(x0 - m_new), p1 = exp2f(x1 - m_new);
+      // no scored token yet (empty entries only): keep every weight at 0
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_ref);
+      const float p0 = exp2f(x0 - m_ref), p1 = exp2f(x1 - m_ref);
       float ps = p0 + p1;
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) ps += __shfl_xor(ps, o);
@@ -619,22 +648,28 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
         reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
 #pragma unroll
     for (int ks = 0; ks < kKHalf; ++ks) qf[ks] = as_bf16x8(qh[(kh * kKHalf + ks) * 4 + g]);
-    load_tile(ra, tb);
-    load_tile(rb, tb + 1);
+    load_tile(ra, va, tb);
+    load_tile(rb, vb, tb + 1);
     store_tile(ra);
+    cv[0] = va[0];
+    cv[1] = va[1];
     __syncthreads();
     // full pairs; one exit, so the loads in flight are the same (rb's) on the
     // back edge and at the exit.  The last pair's ra load and store are of the
     // tile past te: the range check makes them zeros that nothing reads.
     int tile = tb;
     for (; tile + 1 < te; tile += 2) {
-      load_tile(ra, tile + 2);
+      load_tile(ra, va, tile + 2);
       compute(tile);
       store_tile(rb);
+      cv[0] = vb[0];
+      cv[1] = vb[1];
       __syncthreads();
-      load_tile(rb, tile + 3);
+      load_tile(rb, vb, tile + 3);
       compute(tile + 1);
       store_tile(ra);
+      cv[0] = va[0];
+      cv[1] = va[1];
       __syncthreads();
     }
     if (tile < te) compute(tile);   // odd tile count: LDS holds the last tile
@@ -667,7 +702,8 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   __shared__ float inv_l;
   const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   uint2* ob = reinterpret_cast<uint2*>(out + ((long long)b * kHeads + h) * kVDim);
-  if (counts[4 * b + 3] == 0) {   // invalid Top-K: zero output, lse = -inf
+  // invalid Top-K, or no entry at all (padded): zero output, lse = -inf
+  if (counts[4 * b + 3] == 0 || counts[4 * b + 0] + counts[4 * b + 1] == 0) {
     ob[tid] = make_uint2(0u, 0u);
     if (lse != nullptr && tid == 0) lse[b * kHeads + h] = -INFINITY;
     return;
@@ -706,6 +742,37 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   ob[tid] = make_uint2(
       (uint32_t)f32_to_bf16_rne(o0 * il) | ((uint32_t)f32_to_bf16_rne(o1 * il) << 16),
       (uint32_t)f32_to_bf16_rne(o2 * il) | ((uint32_t)f32_to_bf16_rne(o3 * il) << 16));
+}
+
+// ------------------------------------------------------------------ append
+// Lifecycle "publish" of one decode step's new rows: workgroup b writes row b
+// of `rows` into the host pool at (b, layer, pos[b]) (PCIe writes to the
+// mapped pinned pool) and, when that token is resident, over its hot slot, so
+// the hot copy keeps equalling the pool.  pos[b] = -1: nothing to append.
+constexpr int kAppendThreads = 128;   // 72 chunks of one row, one per thread
+static_assert(kRowChunks <= kAppendThreads, "append tiling");
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(
+    const u32x4* __restrict__ rows, const long long* __restrict__ pos, u32x4* pool,
+    u32x4* hot, const int32_t* __restrict__ tok2slot, int32_t* status, long long N, int S,
+    int L, int layer) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const long long p = pos[b];
+  if (p == -1) return;
+  if (p < -1 || p >= N) {
+    if (tid == 0) atomicCAS(status, 0, KVS_ERANGE);
+    return;
+  }
+  const long long u = (long long)b * L + layer;
+  const int s = tok2slot[u * N + p];
+  if (tid < kRowChunks) {
+    const u32x4 v = rows[(long long)b * kRowChunks + tid];
+    pool[(u * N + p) * kRowChunks + tid] = v;
+    if (s >= 0) hot[((long long)u * S + s) * kRowChunks + tid] = v;
+  }
+  // system-scope release: the pool row leaves this XCD's L2 for host memory,
+  // where the host and every other XCD's fetches read it
+  __threadfence_system();
 }
 
 }  // namespace
@@ -804,6 +871,7 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const
   a.L = lay.L;
   a.layer = layer;
   a.hash_bits = hash_bits_for(lay.K);
+  a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
   const void* fn = diff_kernel_for(lay.K, lay.S);
   void* args[] = {&a};
   return hipLaunchKernel(fn, dim3(lay.B), dim3(kDiffThreads), args, lds, s);
@@ -844,13 +912,25 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t*
   AttnArgs a;
   a.cbuf = d.cbuf;
   a.q = q;
+  a.slot_of = d.slot_of;
   a.counts = d.counts;
   a.part_o = d.part_o;
   a.part_ml = d.part_ml;
   a.K = lay.K;
   a.splits = lay.splits;
+  a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(attention_kernel, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* rows,
+                         const int64_t* pos, hipStream_t s) {
+  hipLaunchKernelGGL(append_kernel, dim3(lay.B), dim3(kAppendThreads), 0, s,
+                     reinterpret_cast<const u32x4*>(rows), reinterpret_cast<const long long*>(pos),
+                     reinterpret_cast<u32x4*>(const_cast<uint16_t*>(d.pool)),
+                     reinterpret_cast<u32x4*>(d.hot), d.tok2slot, d.status, (long long)lay.N,
+                     lay.S, lay.L, layer);
   return hipGetLastError();
 }
 
