@@ -57,6 +57,9 @@ def parse():
                    help="launch every (step, layer) as a captured HIP graph (inputs in place)")
     p.add_argument("--hits-first", action="store_true",
                    help="hit-copy workgroups take the first grid indices of the gather")
+    p.add_argument("--direct-hot", action="store_true",
+                   help="attention reads the selected rows in place from the hot buffer (no "
+                        "compute buffer; the gather only fetches misses)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (the known-size "
                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -168,7 +171,8 @@ def main():
 
     pool = kvs.Pool(B, L, N, S, K, scale=wl.scale, attn_splits=args.attn_splits,
                     fetch_blocks=args.fetch_blocks, hit_blocks=args.hit_blocks,
-                    flags=kvs.KVS_FLAG_HITS_FIRST if args.hits_first else 0)
+                    flags=(kvs.KVS_FLAG_HITS_FIRST if args.hits_first else 0)
+                    | (kvs.KVS_FLAG_DIRECT_HOT if args.direct_hot else 0))
     W.fill_pool(pool.host.array, wl)
     topk_np = W.topk_streams(wl, total)
     topk = torch.from_numpy(topk_np).cuda()                         # [T][L][B][K]
@@ -251,13 +255,16 @@ def main():
 
         The gather is bound by the host link: its roofline bytes are the miss
         rows read over PCIe; its HBM traffic (hit rows read and written, miss
-        rows written twice) is listed beside them.
+        rows written twice; with the rows read in place, only the miss rows
+        written once) is listed beside them.
         """
+        gather_hbm = ROW * miss_l if args.direct_hot else 2 * ROW * hit_l + 2 * ROW * miss_l
+        attn_idx = 4 * B * K if args.direct_hot else 0     # row_slot reads
         return {
-            "diff_lru": {"bound": "hbm", "bytes": B * (16 * K + 4 * S) + 32 * miss_l},
-            "gather": {"bound": "pcie", "bytes": ROW * miss_l,
-                       "hbm_bytes": 2 * ROW * hit_l + 2 * ROW * miss_l},
-            "attention": {"bound": "hbm", "bytes": B * (K * ROW + 16 * 576 * 2) + part_bytes,
+            "diff_lru": {"bound": "hbm", "bytes": B * (20 * K + 4 * S) + 32 * miss_l},
+            "gather": {"bound": "pcie", "bytes": ROW * miss_l, "hbm_bytes": gather_hbm},
+            "attention": {"bound": "hbm",
+                          "bytes": B * (K * ROW + 16 * 576 * 2) + part_bytes + attn_idx,
                           "flop": B * 2 * 16 * K * (576 + 512)},
             "combine": {"bound": "hbm", "bytes": part_bytes + B * 16 * 512 * 2},
         }
@@ -359,7 +366,8 @@ def main():
                    "topk": K, "fresh_rate": wl.fresh_rate, "fresh_dist": wl.dist,
                    "heads": 16, "head_dim": 576, "v_dim": 512, "attn_splits": splits,
                    "fetch_blocks": pool.sizes.fetch_blocks, "hit_blocks": args.hit_blocks,
-                   "hits_first": bool(args.hits_first), "hip_graph": bool(args.graph)},
+                   "hits_first": bool(args.hits_first), "hip_graph": bool(args.graph),
+                   "direct_hot": bool(args.direct_hot)},
         "decode_steps_per_s": round(1e3 / ms_step, 2),
         "cold_step_ms": None if cold is None else round(cold, 4),
         "miss_rate": round(miss_rate, 5),

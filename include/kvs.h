@@ -112,6 +112,16 @@ typedef struct kvs_config {
  * it completes the request lifecycle of "XM-Sparse", HiSparse integration
  * section, for requests shorter than K. */
 #define KVS_FLAG_PADDED_TOPK 2
+/* kvs_config.flags: attention reads each selected row in place from the hot
+ * buffer (a hit at its slot, a miss at its victim slot after the write-back)
+ * instead of from an assembled compute buffer.  The gather then only fetches
+ * misses over PCIe into their victim slots; no hit row is copied and cbuf is
+ * not used: kvs_query_sizes reports cbuf_bytes = 0 and kvs_buffers.cbuf may be
+ * NULL.  Results are identical; the on-demand assembly of the pages (the
+ * "Sparse Attention-Driven KVCache Management for Domestic AI Supernodes"
+ * abstract: an index-based copy builds the step's data) becomes an indexed
+ * read inside attention. */
+#define KVS_FLAG_DIRECT_HOT 4
 
 /* Bytes each caller buffer must hold (see kvs_buffers). */
 typedef struct kvs_sizes {
@@ -169,6 +179,7 @@ typedef struct kvs_unit_state {
   int32_t* victims;     /* [K]: slot given to the j-th miss, first n_miss valid */
   int32_t* evicted;     /* [K]: token that slot held, -1 if empty, first n_miss valid */
   int32_t* counts;      /* [4]: n_hit, n_miss, n_evicted, valid (1) / invalid input (0) */
+  int32_t* row_slot;    /* [K]: slot holding topk[i]'s row after the step, -1 = empty entry */
   int32_t step;         /* out: the unit's step counter (steps taken) */
 } kvs_unit_state;
 

@@ -72,15 +72,19 @@ def test_query_sizes_arithmetic():
     assert s.meta_bytes >= 64 * (16384 * 4 + 4096 * 10)
     assert s.meta_bytes < 64 * (16384 * 4 + 4096 * 10) + 64 * 64 + 4096
     assert s.attn_splits == 4
-    per = 4 * 64 * 2048 * 4 + 64 * 16 + 64 * 4 * 16 * (512 + 2) * 4
+    # slot_of, miss_pos, victims, evicted, row_slot [B][K] int32; counts; partials
+    per = 5 * 64 * 2048 * 4 + 64 * 16 + 64 * 4 * 16 * (512 + 2) * 4
     assert per <= s.scratch_bytes < per + 8 * 256
+    d = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096,
+                                        topk=2048, flags=kvs.KVS_FLAG_DIRECT_HOT))
+    assert d.cbuf_bytes == 0 and d.hot_bytes == s.hot_bytes
 
 
 @pytest.mark.parametrize("bad", [
     dict(batch=0), dict(layers=0), dict(topk=0), dict(slots=100, topk=200),
     dict(context=100, topk=200, slots=300), dict(slots=16385), dict(topk=8193, slots=9000),
     dict(heads=8), dict(head_dim=512), dict(v_dim=576), dict(scale=0.0),
-    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=4), dict(context=2**31),
+    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=8), dict(context=2**31),
     dict(fetch_blocks=-1), dict(fetch_blocks=65536), dict(hit_blocks=-1), dict(hit_blocks=70000),
     dict(attn_splits=33),   # more splits than 64-token tiles (K = 2048 -> 32)
 ])

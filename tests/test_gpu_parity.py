@@ -56,6 +56,7 @@ class Harness:
         self.padded = padded
         if padded:
             pool_kw["flags"] = pool_kw.get("flags", 0) | kvs.KVS_FLAG_PADDED_TOPK
+        self.direct = bool(pool_kw.get("flags", 0) & kvs.KVS_FLAG_DIRECT_HOT)
         self.pool = _pool(wl, **pool_kw)
         host = self.pool.host.array
         if fill == "all":
@@ -105,9 +106,13 @@ class Harness:
             order = np.lexsort((np.arange(wl.slots), u.last_used))
             assert np.array_equal(st["lru_order"], order), tag
             assert st["step"] == u.t, tag
-            row = wl.topk * 1152
-            cbuf = _u16(self.pool.cbuf[b * row:(b + 1) * row]).reshape(wl.topk, 576)
-            assert np.array_equal(cbuf, rec.cbuf), tag + " cbuf bytes"
+            tkb = np.asarray(tk[b], dtype=np.int64)
+            want_rs = np.where(tkb >= 0, u.tok2slot[np.maximum(tkb, 0)], -1)
+            assert np.array_equal(st["row_slot"], want_rs), tag + " row_slot"
+            if not self.direct:   # direct mode assembles no compute buffer
+                row = wl.topk * 1152
+                cbuf = _u16(self.pool.cbuf[b * row:(b + 1) * row]).reshape(wl.topk, 576)
+                assert np.array_equal(cbuf, rec.cbuf), tag + " cbuf bytes"
             hrow = wl.slots * 1152
             hu = b * wl.layers + l
             hot = _u16(self.pool.hot[hu * hrow:(hu + 1) * hrow]).reshape(wl.slots, 576)
@@ -204,6 +209,32 @@ def test_padded_topk_explicit_splits():
     _case(wl, wl.steps, range(wl.batch), padded=True, attn_splits=4)
 
 
+# ---------------------------------------------------------------- rows read in place
+
+def _direct():
+    import token_level_gather_amd as kvs
+    return kvs.KVS_FLAG_DIRECT_HOT
+
+
+@pytest.mark.parametrize("shape", [
+    dict(batch=3, layers=1, context=5000, slots=700, topk=300, fresh_rate=0.3),
+    dict(batch=2, layers=3, context=3000, slots=1100, topk=1025, fresh_rate=0.2),
+    dict(batch=2, layers=1, context=2000, slots=40, topk=1, fresh_rate=1.0),
+    dict(batch=5, layers=2, context=20000, slots=16384, topk=8192, fresh_rate=0.4),
+])
+def test_direct_hot_every_unit(shape):
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="direct", steps=6, **shape)
+    _case(wl, wl.steps, range(wl.batch), flags=_direct())
+
+
+@pytest.mark.parametrize("splits", [1, 5])
+def test_direct_hot_padded(splits):
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="direct_padded", batch=8, layers=2,
+                                                  context=5000, slots=1100, topk=300, steps=5,
+                                                  fresh_rate=0.3)
+    _case(wl, wl.steps, range(wl.batch), padded=True, flags=_direct(), attn_splits=splits)
+
+
 def test_zipf_stream_small():
     wl = W.WORKLOADS["ctx128k_b32_l8_zipf"].shrunk(batch=3, layers=2, context=20000, steps=6)
     _case(wl, wl.steps, range(wl.batch))
@@ -280,6 +311,11 @@ def test_invalid_topk_leaves_request_untouched(kind):
 def test_full_size_16k_sampled(name, reqs):
     wl = W.WORKLOADS[name]
     _case(wl, wl.steps, reqs, fill="checked")
+
+
+def test_full_size_16k_direct_hot_sampled():
+    wl = W.WORKLOADS["ctx16k_b64_k2048"]
+    _case(wl, wl.steps, [1, 40, 62], fill="checked", flags=_direct())
 
 
 @pytest.mark.parametrize("name,reqs,steps", [

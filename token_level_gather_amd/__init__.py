@@ -29,6 +29,7 @@ ROW_BYTES = HEAD_DIM * 2
 KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine")
 KVS_FLAG_HITS_FIRST = 1
 KVS_FLAG_PADDED_TOPK = 2
+KVS_FLAG_DIRECT_HOT = 4
 
 # Every exported symbol of include/kvs.h.
 EXPORTS = (
@@ -83,7 +84,7 @@ class kvs_unit_state(ctypes.Structure):
     _fields_ = [
         ("tok2slot", _I32P), ("slot2tok", _I32P), ("last_used", _I32P), ("lru_order", _I32P),
         ("slot_of", _I32P), ("miss_pos", _I32P), ("victims", _I32P), ("evicted", _I32P),
-        ("counts", _I32P), ("step", ctypes.c_int32),
+        ("counts", _I32P), ("row_slot", _I32P), ("step", ctypes.c_int32),
     ]
 
 
@@ -281,7 +282,7 @@ class Pool:
             "last_used": np.empty(self.S, np.int32), "lru_order": np.empty(self.S, np.int32),
             "slot_of": np.empty(self.K, np.int32), "miss_pos": np.empty(self.K, np.int32),
             "victims": np.empty(self.K, np.int32), "evicted": np.empty(self.K, np.int32),
-            "counts": np.empty(4, np.int32),
+            "counts": np.empty(4, np.int32), "row_slot": np.empty(self.K, np.int32),
         }
         st = kvs_unit_state(*[a.ctypes.data_as(_I32P) for a in arr.values()], 0)
         _check(lib().kvs_debug_read_state(self.handle, req, layer, _stream_ptr(stream),

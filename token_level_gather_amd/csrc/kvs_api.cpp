@@ -33,7 +33,8 @@ int make_layout(const kvs_config* c, Layout* lay) {
   if (c->attn_splits < 0 || c->attn_splits > 64) return KVS_EINVAL;
   if (c->fetch_blocks < 0 || c->fetch_blocks > 65535) return KVS_EINVAL;
   if (c->hit_blocks < 0 || c->hit_blocks > 65535) return KVS_EINVAL;
-  if ((c->flags & ~(KVS_FLAG_HITS_FIRST | KVS_FLAG_PADDED_TOPK)) != 0) return KVS_EINVAL;
+  if ((c->flags & ~(KVS_FLAG_HITS_FIRST | KVS_FLAG_PADDED_TOPK | KVS_FLAG_DIRECT_HOT)) != 0)
+    return KVS_EINVAL;
   if ((int64_t)c->batch * c->layers > 0x7fffffffLL) return KVS_EINVAL;
 
   const uint64_t B = c->batch, L = c->layers, N = c->context, S = c->slots, K = c->topk;
@@ -94,6 +95,7 @@ int make_layout(const kvs_config* c, Layout* lay) {
   lay->victims = take(B * K * 4);
   lay->evicted = take(B * K * 4);
   lay->counts = take(B * 16);
+  lay->row_slot = take(B * K * 4);
   lay->part_o = take(B * (uint64_t)splits * kHeads * kVDim * 4);
   lay->part_ml = take(B * (uint64_t)splits * kHeads * 2 * 4);
   lay->scratch_bytes = o;
@@ -163,7 +165,7 @@ int kvs_query_sizes(const kvs_config* cfg, kvs_sizes* out) {
   out->host_pool_bytes = B * L * N * kRowBytes;
   out->hot_bytes = B * L * S * kRowBytes;
   out->meta_bytes = lay.meta_bytes;
-  out->cbuf_bytes = B * K * kRowBytes;
+  out->cbuf_bytes = (cfg->flags & KVS_FLAG_DIRECT_HOT) ? 0 : B * K * kRowBytes;
   out->scratch_bytes = lay.scratch_bytes;
   out->attn_splits = lay.splits;
   out->fetch_blocks = lay.fetch_blocks;
@@ -200,7 +202,7 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
   int rc = kvs_query_sizes(cfg, &need);
   if (rc != KVS_OK) return rc;
   if (bufs->host_pool == nullptr || bufs->hot == nullptr || bufs->meta == nullptr ||
-      bufs->cbuf == nullptr || bufs->scratch == nullptr)
+      (bufs->cbuf == nullptr && need.cbuf_bytes != 0) || bufs->scratch == nullptr)
     return KVS_EINVAL;
   if (bufs->host_pool_bytes < need.host_pool_bytes || bufs->hot_bytes < need.hot_bytes ||
       bufs->meta_bytes < need.meta_bytes || bufs->cbuf_bytes < need.cbuf_bytes ||
@@ -249,6 +251,7 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
   d.victims = (int32_t*)(scr + L.victims);
   d.evicted = (int32_t*)(scr + L.evicted);
   d.counts = (int32_t*)(scr + L.counts);
+  d.row_slot = (int32_t*)(scr + L.row_slot);
   d.part_o = (float*)(scr + L.part_o);
   d.part_ml = (float*)(scr + L.part_ml);
 
@@ -306,7 +309,7 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
   KVS_TRY_HIP(timed(p, KVS_KERNEL_GATHER, s, [&] { return launch_gather(L, d, layer, topk, s); }));
   // Top-K sparse attention over the compute buffer
   KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s, [&] {
-    return launch_attention(L, d, (const uint16_t*)q, p->cfg.scale, s);
+    return launch_attention(L, d, layer, (const uint16_t*)q, p->cfg.scale, s);
   }));
   KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
                     [&] { return launch_combine(L, d, (uint16_t*)out, lse, s); }));
@@ -370,6 +373,7 @@ int kvs_debug_read_state(kvs_pool* p, int32_t req, int32_t layer, void* stream,
   KVS_TRY_HIP(get(st->victims, d.victims + (long long)req * L.K, (size_t)L.K * 4));
   KVS_TRY_HIP(get(st->evicted, d.evicted + (long long)req * L.K, (size_t)L.K * 4));
   KVS_TRY_HIP(get(st->counts, d.counts + 4LL * req, 16));
+  KVS_TRY_HIP(get(st->row_slot, d.row_slot + (long long)req * L.K, (size_t)L.K * 4));
   std::vector<uint16_t> order(st->lru_order ? L.S : 0);
   KVS_TRY_HIP(get(st->lru_order ? order.data() : nullptr, d.order + u * L.S, (size_t)L.S * 2));
   int32_t step = 0;

@@ -37,6 +37,7 @@ struct Layout {
   uint64_t victims;    // int32 [B][K]
   uint64_t evicted;    // int32 [B][K]
   uint64_t counts;     // int32 [B][4]: n_hit, n_miss, n_evict, valid
+  uint64_t row_slot;   // int32 [B][K]: slot of position i's row after the step, -1 empty
   uint64_t part_o;     // float [B][splits][16][512]
   uint64_t part_ml;    // float [B][splits][16][2]: running max (log2 units), sum
   uint64_t scratch_bytes;
@@ -65,6 +66,7 @@ struct DevPtrs {
   int32_t* victims;
   int32_t* evicted;
   int32_t* counts;
+  int32_t* row_slot;
   float* part_o;
   float* part_ml;
 };
@@ -78,7 +80,7 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer,
                            const int32_t* topk, hipStream_t s);
 hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
                          hipStream_t s);
-hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t* q,
+hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* q,
                             float scale, hipStream_t s);
 hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
                           hipStream_t s);

@@ -89,6 +89,7 @@ struct DiffArgs {
   int32_t* victims;        // [B][K]
   int32_t* evicted;        // [B][K]
   int32_t* counts;         // [B][4]
+  int32_t* row_slot;       // [B][K]: slot of position i's row after the step, -1 empty
   long long N;
   int S, K, L, layer, hash_bits;
   int padded;              // 1: a Top-K entry of -1 is empty
@@ -243,6 +244,8 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     const int i = i0 + j;
     if (j < kpt && i < K) {
       a.slot_of[bk + i] = my_slot[j];
+      // a miss's row slot is its victim, written once in step 5
+      if (my_slot[j] != -1) a.row_slot[bk + i] = my_slot[j] >= 0 ? my_slot[j] : -1;
       if (my_slot[j] >= 0) lu[my_slot[j]] = t;
       else cnt += my_slot[j] == -1 ? 1 : (1 << 16);
     }
@@ -331,6 +334,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     lu[v] = t;
     a.miss_pos[bk + j] = i;
     a.victims[bk + j] = v;
+    a.row_slot[bk + i] = v;
   }
 }
 
@@ -355,6 +359,7 @@ struct GatherArgs {
   int fetch_wgs;           // fetch_per_req * B
   int hit_wgs;             // hit-role workgroups (each loops over 32-position groups)
   int hits_first;          // 0: fetch workgroups take the first grid indices; 1: hit ones do
+  int write_cbuf;          // 0: rows are read in place from the hot buffer (no compute buffer)
 };
 
 // The index copy of one layer.  Workgroups [0, fetch_wgs) fetch misses: row =
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
         if (pos[j] >= 0) {
           const int c = j * kCopyThreads + threadIdx.x;
           const int col = c - (c / kRowChunks) * kRowChunks;
-          a.cbuf[(bk + pos[j]) * kRowChunks + col] = v[j];
+          if (a.write_cbuf) a.cbuf[(bk + pos[j]) * kRowChunks + col] = v[j];
           a.hot[(u * a.S + vic[j]) * kRowChunks + col] = v[j];
         }
       }
@@ -472,15 +477,18 @@ __device__ __forceinline__ int lds_swz(int r) {
 }
 
 struct AttnArgs {
-  const uint16_t* cbuf;   // [B][K][576]
-  const uint16_t* q;      // [B][16][576]
-  const int32_t* slot_of; // [B][K]: -2 marks an empty entry of a padded Top-K
-  const int32_t* counts;  // [B][4]
-  float* part_o;          // [B][splits][16][512]
-  float* part_ml;         // [B][splits][16][2]
-  int K, splits;
-  int padded;             // 1: mask the entries whose slot_of is -2
-  float scale_log2;       // softmax scale * log2(e): scores are kept in log2 units
+  const uint16_t* cbuf;     // [B][K][576]: assembled rows (direct == 0)
+  const uint16_t* hot;      // [B*L][S][576]: hot buffer, rows read in place (direct == 1)
+  const uint16_t* q;        // [B][16][576]
+  const int32_t* slot_of;   // [B][K]: -2 marks an empty entry of a padded Top-K
+  const int32_t* row_slot;  // [B][K]: slot of position i's row, -1 empty
+  const int32_t* counts;    // [B][4]
+  float* part_o;            // [B][splits][16][512]
+  float* part_ml;           // [B][splits][16][2]
+  int K, splits, S, L, layer;
+  int padded;               // 1: mask the empty entries of a padded Top-K
+  int direct;               // 1: read rows from the hot buffer at row_slot
+  float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units
 };
 
 // One workgroup = (split sp, request b): the tiles [tb, te) of request b's
@@ -511,7 +519,6 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   const int ntiles = (K + kTile - 1) / kTile;
   const int tb = (int)((long long)sp * ntiles / a.splits);
   const int te = (int)((long long)(sp + 1) * ntiles / a.splits);
-  const u32x4* rows = reinterpret_cast<const u32x4*>(a.cbuf + (long long)b * K * kRowElems);
 
   bf16x8 qf[kKHalf];
   float m_run = -INFINITY, l_run = 0.f;   // per head, replicated over its 32 softmax threads
@@ -532,16 +539,35 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   // own loads (a branch per load would make the count path-dependent and the
   // compiler would then drain everything before each use).
   const int lrow = tid >> 3, lsub = tid & 7;
-  const int rec_bytes = K * kRowBytes;
+  // Rows: request b's K assembled rows in position order, or (direct) the
+  // rows of unit (b, layer)'s hot buffer, indexed by row_slot.
+  const uint16_t* base = a.direct ? a.hot + ((long long)b * a.L + a.layer) * a.S * kRowElems
+                                  : a.cbuf + (long long)b * K * kRowElems;
+  const int rec_bytes = (a.direct ? a.S : K) * kRowBytes;
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, rec_bytes, kBufRsrcWord3);
-  // The slot_of entries of the softmax tokens travel with their tile.  Without
-  // padding the resource is empty: the loads return 0 (valid) and read nothing.
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rec_bytes, kBufRsrcWord3);
+  // row_slot of this thread's tile row, loaded one tile ahead of the rows
+  // (direct only; otherwise the resource is empty and the loads read nothing)
+  const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.row_slot + (long long)b * K), (short)0, a.direct ? K * 4 : 0, kBufRsrcWord3);
+  // The entries of the softmax tokens that mark an empty position (slot_of -2,
+  // or row_slot -1 when direct) travel with their tile.  Without padding the
+  // resource is empty: the loads return 0 (valid) and read nothing.
   const __amdgpu_buffer_rsrc_t vsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.slot_of + (long long)b * K), (short)0, a.padded ? K * 4 : 0, kBufRsrcWord3);
+      (void*)((a.direct ? a.row_slot : a.slot_of) + (long long)b * K), (short)0,
+      a.padded ? K * 4 : 0, kBufRsrcWord3);
+  const int pad_mark = a.direct ? -1 : -2;
   const int c2 = (tid & 31) * 2;   // softmax tokens c2, c2 + 1 of a tile
-  auto load_tile = [&](u32x4 (&dst)[kAttnItems], int (&dv)[2], int tile) {
-    const int off = tile < te ? (tile * kTile + lrow) * kRowBytes + lsub * 16 : rec_bytes;
+  auto load_slot = [&](int tile) -> int {
+    return __builtin_amdgcn_raw_buffer_load_b32(
+        ssrc, tile < te ? (tile * kTile + lrow) * 4 : K * 4, 0, 0);
+  };
+  auto load_tile = [&](u32x4 (&dst)[kAttnItems], int (&dv)[2], int tile, int slot) {
+    const int tok = tile * kTile + lrow;
+    const bool in = tile < te && tok < K;
+    const int off = !in       ? rec_bytes
+                    : a.direct ? (slot >= 0 ? slot * kRowBytes + lsub * 16 : rec_bytes)
+                               : tok * kRowBytes + lsub * 16;
 #pragma unroll
     for (int j = 0; j < kAttnItems; ++j)
       dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + j * 128, 0, 0);
@@ -586,9 +612,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
       const float* s0 = sc + h * kTile + c2;
       const float* s1 = sc + kHeads * kTile + h * kTile + c2;
       const float x0 =
-          tok0 < K && cv[0] != -2 ? (s0[0] + s1[0]) * a.scale_log2 : -INFINITY;
+          tok0 < K && cv[0] != pad_mark ? (s0[0] + s1[0]) * a.scale_log2 : -INFINITY;
       const float x1 =
-          tok0 + 1 < K && cv[1] != -2 ? (s0[1] + s1[1]) * a.scale_log2 : -INFINITY;
+          tok0 + 1 < K && cv[1] != pad_mark ? (s0[1] + s1[1]) * a.scale_log2 : -INFINITY;
       float mx = fmaxf(x0, x1);
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -648,8 +674,12 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
         reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
 #pragma unroll
     for (int ks = 0; ks < kKHalf; ++ks) qf[ks] = as_bf16x8(qh[(kh * kKHalf + ks) * 4 + g]);
-    load_tile(ra, va, tb);
-    load_tile(rb, vb, tb + 1);
+    // every slot load is issued before the rows of the tile ahead of it, in
+    // the prologue as in the loop, so the wait for a slot never covers rows
+    int sa = load_slot(tb), sb = load_slot(tb + 1);
+    load_tile(ra, va, tb, sa);
+    sa = load_slot(tb + 2);
+    load_tile(rb, vb, tb + 1, sb);
     store_tile(ra);
     cv[0] = va[0];
     cv[1] = va[1];
@@ -659,13 +689,15 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     // tile past te: the range check makes them zeros that nothing reads.
     int tile = tb;
     for (; tile + 1 < te; tile += 2) {
-      load_tile(ra, va, tile + 2);
+      sb = load_slot(tile + 3);
+      load_tile(ra, va, tile + 2, sa);
       compute(tile);
       store_tile(rb);
       cv[0] = vb[0];
       cv[1] = vb[1];
       __syncthreads();
-      load_tile(rb, vb, tile + 3);
+      sa = load_slot(tile + 4);
+      load_tile(rb, vb, tile + 3, sb);
       compute(tile + 1);
       store_tile(ra);
       cv[0] = va[0];
@@ -865,6 +897,7 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const
   a.victims = d.victims;
   a.evicted = d.evicted;
   a.counts = d.counts;
+  a.row_slot = d.row_slot;
   a.N = lay.N;
   a.S = lay.S;
   a.K = lay.K;
@@ -902,23 +935,31 @@ hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const i
   const long long all_groups = (long long)groups_per_req * lay.B;
   a.hit_wgs = (int)(lay.hit_blocks > 0 && lay.hit_blocks < all_groups ? lay.hit_blocks : all_groups);
   a.hits_first = (lay.flags & KVS_FLAG_HITS_FIRST) != 0;
+  a.write_cbuf = (lay.flags & KVS_FLAG_DIRECT_HOT) == 0;
+  if (!a.write_cbuf) a.hit_wgs = 0;   // hits stay where they are
   const long long grid = (long long)a.fetch_wgs + (long long)a.hit_wgs;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const Layout& lay, const DevPtrs& d, const uint16_t* q, float scale,
-                            hipStream_t s) {
+hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* q,
+                            float scale, hipStream_t s) {
   AttnArgs a;
   a.cbuf = d.cbuf;
+  a.hot = d.hot;
   a.q = q;
   a.slot_of = d.slot_of;
+  a.row_slot = d.row_slot;
   a.counts = d.counts;
   a.part_o = d.part_o;
   a.part_ml = d.part_ml;
   a.K = lay.K;
   a.splits = lay.splits;
+  a.S = lay.S;
+  a.L = lay.L;
+  a.layer = layer;
   a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
+  a.direct = (lay.flags & KVS_FLAG_DIRECT_HOT) != 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(attention_kernel, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
