@@ -15,19 +15,25 @@ from oracle import OracleUnit
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replay_equals_eager_and_oracle():
+@pytest.mark.parametrize("mode", ["default", "padded", "direct", "padded_direct"])
+def test_graph_replay_equals_eager_and_oracle(mode):
     import torch
 
     import token_level_gather_amd as kvs
-    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="graph", batch=3, layers=2, context=5000,
+    padded = "padded" in mode
+    flags = (kvs.KVS_FLAG_PADDED_TOPK if padded else 0) | \
+        (kvs.KVS_FLAG_DIRECT_HOT if "direct" in mode else 0)
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="graph", batch=4, layers=2, context=5000,
                                                   slots=700, topk=300, steps=8, fresh_rate=0.3)
     B, L = wl.batch, wl.layers
     host = kvs.HostPool(B, L, wl.context)
     W.fill_pool(host.array, wl)
-    pg = kvs.Pool(B, L, wl.context, wl.slots, wl.topk, scale=wl.scale, host=host)
-    pe = kvs.Pool(B, L, wl.context, wl.slots, wl.topk, scale=wl.scale, host=host)
+    pg = kvs.Pool(B, L, wl.context, wl.slots, wl.topk, scale=wl.scale, host=host, flags=flags)
+    pe = kvs.Pool(B, L, wl.context, wl.slots, wl.topk, scale=wl.scale, host=host, flags=flags)
     try:
         topk = W.topk_streams(wl)
+        if padded:
+            topk = W.pad_topk_streams(topk, wl.seed)
         tk_s = [torch.empty((B, wl.topk), dtype=torch.int32, device="cuda") for _ in range(L)]
         q_s = [torch.empty((B, 16, 576), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
         out_g = [torch.empty((B, 16, 512), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
@@ -51,18 +57,24 @@ def test_graph_replay_equals_eager_and_oracle():
                 torch.cuda.synchronize()
                 assert torch.equal(out_g[l].view(torch.int16), out_e.view(torch.int16)), (t, l)
                 assert torch.equal(lse_g[l], lse_e), (t, l)
-                assert torch.equal(pg.cbuf, pe.cbuf), (t, l)
+                if not flags & kvs.KVS_FLAG_DIRECT_HOT:   # direct mode has no compute buffer
+                    assert torch.equal(pg.cbuf, pe.cbuf), (t, l)
                 for b in range(B):
-                    rec = oracle[(b, l)].step(topk[t, l, b], host.array[b, l], q[b], wl.scale)
+                    rec = oracle[(b, l)].step(topk[t, l, b], host.array[b, l], q[b], wl.scale,
+                                              padded=padded)
                     sg = pg.read_state(b, l)
                     se = pe.read_state(b, l)
-                    for key in ("tok2slot", "slot2tok", "last_used", "lru_order", "slot_of"):
+                    for key in ("tok2slot", "slot2tok", "last_used", "lru_order", "slot_of",
+                                "row_slot"):
                         assert np.array_equal(sg[key], se[key]), (t, l, b, key)
                     assert np.array_equal(sg["tok2slot"], oracle[(b, l)].tok2slot)
                     assert np.array_equal(sg["victims"][:rec.n_miss], rec.victims)
                     assert sg["step"] == t + 1
                     got = (out_g[l][b].view(torch.int16).cpu().numpy().view(np.uint16)
                            .astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                    if rec.n_hit + rec.n_miss == 0:   # all entries empty
+                        assert not got.any() and torch.all(lse_g[l][b] == -np.inf)
+                        continue
                     err = got - rec.out
                     assert np.abs(err).max() <= 2e-2
                     assert np.linalg.norm(err) / np.linalg.norm(rec.out) <= 1e-2

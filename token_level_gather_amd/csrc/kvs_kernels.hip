@@ -28,6 +28,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;         // LDS-qualified
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -643,21 +645,29 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[nt][j] *= al[j];
+      // B operand by transpose reads (ds_read_b64_tr_b16): within each
+      // 16-lane block, lane c receives element c % 4 of the 8-byte row piece
+      // addressed by lane 4j + c / 4, for j = 0..3.  Lane a = r16 of block g
+      // therefore addresses V[row0 + a / 4][n0 + 4 (a % 4) .. +3], and lane
+      // (g, r16) receives V[row0 + j][n0 + r16], j = 0..3: four consecutive
+      // k-values of column n0 + r16.  Two reads (rows +0 and +4) give the 8
+      // k-values 8g .. 8g + 7 of the MFMA's B operand.
+      const int tr_row = g * 8 + (r16 >> 2);
+      const int tr_sub = (r16 & 1) * 8;            // byte offset inside the 16-byte chunk
 #pragma unroll
       for (int kk = 0; kk < kTile / 32; ++kk) {
         const bf16x8 pf =
             as_bf16x8(*reinterpret_cast<const u32x4*>(pb + r16 * kPRow + kk * 32 + g * 8));
-        const int vrow0 = kk * 32 + g * 8;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const int e = wave * 64 + nt * 16 + r16;
-          u16x8 vv;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int vr = vrow0 + jj;
-            vv[jj] = *reinterpret_cast<const uint16_t*>(
-                kv + vr * kLdsRow + (((e >> 3) ^ lds_swz(vr)) * 16) + (e & 7) * 2);
-          }
+          const int chunk = wave * 8 + nt * 2 + ((r16 & 3) >> 1);   // column (n0 + 4(a%4)) / 8
+          const int r0 = kk * 32 + tr_row, r1 = r0 + 4;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(kv + r0 * kLdsRow + ((chunk ^ lds_swz(r0)) * 16) + tr_sub));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(kv + r1 * kLdsRow + ((chunk ^ lds_swz(r1)) * 16) + tr_sub));
+          const u16x8 vv = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                            (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
           acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               pf, __builtin_bit_cast(bf16x8, vv), acc[nt], 0, 0, 0);
         }
