@@ -259,13 +259,16 @@ def test_free_request_then_cold_refill():
         h.close()
 
 
+@pytest.mark.parametrize("padded", [False, True])
 @pytest.mark.parametrize("kind", ["range", "negative", "duplicate"])
-def test_invalid_topk_leaves_request_untouched(kind):
+def test_invalid_topk_leaves_request_untouched(kind, padded):
+    # with padding only -1 is empty: -5 stays out of range, and a token repeated
+    # beside empty entries is still a duplicate
     import token_level_gather_amd as kvs
     torch = _torch()
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(batch=3, context=3000, slots=500, topk=200,
                                                   steps=6)
-    h = Harness(wl, wl.steps, range(3))
+    h = Harness(wl, wl.steps, range(3), padded=padded)
     try:
         for t in range(2):
             h.check(t, 0, *h.device_step(t, 0))
@@ -276,9 +279,10 @@ def test_invalid_topk_leaves_request_untouched(kind):
         elif kind == "negative":
             bad[1, 0] = -5
         else:
-            bad[1, 9] = bad[1, 3]
+            src = int(np.flatnonzero(bad[1] >= 0)[0])
+            bad[1, (src + 9) % wl.topk] = bad[1, src]
         with pytest.raises(OracleError):
-            h.oracle[(1, 0)].step(bad[1], h.pool.host.array[1, 0])
+            h.oracle[(1, 0)].step(bad[1], h.pool.host.array[1, 0], padded=padded)
         h.device_step(2, 0, topk=bad)
         rc, _ = h.pool.sync_status()
         assert rc == (kvs.KVS_EDUP if kind == "duplicate" else kvs.KVS_ERANGE)
@@ -290,7 +294,7 @@ def test_invalid_topk_leaves_request_untouched(kind):
         assert torch.isinf(h.lse[1]).all().item()
         # the other requests took the step normally
         for b in (0, 2):
-            rec = h.oracle[(b, 0)].step(bad[b], h.pool.host.array[b, 0])
+            rec = h.oracle[(b, 0)].step(bad[b], h.pool.host.array[b, 0], padded=padded)
             assert np.array_equal(h.pool.read_state(b, 0)["slot2tok"], h.oracle[(b, 0)].slot2tok)
             assert rec.t == 2
         # the status was cleared and the request continues from its old state

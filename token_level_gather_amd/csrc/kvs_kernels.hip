@@ -150,6 +150,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   // LDS: per-slot flag [S] u8 (1 = hit, 2 = victim) | token hash set [H] i32,
   //      reused after validation as miss list [K] + victims [K]
   uint8_t* flag = smem;
+  unsigned* flagw = reinterpret_cast<unsigned*>(smem);   // the same flags, 4 per word
   int32_t* hash = reinterpret_cast<int32_t*>(smem + ((S + 15) & ~15));
   int32_t* lmiss = hash;
   int32_t* lvict = hash + K;
@@ -198,8 +199,10 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   }
   __syncthreads();
 
-  // 1b. validation (range, duplicates via an LDS open-addressing set); hit flags.
-  //     my_slot: >= 0 hit slot, -1 miss, -2 empty entry of a padded Top-K
+  // 1b. validation and hit flags.  my_slot: >= 0 hit slot, -1 miss, -2 empty
+  //     entry of a padded Top-K.  A token given twice is resident in one slot
+  //     (the second flag set of that slot reveals it) or in none (misses go
+  //     through an LDS open-addressing set of tokens).
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
@@ -210,18 +213,22 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
       } else if (tok < 0 || (long long)tok >= a.N) {
         atomicOr(&err_bits, 1);
       } else {
-        unsigned h = ((unsigned)tok * 2654435761u) >> (32 - a.hash_bits);
-        while (true) {
-          const int prev = atomicCAS(&hash[h], -1, tok);
-          if (prev == -1) break;
-          if (prev == tok) {
-            atomicOr(&err_bits, 2);
-            break;
-          }
-          h = (h + 1) & (unsigned)(H - 1);
-        }
         if (my_slot[j] >= S) my_slot[j] = -1;
-        if (my_slot[j] >= 0) flag[my_slot[j]] = 1;
+        if (my_slot[j] >= 0) {
+          const unsigned bit = 1u << ((my_slot[j] & 3) * 8);   // flag byte := 1
+          if (atomicOr(&flagw[my_slot[j] >> 2], bit) & bit) atomicOr(&err_bits, 2);
+        } else {
+          unsigned h = ((unsigned)tok * 2654435761u) >> (32 - a.hash_bits);
+          while (true) {
+            const int prev = atomicCAS(&hash[h], -1, tok);
+            if (prev == -1) break;
+            if (prev == tok) {
+              atomicOr(&err_bits, 2);
+              break;
+            }
+            h = (h + 1) & (unsigned)(H - 1);
+          }
+        }
       }
     }
   }
@@ -237,9 +244,11 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     return;
   }
 
-  // 2. sparse diff: record slot_of, touch hits, compact misses in Top-K order.
-  //    One scan counts misses (low 16 bits) and empty entries (high bits):
-  //    K <= 8192, so the low field never carries into the high one.
+  // 2 + 3. The two order-preserving compactions share one scan: misses in
+  //    Top-K order (low 16 bits, m <= K <= 8192) and non-hit slots in LRU
+  //    order (high 16 bits, at most S <= 16384).  The hit slots are distinct
+  //    (a repeat was rejected above), so n_hit = S - non-hit slots.
+  // 2. sparse diff: record slot_of, touch hits, compact misses in Top-K order
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -249,13 +258,19 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
       // a miss's row slot is its victim, written once in step 5
       if (my_slot[j] != -1) a.row_slot[bk + i] = my_slot[j] >= 0 ? my_slot[j] : -1;
       if (my_slot[j] >= 0) lu[my_slot[j]] = t;
-      else cnt += my_slot[j] == -1 ? 1 : (1 << 16);
+      else if (my_slot[j] == -1) ++cnt;
     }
   }
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int p = p0 + q;
+    if (q < spt && p < S && flag[my_ord[q]] == 0) cnt += 1 << 16;
+  }
   int packed;
-  int r = wg_exclusive_scan(cnt, wtot, packed) & 0xffff;
+  const int ex = wg_exclusive_scan(cnt, wtot, packed);
   const int m = packed & 0xffff;
-  const int n_hit = K - m - (packed >> 16);
+  const int n_hit = S - (packed >> 16);
+  int r = ex & 0xffff;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
@@ -263,15 +278,10 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   }
 
   // 3. victims: the first m non-hit slots of the LRU order, evicted here; the
-  //    other non-hit slots keep their relative order at the front of the new order
-  cnt = 0;
-#pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    const int p = p0 + q;
-    if (q < spt && p < S && flag[my_ord[q]] == 0) ++cnt;
-  }
-  int n_nonhit;
-  r = wg_exclusive_scan(cnt, wtot, n_nonhit);
+  //    other non-hit slots keep their relative order at the front of the new
+  //    order.  Each slot sits at one order position, so each flag byte below
+  //    is read and written by one thread only.
+  r = ex >> 16;
   int my_evict = 0;
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
