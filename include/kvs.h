@@ -45,6 +45,9 @@
  *  - A `stream` argument is a hipStream_t passed as void* (NULL = the default
  *    stream).  Calls only enqueue work on it, except where stated.
  *  - A pool is not thread-safe: calls on one pool must not overlap.
+ *  - A pool's buffers live on the device current at kvs_create_pool; calls
+ *    that enqueue work take a stream of that device (NULL = that device's
+ *    default stream while it is current) and return KVS_EINVAL otherwise.
  */
 #ifndef KVS_H_
 #define KVS_H_

@@ -136,6 +136,23 @@ static void destroy_pool(kvs_pool* p) {
   delete p;
 }
 
+// The pool's buffers live on the device that was current at kvs_create_pool:
+// work enqueued on a stream of another device would address them there.
+static int check_device(const kvs_pool* p, hipStream_t s) {
+  hipDevice_t dev = -1;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return KVS_EINVAL;
+  }
+  return dev == p->device ? KVS_OK : KVS_EINVAL;
+}
+
+#define KVS_TRY(expr)            \
+  do {                           \
+    const int rc_ = (expr);      \
+    if (rc_ != KVS_OK) return rc_; \
+  } while (0)
+
 // Launch `fn` on `s`, bracketed by timing events when profiling.
 template <typename F>
 static hipError_t timed(kvs_pool* p, int kernel, hipStream_t s, F fn) {
@@ -282,6 +299,7 @@ int kvs_publish_device(kvs_pool* p, int32_t req, int32_t layer, int64_t first_to
   if (p == nullptr || rows == nullptr) return KVS_EINVAL;
   if (req < 0 || req >= p->lay.B || layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
   if (first_tok < 0 || n_tok < 0 || first_tok + n_tok > p->lay.N) return KVS_EINVAL;
+  KVS_TRY(check_device(p, (hipStream_t)stream));
   if (n_tok == 0) return KVS_OK;
   const uint64_t row0 = ((uint64_t)req * p->lay.L + layer) * (uint64_t)p->lay.N + first_tok;
   return hip_err(hipMemcpyAsync(p->host_pool + row0 * kRowBytes, rows, (size_t)n_tok * kRowBytes,
@@ -292,6 +310,7 @@ int kvs_append(kvs_pool* p, int32_t layer, const void* rows, const int64_t* pos,
   if (p == nullptr || rows == nullptr || pos == nullptr) return KVS_EINVAL;
   if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
   if (((uintptr_t)rows & 15) != 0 || ((uintptr_t)pos & 7) != 0) return KVS_EINVAL;
+  KVS_TRY(check_device(p, (hipStream_t)stream));
   return hip_err(launch_append(p->lay, p->d, layer, (const uint16_t*)rows, pos,
                                (hipStream_t)stream));
 }
@@ -301,6 +320,7 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
   if (p == nullptr || topk == nullptr || q == nullptr || out == nullptr) return KVS_EINVAL;
   if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
   const hipStream_t s = (hipStream_t)stream;
+  KVS_TRY(check_device(p, s));
   const Layout& L = p->lay;
   const DevPtrs& d = p->d;
   // lookup, sparse diff, LRU and map update for every request of the layer
@@ -319,6 +339,7 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
 
 int kvs_free_request(kvs_pool* p, int32_t req, void* stream) {
   if (p == nullptr || req < 0 || req >= p->lay.B) return KVS_EINVAL;
+  KVS_TRY(check_device(p, (hipStream_t)stream));
   return hip_err(launch_init_units(p->lay, p->d, req * p->lay.L, p->lay.L, false,
                                    (hipStream_t)stream));
 }
@@ -424,6 +445,7 @@ int kvs_profile_end(kvs_pool* p, kvs_kernel_times* out) {
 
 struct kvs_graph {
   hipGraphExec_t exec;
+  int device;   // the pool's device: replays must go to a stream of it
 };
 
 int kvs_graph_capture(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, void* out,
@@ -462,12 +484,18 @@ int kvs_graph_capture(kvs_pool* p, int32_t layer, const int32_t* topk, const voi
     return KVS_ENOMEM;
   }
   kg->exec = exec;
+  kg->device = p->device;
   *out_graph = kg;
   return KVS_OK;
 }
 
 int kvs_graph_launch(kvs_graph* g, void* stream) {
   if (g == nullptr) return KVS_EINVAL;
+  hipDevice_t dev = -1;
+  if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess || dev != g->device) {
+    (void)hipGetLastError();
+    return KVS_EINVAL;
+  }
   return hip_err(hipGraphLaunch(g->exec, (hipStream_t)stream));
 }
 
@@ -489,7 +517,7 @@ const char* kvs_strerror(int code) {
     case KVS_OK: return "ok";
     case KVS_EINVAL: return "invalid argument or configuration";
     case KVS_ENOMEM: return "buffer smaller than kvs_query_sizes requires";
-    case KVS_ERANGE: return "Top-K index outside [0, context)";
+    case KVS_ERANGE: return "Top-K index or append position outside [0, context)";
     case KVS_EDUP: return "duplicate Top-K index within a request";
     default: break;
   }
