@@ -42,6 +42,29 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// A lane's value from another lane of its 16-lane DPP row (gfx9 DPP control).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                            0xf, 0xf, false));
+}
+// Max / sum over the 16 lanes of a DPP row.  Each step pairs lanes
+// symmetrically (lane ^ 1, lane ^ 2 inside a quad, then the mirror inside 8
+// and inside 16 lanes), so after each step the lanes of a group hold the same
+// value, and the sum is the same bit pattern in all 16 lanes.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<0xb1>(x));    // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_f32<0x4e>(x));    // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_f32<0x141>(x));   // row_half_mirror
+  return fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<0xb1>(x);
+  x += dpp_f32<0x4e>(x);
+  x += dpp_f32<0x141>(x);
+  return x + dpp_f32<0x140>(x);
+}
+
 // ------------------------------------------------------------------ init
 // Empties units [u0, u0 + count): maps -1, last_used -1, LRU order 0..S-1.
 __global__ void init_units_kernel(int32_t* tok2slot, int32_t* slot2tok, int32_t* last_used,
@@ -499,7 +522,6 @@ struct AttnArgs {
   float* part_ml;           // [B][splits][16][2]
   int K, splits, S, L, layer;
   int padded;               // 1: mask the empty entries of a padded Top-K
-  int direct;               // 1: read rows from the hot buffer at row_slot
   float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units
 };
 
@@ -515,11 +537,15 @@ struct AttnArgs {
 //           partial score tiles per token block, summed in the softmax);
 //   softmax 32 threads per head, 2 tokens each;
 //   P.V     wave w: value columns 64*w .. +64 (4 MFMA column tiles).
+// DIRECT: rows read in place from the hot buffer at row_slot (a separate
+// instantiation, so the assembled-buffer path carries no slot loads at all).
+template <bool DIRECT>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char kv[kTile * kLdsRow];
   __shared__ float sc[2 * kHeads * kTile];
   __shared__ __attribute__((aligned(16))) uint16_t pb[kHeads * kPRow];
   __shared__ float alpha_s[kHeads];
+  __shared__ __attribute__((aligned(16))) int vmark[kTile];   // the tile's empty-entry marks
 
   const int b = blockIdx.y, sp = blockIdx.x;
   // invalid input, or no entry at all (padded): combine writes the zero output
@@ -533,7 +559,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   const int te = (int)((long long)(sp + 1) * ntiles / a.splits);
 
   bf16x8 qf[kKHalf];
-  float m_run = -INFINITY, l_run = 0.f;   // per head, replicated over its 32 softmax threads
+  float m_run = -INFINITY, l_run = 0.f;   // per head, replicated over its 16 softmax threads
   f32x4 acc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -541,7 +567,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   // two register buffers: the rows of the next two tiles are in flight while a
   // tile is consumed from LDS
   u32x4 ra[kAttnItems], rb[kAttnItems];
-  int va[2], vb[2], cv[2];   // slot_of of this thread's two softmax tokens: next tiles, current
+  int va, vb;   // empty-entry mark of this thread's tile row, stored to LDS with the rows
   // 8 threads per row: thread (row tid / 8, sub tid % 8) moves chunks sub + 8j.
   // The rows are read through a buffer resource that spans this request's K
   // rows: the hardware range check returns zeros for rows >= K and for the
@@ -553,45 +579,49 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   const int lrow = tid >> 3, lsub = tid & 7;
   // Rows: request b's K assembled rows in position order, or (direct) the
   // rows of unit (b, layer)'s hot buffer, indexed by row_slot.
-  const uint16_t* base = a.direct ? a.hot + ((long long)b * a.L + a.layer) * a.S * kRowElems
+  const uint16_t* base = DIRECT ? a.hot + ((long long)b * a.L + a.layer) * a.S * kRowElems
                                   : a.cbuf + (long long)b * K * kRowElems;
-  const int rec_bytes = (a.direct ? a.S : K) * kRowBytes;
+  const int rec_bytes = (DIRECT ? a.S : K) * kRowBytes;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rec_bytes, kBufRsrcWord3);
   // row_slot of this thread's tile row, loaded one tile ahead of the rows
-  // (direct only; otherwise the resource is empty and the loads read nothing)
+  // (DIRECT instantiation only)
   const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.row_slot + (long long)b * K), (short)0, a.direct ? K * 4 : 0, kBufRsrcWord3);
-  // The entries of the softmax tokens that mark an empty position (slot_of -2,
-  // or row_slot -1 when direct) travel with their tile.  Without padding the
-  // resource is empty: the loads return 0 (valid) and read nothing.
+      (void*)(a.row_slot + (long long)b * K), (short)0, DIRECT ? K * 4 : 0, kBufRsrcWord3);
+  // The entry of each tile row that marks an empty position (slot_of -2, or
+  // row_slot -1 when DIRECT) travels with the row and is stored beside it.
+  // Without padding the resource is empty: the loads return 0 (valid) and
+  // read nothing.
   const __amdgpu_buffer_rsrc_t vsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((a.direct ? a.row_slot : a.slot_of) + (long long)b * K), (short)0,
+      (void*)((DIRECT ? a.row_slot : a.slot_of) + (long long)b * K), (short)0,
       a.padded ? K * 4 : 0, kBufRsrcWord3);
-  const int pad_mark = a.direct ? -1 : -2;
-  const int c2 = (tid & 31) * 2;   // softmax tokens c2, c2 + 1 of a tile
+  const int pad_mark = DIRECT ? -1 : -2;
+  // softmax: threads 0..255, 16 lanes per head (one DPP row), tokens c4 .. c4 + 3
+  const bool sm_on = tid < kHeads * 16;
+  const int c4 = (tid & 15) * 4;
   auto load_slot = [&](int tile) -> int {
+    if (!DIRECT) return 0;
     return __builtin_amdgcn_raw_buffer_load_b32(
         ssrc, tile < te ? (tile * kTile + lrow) * 4 : K * 4, 0, 0);
   };
-  auto load_tile = [&](u32x4 (&dst)[kAttnItems], int (&dv)[2], int tile, int slot) {
+  auto load_tile = [&](u32x4 (&dst)[kAttnItems], int& dv, int tile, int slot) {
     const int tok = tile * kTile + lrow;
     const bool in = tile < te && tok < K;
     const int off = !in       ? rec_bytes
-                    : a.direct ? (slot >= 0 ? slot * kRowBytes + lsub * 16 : rec_bytes)
+                    : DIRECT ? (slot >= 0 ? slot * kRowBytes + lsub * 16 : rec_bytes)
                                : tok * kRowBytes + lsub * 16;
 #pragma unroll
     for (int j = 0; j < kAttnItems; ++j)
       dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + j * 128, 0, 0);
-    const int voff = tile < te ? (tile * kTile + c2) * 4 : K * 4;
-    dv[0] = __builtin_amdgcn_raw_buffer_load_b32(vsrc, voff, 0, 0);
-    dv[1] = __builtin_amdgcn_raw_buffer_load_b32(vsrc, voff + 4, 0, 0);
+    dv = __builtin_amdgcn_raw_buffer_load_b32(vsrc, tile < te ? (tile * kTile + lrow) * 4 : K * 4,
+                                              0, 0);
   };
   const int lsw = lds_swz(lrow);
-  auto store_tile = [&](const u32x4 (&src)[kAttnItems]) {
+  auto store_tile = [&](const u32x4 (&src)[kAttnItems], int mark) {
     unsigned char* d = kv + lrow * kLdsRow + ((lsub ^ lsw) * 16);
 #pragma unroll
     for (int j = 0; j < kAttnItems; ++j) *reinterpret_cast<u32x4*>(d + j * 128) = src[j];
+    if (lsub == 0) vmark[lrow] = mark;
   };
 
   // one tile from LDS: scores, online softmax, P.V; ends with a barrier after
@@ -616,33 +646,34 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     }
     __syncthreads();
 
-    // online softmax: head h = tid / 32, tokens c2 = 2*(tid % 32) .. +1; tokens
-    // past K and empty entries score -inf
-    {
-      const int h = tid >> 5;
-      const int tok0 = tile * kTile + c2;
-      const float* s0 = sc + h * kTile + c2;
-      const float* s1 = sc + kHeads * kTile + h * kTile + c2;
-      const float x0 =
-          tok0 < K && cv[0] != pad_mark ? (s0[0] + s1[0]) * a.scale_log2 : -INFINITY;
-      const float x1 =
-          tok0 + 1 < K && cv[1] != pad_mark ? (s0[1] + s1[1]) * a.scale_log2 : -INFINITY;
-      float mx = fmaxf(x0, x1);
+    // online softmax: head h = tid / 16 (threads 0..255, whole waves), tokens
+    // c4 .. c4 + 3; tokens past K and empty entries score -inf.  The max and
+    // the sum stay inside one 16-lane DPP row.
+    if (sm_on) {
+      const int h = tid >> 4;
+      const int tok0 = tile * kTile + c4;
+      const float4 s0 = *reinterpret_cast<const float4*>(sc + h * kTile + c4);
+      const float4 s1 = *reinterpret_cast<const float4*>(sc + kHeads * kTile + h * kTile + c4);
+      const float z[4] = {s0.x + s1.x, s0.y + s1.y, s0.z + s1.z, s0.w + s1.w};
+      const int4 mk = *reinterpret_cast<const int4*>(vmark + c4);
+      const int mks[4] = {mk.x, mk.y, mk.z, mk.w};
+      float x[4];
 #pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const float m_new = fmaxf(m_run, mx);
+      for (int k = 0; k < 4; ++k)
+        x[k] = tok0 + k < K && mks[k] != pad_mark ? z[k] * a.scale_log2 : -INFINITY;
+      const float m_new = fmaxf(m_run, row16_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))));
       // no scored token yet (empty entries only): keep every weight at 0
       const float m_ref = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = exp2f(m_run - m_ref);
-      const float p0 = exp2f(x0 - m_ref), p1 = exp2f(x1 - m_ref);
-      float ps = p0 + p1;
+      float p[4];
 #pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) ps += __shfl_xor(ps, o);
-      l_run = l_run * alpha + ps;
+      for (int k = 0; k < 4; ++k) p[k] = exp2f(x[k] - m_ref);
+      l_run = l_run * alpha + row16_sum((p[0] + p[1]) + (p[2] + p[3]));
       m_run = m_new;
-      *reinterpret_cast<uint32_t*>(pb + h * kPRow + c2) =
-          (uint32_t)f32_to_bf16_rne(p0) | ((uint32_t)f32_to_bf16_rne(p1) << 16);
-      if ((tid & 31) == 0) alpha_s[h] = alpha;
+      *reinterpret_cast<uint2*>(pb + h * kPRow + c4) =
+          make_uint2((uint32_t)f32_to_bf16_rne(p[0]) | ((uint32_t)f32_to_bf16_rne(p[1]) << 16),
+                     (uint32_t)f32_to_bf16_rne(p[2]) | ((uint32_t)f32_to_bf16_rne(p[3]) << 16));
+      if ((tid & 15) == 0) alpha_s[h] = alpha;
     }
     __syncthreads();
 
@@ -700,9 +731,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     load_tile(ra, va, tb, sa);
     sa = load_slot(tb + 2);
     load_tile(rb, vb, tb + 1, sb);
-    store_tile(ra);
-    cv[0] = va[0];
-    cv[1] = va[1];
+    store_tile(ra, va);
     __syncthreads();
     // full pairs; one exit, so the loads in flight are the same (rb's) on the
     // back edge and at the exit.  The last pair's ra load and store are of the
@@ -712,16 +741,12 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
       sb = load_slot(tile + 3);
       load_tile(ra, va, tile + 2, sa);
       compute(tile);
-      store_tile(rb);
-      cv[0] = vb[0];
-      cv[1] = vb[1];
+      store_tile(rb, vb);
       __syncthreads();
       sa = load_slot(tile + 4);
       load_tile(rb, vb, tile + 3, sb);
       compute(tile + 1);
-      store_tile(ra);
-      cv[0] = va[0];
-      cv[1] = va[1];
+      store_tile(ra, va);
       __syncthreads();
     }
     if (tile < te) compute(tile);   // odd tile count: LDS holds the last tile
@@ -734,8 +759,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) po[(4 * g + j) * kVDim + wave * 64 + nt * 16 + r16] = acc[nt][j];
-  if ((tid & 31) == 0) {
-    const int h = tid >> 5;
+  if (sm_on && (tid & 15) == 0) {
+    const int h = tid >> 4;
     a.part_ml[(part * kHeads + h) * 2 + 0] = m_run;
     a.part_ml[(part * kHeads + h) * 2 + 1] = l_run;
   }
@@ -979,9 +1004,12 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, cons
   a.L = lay.L;
   a.layer = layer;
   a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
-  a.direct = (lay.flags & KVS_FLAG_DIRECT_HOT) != 0;
+  const bool direct = (lay.flags & KVS_FLAG_DIRECT_HOT) != 0;
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attention_kernel, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
+  if (direct)
+    hipLaunchKernelGGL(attention_kernel<true>, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attention_kernel<false>, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
 }
 
