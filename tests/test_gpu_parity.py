@@ -455,3 +455,52 @@ def test_publish_device_rows_then_fetch():
         h.run()
     finally:
         h.close()
+
+
+# ---------------------------------------------------------------- optional outputs, empty starts
+
+def test_step_without_lse_matches_step_with_it():
+    # two pools on the same host rows and inputs: lse = NULL must not change out
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="nolse", batch=3, context=3000, slots=500,
+                                                  topk=200, steps=4, fresh_rate=0.3)
+    host = kvs.HostPool(wl.batch, wl.layers, wl.context)
+    W.fill_pool(host.array, wl)
+    pa = _pool(wl, host=host)
+    pb = _pool(wl, host=host)
+    try:
+        topk = W.topk_streams(wl)
+        out_a = torch.empty((wl.batch, 16, 512), dtype=torch.bfloat16, device="cuda")
+        out_b = torch.empty_like(out_a)
+        lse = torch.empty((wl.batch, 16), dtype=torch.float32, device="cuda")
+        for t in range(wl.steps):
+            tk = torch.from_numpy(topk[t, 0]).cuda()
+            q = torch.from_numpy(W.queries(wl, 0, t).view(np.int16)).cuda()
+            pa.step(0, tk, q, out_a, lse)
+            pb.step(0, tk, q, out_b)
+            torch.cuda.synchronize()
+            assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16)), t
+        assert pa.sync_status()[0] == 0 and pb.sync_status()[0] == 0
+    finally:
+        pa.release()
+        pb.release()
+        host.free()
+
+
+@pytest.mark.parametrize("direct", [False, True])
+def test_padded_request_starting_empty(direct):
+    # request 0 has no entry at all on its first two steps, then ragged tails:
+    # its running max starts from -inf in every split
+    import token_level_gather_amd as kvs
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="empty_start", batch=3, context=4000,
+                                                  slots=700, topk=300, steps=5, fresh_rate=0.3)
+    flags = kvs.KVS_FLAG_DIRECT_HOT if direct else 0
+    h = Harness(wl, wl.steps, range(wl.batch), padded=True, flags=flags)
+    try:
+        h.topk[0:2, :, 0, :] = -1
+        h.topk[2, :, 0, 250:] = -1
+        h.topk[3, :, 0, 1:] = -1
+        h.run()
+    finally:
+        h.close()

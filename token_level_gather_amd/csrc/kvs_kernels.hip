@@ -185,35 +185,36 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   const int32_t* topk = a.topk + (long long)b * K;
   const long long bk = (long long)b * K;
 
-  // 0. independent loads first: Top-K entries, LRU order, step counter
+  // 0. independent loads first: Top-K entries, LRU order, step counter.  No
+  //    load sits behind a branch: indices are clamped into range and the
+  //    values of positions past K or S are never used (every later use is
+  //    guarded).  With a branch per load the compiler's wait counting takes
+  //    the path with no loads and drains every load before the next one is
+  //    issued, which serialises the two independent chains below.
   int my_tok[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int i = i0 + j;
-    my_tok[j] = (j < kpt && i < K) ? topk[i] : 0;
-  }
+  for (int j = 0; j < KPT; ++j) my_tok[j] = topk[min(i0 + j, K - 1)];
   int my_ord[SPT];
 #pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    const int p = p0 + q;
-    my_ord[q] = (q < spt && p < S) ? (int)gorder[p] : 0;
-  }
+  for (int q = 0; q < SPT; ++q) my_ord[q] = (int)gorder[min(p0 + q, S - 1)];
   const int t = a.stepctr[u];
-  // the token held by the slot at each of this thread's order positions
+  // the token held by the slot at each of this thread's order positions (the
+  // order array is a permutation of the slots, so my_ord is in range)
   int my_old[SPT];
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
     const int p = p0 + q;
-    my_old[q] = (q < spt && p < S) ? slot2tok[my_ord[q]] : -1;
+    my_old[q] = slot2tok[my_ord[q]];
     if (q < spt && p < S) flag[p] = 0;
   }
-  // 1a. slot lookup of every in-range entry, issued before the first barrier
+  // 1a. slot lookup of every entry, issued before the first barrier and not
+  //     used before it (an entry outside [0, N) reads token 0's slot; the
+  //     validation after the barrier discards it)
   int my_slot[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int i = i0 + j;
     const int tok = my_tok[j];
-    my_slot[j] = (j < kpt && i < K && tok >= 0 && (long long)tok < a.N) ? tok2slot[tok] : -1;
+    my_slot[j] = tok2slot[tok >= 0 && (long long)tok < a.N ? tok : 0];
   }
   for (int h = tid; h < H; h += kDiffThreads) hash[h] = -1;
   if (tid == 0) {
