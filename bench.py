@@ -150,8 +150,9 @@ def cpu_baseline(wl, host, topk, q, total_steps, seconds, keep_requests):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; run with --gpus 1 "
-                                   "(the path shards by request, see the design notes)"}))
+        print(json.dumps({"error": "bench.py measures one GPU only; run with --gpus 1 (the path "
+                                   "shards by request with no exchange between GPUs, so one "
+                                   "GPU's share at its real shape is the measurement)"}))
         sys.exit(2)
     import torch
 
