@@ -131,7 +131,8 @@ typedef struct kvs_sizes {
   uint64_t host_pool_bytes; /* B*L*N*576*2: the full-history pool, host */
   uint64_t hot_bytes;       /* B*L*S*576*2: hot KV buffer, device */
   uint64_t meta_bytes;      /* index maps, LRU state, counters, status, device */
-  uint64_t cbuf_bytes;      /* B*K*576*2: compute buffer of one step, device */
+  uint64_t cbuf_bytes;      /* B*K*576*2: compute buffer of one step, device (0 with
+                               KVS_FLAG_DIRECT_HOT) */
   uint64_t scratch_bytes;   /* per-step lists and attention partials, device */
   int32_t attn_splits;      /* the split count these sizes assume */
   int32_t fetch_blocks;     /* resolved kvs_config.fetch_blocks */
@@ -141,7 +142,8 @@ typedef struct kvs_sizes {
  * Buffers handed to kvs_create_pool.  Layouts (row = 576 bf16, row-major):
  *   host_pool [B][L][N] rows: token n of unit (b, l) at row (b*L + l)*N + n.
  *             Must come from kvs_host_alloc (pinned and mapped for the GPU).
- *   hot       [B][L][S] rows, device.   cbuf [B][K] rows, device.
+ *   hot       [B][L][S] rows, device.
+ *   cbuf      [B][K] rows, device; may be NULL with KVS_FLAG_DIRECT_HOT.
  *   meta, scratch: opaque device memory, 256-byte aligned.
  * The *_bytes fields state each buffer's capacity; a capacity below
  * kvs_query_sizes gives KVS_ENOMEM.  meta is initialised by kvs_create_pool.
