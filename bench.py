@@ -66,6 +66,25 @@ def parse():
     return p.parse_args()
 
 
+def measure_zero_copy_peak(torch, pool, reps=5):
+    """Best of `reps` zero-copy reads of up to 1 GiB of the pinned pool by a plain
+    GPU read kernel with the fetch's load pattern (the host link's ceiling for
+    GPU-initiated reads), timed with events on the stream it runs on."""
+    import token_level_gather_amd as kvs
+    nbytes = min(pool.host.nbytes, 1 << 30) // 16 * 16
+    sink = torch.empty(kvs.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvs.probe_host_read(pool.host.ptr, nbytes, sink)
+        e1.record()
+        e1.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    return best
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -307,6 +326,7 @@ def main():
         kernels = kernel_stats(ktimes, alg_b, kvs.KERNEL_NAMES)
 
     h2d = measure_h2d_peak(torch)
+    zc = measure_zero_copy_peak(torch, pool)
     roofline = None
     if dom is not None:
         roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved_gbs"],
@@ -315,6 +335,7 @@ def main():
                     "bytes_per_launch": dom["bytes_per_launch"]}
         if dom["bound"] == "pcie":
             roofline["frac_of_measured_h2d"] = round(dom["achieved_gbs"] / h2d, 4)
+            roofline["frac_of_zero_copy_peak"] = round(dom["achieved_gbs"] / zc, 4)
         if "hbm_bytes" in alg[dominant]:
             # what the HBM counters should read if nothing is re-read: the kernel's
             # algorithmic HBM bytes plus the host rows it pulls through the L2
@@ -401,6 +422,7 @@ def main():
         "host_link_gbs_step": round(ROW * misses / args.steps / (ms_step * 1e-3) / 1e9, 3),
         "hbm_gbs_step": round(hbm_bytes_step / (ms_step * 1e-3) / 1e9, 2),
         "h2d_peak_measured_gbs": round(h2d, 2),
+        "zero_copy_read_peak_gbs": round(zc, 2),
         "kernels": kernels,
         "kernels_note": f"per-kernel HIP events around every launch over {breakdown} extra steps "
                         "after the timed region; inside the timed region only the dominant "

@@ -303,6 +303,19 @@ int kvs_graph_destroy(kvs_graph* graph);
 /* Destroy the pool's timing events and host-side state.  Caller buffers are untouched. */
 int kvs_release(kvs_pool* pool);
 
+/* ---- measurement helper (not a step of the path) ------------------------ */
+
+/* The host link's zero-copy read ceiling, against which the miss fetch is
+ * judged: read `bytes` of pinned host memory (from kvs_host_alloc; 16-byte
+ * aligned, a multiple of 16 bytes) from the GPU with the fetch's own load
+ * pattern (16 B per lane, consecutive lanes on consecutive 16-byte chunks,
+ * 256 workgroups of 256 threads) and XOR-reduce it into `sink` (device,
+ * KVS_PROBE_SINK_WORDS uint32, overwritten).  Enqueued on `stream`; the
+ * caller times it with events on that stream.  KVS_EINVAL for a pointer the
+ * GPU cannot address or a bad size or alignment. */
+#define KVS_PROBE_SINK_WORDS 65536
+int kvs_probe_host_read(const void* host, uint64_t bytes, uint32_t* sink, void* stream);
+
 /* Static description of a return code. */
 const char* kvs_strerror(int code);
 

@@ -504,3 +504,29 @@ def test_padded_request_starting_empty(direct):
         h.run()
     finally:
         h.close()
+
+
+# ---------------------------------------------------------------- measurement helper
+
+def test_host_read_probe_reads_every_byte():
+    # the probe's per-thread XOR fold, recomputed from the host bytes: thread t
+    # folds the 16-byte chunks t, t + 65536, ... of the buffer
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    host = kvs.HostPool(1, 1, 3000)   # 3000 rows x 1152 B: 216,000 chunks, a ragged last pass
+    try:
+        rng = np.random.default_rng(11)
+        host.array[...] = rng.integers(0, 65536, size=host.array.shape, dtype=np.uint16)
+        sink = torch.empty(kvs.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+        kvs.probe_host_read(host.ptr, host.nbytes, sink)
+        torch.cuda.synchronize()
+        words = host.array.reshape(-1).view(np.uint32).reshape(-1, 4)
+        per_chunk = np.bitwise_xor.reduce(words, axis=1)
+        n = per_chunk.size
+        pad = (-n) % kvs.PROBE_SINK_WORDS
+        folded = np.bitwise_xor.reduce(
+            np.concatenate([per_chunk, np.zeros(pad, np.uint32)]).reshape(-1, kvs.PROBE_SINK_WORDS),
+            axis=0)
+        assert np.array_equal(sink.cpu().numpy().view(np.uint32), folded)
+    finally:
+        host.free()

@@ -30,6 +30,7 @@ KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine")
 KVS_FLAG_HITS_FIRST = 1
 KVS_FLAG_PADDED_TOPK = 2
 KVS_FLAG_DIRECT_HOT = 4
+PROBE_SINK_WORDS = 65536
 
 # Every exported symbol of include/kvs.h.
 EXPORTS = (
@@ -37,7 +38,7 @@ EXPORTS = (
     "kvs_step", "kvs_free_request", "kvs_sync_status", "kvs_debug_read_state",
     "kvs_profile_begin", "kvs_profile_end", "kvs_release", "kvs_strerror",
     "kvs_graph_capture", "kvs_graph_launch", "kvs_graph_destroy", "kvs_publish_device",
-    "kvs_append",
+    "kvs_append", "kvs_probe_host_read",
 )
 
 
@@ -121,6 +122,7 @@ def lib() -> ctypes.CDLL:
         "kvs_publish": [vp, i32, i32, i64, i64, vp],
         "kvs_publish_device": [vp, i32, i32, i64, i64, vp, vp],
         "kvs_append": [vp, i32, vp, vp, vp],
+        "kvs_probe_host_read": [vp, u64, vp, vp],
         "kvs_step": [vp, i32, vp, vp, vp, vp, vp],
         "kvs_free_request": [vp, i32, vp],
         "kvs_sync_status": [vp, vp, ctypes.POINTER(kvs_step_stats)],
@@ -183,6 +185,15 @@ class HostPool:
             self.array = None
             lib().kvs_host_free(self.ptr)
             self.ptr = None
+
+
+def probe_host_read(host_ptr: int, nbytes: int, sink, stream=None) -> None:
+    """Enqueue the zero-copy host-read probe (measurement helper): ``sink`` is a
+    contiguous device tensor of PROBE_SINK_WORDS 4-byte words."""
+    if not sink.is_cuda or sink.numel() * sink.element_size() < 4 * PROBE_SINK_WORDS:
+        raise ValueError("sink must be a device tensor of PROBE_SINK_WORDS 4-byte words")
+    _check(lib().kvs_probe_host_read(host_ptr, nbytes, sink.data_ptr(), _stream_ptr(stream)),
+           "kvs_probe_host_read")
 
 
 def _stream_ptr(stream) -> Optional[int]:

@@ -512,6 +512,17 @@ int kvs_release(kvs_pool* p) {
   return KVS_OK;
 }
 
+int kvs_probe_host_read(const void* host, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (host == nullptr || sink == nullptr || bytes == 0 || (bytes & 15) != 0) return KVS_EINVAL;
+  if (((uintptr_t)host & 15) != 0 || ((uintptr_t)sink & 3) != 0) return KVS_EINVAL;
+  void* dev = nullptr;
+  if (hipHostGetDevicePointer(&dev, const_cast<void*>(host), 0) != hipSuccess || dev == nullptr) {
+    (void)hipGetLastError();
+    return KVS_EINVAL;
+  }
+  return hip_err(launch_host_read_probe(dev, (long long)(bytes / 16), sink, (hipStream_t)stream));
+}
+
 const char* kvs_strerror(int code) {
   switch (code) {
     case KVS_OK: return "ok";

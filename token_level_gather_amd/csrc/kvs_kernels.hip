@@ -853,6 +853,30 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
   __threadfence_system();
 }
 
+// ------------------------------------------------------------------ host read probe
+// Zero-copy read of pinned host memory with the fetch role's access pattern:
+// each wave instruction reads 1 KB of consecutive host memory.  Every thread
+// XOR-folds its chunks and stores one word, so no load can be dropped.
+constexpr int kProbeBlocks = 256, kProbeThreads = 256;
+static_assert(kProbeBlocks * kProbeThreads == KVS_PROBE_SINK_WORDS, "probe sink size");
+
+__global__ __launch_bounds__(kProbeThreads) void host_read_probe_kernel(const u32x4* src,
+                                                                         long long chunks,
+                                                                         uint32_t* sink) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  long long c = t;
+  // four chunks in flight per thread per pass
+  for (; c + 3 * stride < chunks; c += 4 * stride) {
+    const u32x4 v0 = src[c], v1 = src[c + stride], v2 = src[c + 2 * stride],
+                v3 = src[c + 3 * stride];
+    acc ^= v0 ^ v1 ^ v2 ^ v3;
+  }
+  for (; c < chunks; c += stride) acc ^= src[c];
+  sink[t] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -1021,6 +1045,13 @@ hipError_t launch_append(const Layout& lay, const DevPtrs& d, int layer, const u
                      reinterpret_cast<u32x4*>(const_cast<uint16_t*>(d.pool)),
                      reinterpret_cast<u32x4*>(d.hot), d.tok2slot, d.status, (long long)lay.N,
                      lay.S, lay.L, layer);
+  return hipGetLastError();
+}
+
+hipError_t launch_host_read_probe(const void* src, long long chunks, uint32_t* sink,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(host_read_probe_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0, s,
+                     reinterpret_cast<const u32x4*>(src), chunks, sink);
   return hipGetLastError();
 }
 
