@@ -7,10 +7,14 @@
 //              eviction and map update.
 //   gather     the index copy: miss rows read from pinned host memory over
 //              PCIe into the compute buffer and the victim slots, hit rows
-//              copied from the hot buffer to the compute buffer, in one grid.
-//   attention  split-K sparse MLA decode over the K gathered rows:
-//              v_mfma_f32_16x16x32_bf16 for Q.K^T and P.V, fp32 online softmax.
+//              copied from the hot buffer to the compute buffer, in one grid
+//              (rows read in place: only the misses, into their slots).
+//   attention  split-K sparse MLA decode over the K gathered rows (or over
+//              the hot buffer through row_slot): v_mfma_f32_16x16x32_bf16 for
+//              Q.K^T and P.V, fp32 online softmax.
 //   combine    merges the split partials, writes bf16 out and fp32 lse.
+// Outside the step: init/reset kernels (pool creation, kvs_free_request), the
+// append kernel (kvs_append) and the host-read probe (a measurement helper).
 //
 // Passages: index mapping / host pool / device cache / index-copy assembly
 // ("Sparse Attention-Driven KVCache Management for Domestic AI Supernodes",
@@ -536,8 +540,9 @@ struct AttnArgs {
 // Wave roles per 64-token tile:
 //   Q.K^T   wave w: tokens 16*(w % 4) .. +16, k-steps 9*(w / 4) .. +9 (two
 //           partial score tiles per token block, summed in the softmax);
-//   softmax 32 threads per head, 2 tokens each;
-//   P.V     wave w: value columns 64*w .. +64 (4 MFMA column tiles).
+//   softmax waves 0..3: 16 lanes (one DPP row) per head, 4 tokens each;
+//   P.V     wave w: value columns 64*w .. +64 (4 MFMA column tiles), the
+//           value operand through transpose LDS reads.
 // DIRECT: rows read in place from the hot buffer at row_slot (a separate
 // instantiation, so the assembled-buffer path carries no slot loads at all).
 template <bool DIRECT>
