@@ -242,10 +242,11 @@ def test_zipf_stream_small():
 
 # ---------------------------------------------------------------- lifecycle and errors
 
-def test_free_request_then_cold_refill():
+@pytest.mark.parametrize("direct", [False, True])
+def test_free_request_then_cold_refill(direct):
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(batch=3, context=4000, slots=600, topk=256,
                                                   steps=8)
-    h = Harness(wl, wl.steps, range(3))
+    h = Harness(wl, wl.steps, range(3), flags=_direct() if direct else 0)
     try:
         for t in range(4):
             h.check(t, 0, *h.device_step(t, 0))
@@ -259,16 +260,17 @@ def test_free_request_then_cold_refill():
         h.close()
 
 
+@pytest.mark.parametrize("direct", [False, True])
 @pytest.mark.parametrize("padded", [False, True])
 @pytest.mark.parametrize("kind", ["range", "negative", "duplicate"])
-def test_invalid_topk_leaves_request_untouched(kind, padded):
+def test_invalid_topk_leaves_request_untouched(kind, padded, direct):
     # with padding only -1 is empty: -5 stays out of range, and a token repeated
     # beside empty entries is still a duplicate
     import token_level_gather_amd as kvs
     torch = _torch()
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(batch=3, context=3000, slots=500, topk=200,
                                                   steps=6)
-    h = Harness(wl, wl.steps, range(3), padded=padded)
+    h = Harness(wl, wl.steps, range(3), padded=padded, flags=_direct() if direct else 0)
     try:
         for t in range(2):
             h.check(t, 0, *h.device_step(t, 0))
@@ -384,7 +386,8 @@ def _bf16_rows(rng, n):
     return W.f32_to_bf16_bits(rng.standard_normal((n, 576)).astype(np.float32))
 
 
-def test_append_rows_then_hit_and_fetch():
+@pytest.mark.parametrize("direct", [False, True])
+def test_append_rows_then_hit_and_fetch(direct):
     # one new row per request: a token resident in the hot buffer (the next
     # step hits it and must read the new bytes from the hot copy), a token that
     # is not (the next step fetches it from the pool), and two requests with
@@ -392,7 +395,7 @@ def test_append_rows_then_hit_and_fetch():
     torch = _torch()
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="append", batch=4, layers=2, context=3000,
                                                   slots=400, topk=200, steps=6, fresh_rate=0.3)
-    h = Harness(wl, wl.steps, range(wl.batch))
+    h = Harness(wl, wl.steps, range(wl.batch), flags=_direct() if direct else 0)
     try:
         for t in range(2):
             for l in range(wl.layers):
