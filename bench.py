@@ -35,6 +35,17 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 PCIE_PEAK_GBS = 63.0             # PCIe Gen5 x16, one direction: 32 GT/s * 16 * 128/130 / 8
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 ROW = W.ROW_BYTES
+# The pages' own figures are system-level (whole models, other hardware and
+# serving stacks); none is a figure for this path, so none is compared.
+PAGES_CONTEXT = {
+    "comparable": False,
+    "device_memory_per_request": "8 GB to 200 MB with about 3x single-machine throughput "
+                                 "(DeepSeek DSA scenario; SGLang/Tair hierarchical sparse "
+                                 "attention summary)",
+    "tpot_reduction": "49.25 % at 20 % and 63.58 % at 40 % Top-K miss, GLM-5.3 at 16K context "
+                      "and per-GPU batch 192 on NVIDIA B300 decode GPUs, X-Mem against PCIe "
+                      "host DRAM (XM-Sparse)",
+}
 
 
 def parse():
@@ -423,6 +434,11 @@ def main():
         "hbm_gbs_step": round(hbm_bytes_step / (ms_step * 1e-3) / 1e9, 2),
         "h2d_peak_measured_gbs": round(h2d, 2),
         "zero_copy_read_peak_gbs": round(zc, 2),
+        # decode steps/s if the step were only its miss bytes at the link's rate
+        "steps_per_s_link_ceiling": {
+            "pcie_gen5_x16_63gbs": round(63.0e9 / max(1.0, ROW * misses / args.steps), 1),
+            "measured_zero_copy": round(zc * 1e9 / max(1.0, ROW * misses / args.steps), 1)},
+        "pages_context": PAGES_CONTEXT,
         "kernels": kernels,
         "kernels_note": f"per-kernel HIP events around every launch over {breakdown} extra steps "
                         "after the timed region; inside the timed region only the dominant "
