@@ -196,19 +196,24 @@ def probe_host_read(host_ptr: int, nbytes: int, sink, stream=None) -> None:
            "kvs_probe_host_read")
 
 
-def _stream_ptr(stream) -> Optional[int]:
+def _stream_ptr(stream, device=None) -> Optional[int]:
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return stream.cuda_stream
 
 
 class Pool:
     """One pool of B requests x L layers: hot buffers, maps and the host pool.
 
-    Device buffers are torch tensors on the current HIP device; the host pool
-    is pinned memory from kvs_host_alloc (``self.host.array`` is its numpy
-    view).  ``step`` enqueues one layer's fetch + write-back + attention.
+    Device buffers are torch tensors on ``device`` (default: the current HIP
+    device); the host pool is pinned memory from kvs_host_alloc
+    (``self.host.array`` is its numpy view).  ``step`` enqueues one layer's
+    fetch + write-back + attention.  Calls without a stream use ``device``'s
+    current stream; when that is the default (NULL) stream, ``device`` must be
+    the current device (the library rejects a stream of another device).
+    ``close()`` (or leaving a ``with`` block) releases the
+    pool and frees a host pool the pool allocated itself.
     """
 
     def __init__(self, batch, layers, context, slots, topk, scale=None, attn_splits=0,
@@ -219,7 +224,9 @@ class Pool:
                                fetch_blocks, hit_blocks, flags)
         self.sizes = query_sizes(self.cfg)
         self.B, self.L, self.N, self.S, self.K = batch, layers, context, slots, topk
-        self.device = torch.device("cuda" if device is None else device)
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        self._owns_host = host is None
         self.host = host if host is not None else HostPool(batch, layers, context)
         if self.host.nbytes < self.sizes.host_pool_bytes:
             raise KvsError(KVS_ENOMEM, "host pool")
@@ -236,8 +243,10 @@ class Pool:
                            self.hot.numel(), self.meta.numel(), self.cbuf.numel(),
                            self.scratch.numel())
         handle = ctypes.c_void_p()
-        _check(lib().kvs_create_pool(ctypes.byref(self.cfg), ctypes.byref(bufs),
-                                     _stream_ptr(stream), ctypes.byref(handle)),
+        with torch.cuda.device(self.device):   # the library binds the pool to the current device
+            rc = lib().kvs_create_pool(ctypes.byref(self.cfg), ctypes.byref(bufs),
+                                       _stream_ptr(stream, self.device), ctypes.byref(handle))
+        _check(rc,
                "kvs_create_pool")
         self.handle = handle
 
@@ -254,7 +263,7 @@ class Pool:
                 or rows.element_size() != 2 or not rows.is_contiguous():
             raise ValueError("expected a contiguous device tensor [n][576] of bf16")
         _check(lib().kvs_publish_device(self.handle, req, layer, first_tok, rows.shape[0],
-                                        rows.data_ptr(), _stream_ptr(stream)),
+                                        rows.data_ptr(), _stream_ptr(stream, self.device)),
                "kvs_publish_device")
 
     def append(self, layer, rows, pos, stream=None):
@@ -262,7 +271,7 @@ class Pool:
         self._check_dev(rows, (self.B, HEAD_DIM), 2)
         self._check_dev(pos, (self.B,), 8)
         _check(lib().kvs_append(self.handle, layer, rows.data_ptr(), pos.data_ptr(),
-                                _stream_ptr(stream)), "kvs_append")
+                                _stream_ptr(stream, self.device)), "kvs_append")
 
     def step(self, layer, topk, q, out, lse=None, stream=None):
         """topk [B][K] int32, q [B][16][576] bf16/uint16, out [B][16][512] bf16 (device)."""
@@ -274,15 +283,17 @@ class Pool:
             self._check_dev(lse, (self.B, HEADS), 4)
             lse_ptr = lse.data_ptr()
         _check(lib().kvs_step(self.handle, layer, topk.data_ptr(), q.data_ptr(), out.data_ptr(),
-                              lse_ptr, _stream_ptr(stream)), "kvs_step")
+                              lse_ptr, _stream_ptr(stream, self.device)), "kvs_step")
 
     def free_request(self, req, stream=None):
-        _check(lib().kvs_free_request(self.handle, req, _stream_ptr(stream)), "kvs_free_request")
+        _check(lib().kvs_free_request(self.handle, req, _stream_ptr(stream, self.device)),
+               "kvs_free_request")
 
     def sync_status(self, stream=None):
         """Returns (status code, kvs_step_stats); the status is cleared."""
         st = kvs_step_stats()
-        rc = lib().kvs_sync_status(self.handle, _stream_ptr(stream), ctypes.byref(st))
+        rc = lib().kvs_sync_status(self.handle, _stream_ptr(stream, self.device),
+                                   ctypes.byref(st))
         if rc not in (KVS_OK, KVS_ERANGE, KVS_EDUP):
             raise KvsError(rc, "kvs_sync_status")
         return rc, st
@@ -296,7 +307,7 @@ class Pool:
             "counts": np.empty(4, np.int32), "row_slot": np.empty(self.K, np.int32),
         }
         st = kvs_unit_state(*[a.ctypes.data_as(_I32P) for a in arr.values()], 0)
-        _check(lib().kvs_debug_read_state(self.handle, req, layer, _stream_ptr(stream),
+        _check(lib().kvs_debug_read_state(self.handle, req, layer, _stream_ptr(stream, self.device),
                                           ctypes.byref(st)), "kvs_debug_read_state")
         arr["step"] = int(st.step)
         return arr
@@ -322,16 +333,32 @@ class Pool:
         self._check_dev(out, (self.B, HEADS, V_DIM), 2)
         if lse is not None:
             self._check_dev(lse, (self.B, HEADS), 4)
+        import torch
         g = ctypes.c_void_p()
-        _check(lib().kvs_graph_capture(self.handle, layer, topk.data_ptr(), q.data_ptr(),
-                                       out.data_ptr(), None if lse is None else lse.data_ptr(),
-                                       ctypes.byref(g)), "kvs_graph_capture")
-        return StepGraph(g, (topk, q, out, lse))
+        with torch.cuda.device(self.device):   # the capture stream is made on the current device
+            rc = lib().kvs_graph_capture(self.handle, layer, topk.data_ptr(), q.data_ptr(),
+                                         out.data_ptr(), None if lse is None else lse.data_ptr(),
+                                         ctypes.byref(g))
+        _check(rc, "kvs_graph_capture")
+        return StepGraph(g, (topk, q, out, lse), self.device)
 
     def release(self):
         if self.handle:
             _check(lib().kvs_release(self.handle), "kvs_release")
             self.handle = None
+
+    def close(self):
+        """Release the pool and free the host pool if this pool allocated it."""
+        self.release()
+        if self._owns_host and self.host.ptr:
+            self.host.free()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
 
     # -- helpers ----------------------------------------------------------
     def _check_dev(self, t, shape, itemsize):
@@ -342,14 +369,16 @@ class Pool:
 
 
 class StepGraph:
-    """A captured kvs_step; launch() replays it on a stream."""
+    """A captured kvs_step; launch() replays it on a stream of the pool's device."""
 
-    def __init__(self, handle, keep_alive):
+    def __init__(self, handle, keep_alive, device=None):
         self.handle = handle
         self._keep = keep_alive
+        self.device = device
 
     def launch(self, stream=None):
-        _check(lib().kvs_graph_launch(self.handle, _stream_ptr(stream)), "kvs_graph_launch")
+        _check(lib().kvs_graph_launch(self.handle, _stream_ptr(stream, self.device)),
+               "kvs_graph_launch")
 
     def destroy(self):
         if self.handle:
