@@ -350,8 +350,8 @@ def main():
         if "hbm_bytes" in alg[dominant]:
             # what the HBM counters should read if nothing is re-read: the kernel's
             # algorithmic HBM bytes plus the host rows it pulls through the L2
-            roofline["algorithmic_traffic"] = int((alg[dominant]["hbm_bytes"]
-                                                   + alg[dominant]["bytes"]) / dom["launches_per_call"])
+            alg_hbm = alg[dominant]["hbm_bytes"] + alg[dominant]["bytes"]
+            roofline["algorithmic_traffic"] = int(alg_hbm / dom["launches_per_call"])
 
     # parity of sampled requests against the oracle, plus the CPU baseline
     cpu = None
@@ -367,7 +367,8 @@ def main():
             for l in range(L):
                 for t in range(total):
                     ref = rec[(t, l, b)]
-                    got = (out_np[t, l, b].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                    got = ((out_np[t, l, b].astype(np.uint32) << 16).view(np.float32)
+                           .astype(np.float64))
                     err = got - ref
                     max_abs = max(max_abs, float(np.abs(err).max()))
                     max_rel = max(max_rel, float(np.linalg.norm(err) / np.linalg.norm(ref)))

@@ -106,7 +106,8 @@ def test_create_pool_argument_checks_before_any_gpu_call():
     lib = kvs.lib()
     cfg = kvs.make_config(batch=1, layers=1, context=4096, slots=512, topk=256)
     handle = ctypes.c_void_p()
-    assert lib.kvs_create_pool(ctypes.byref(cfg), None, None, ctypes.byref(handle)) == kvs.KVS_EINVAL
+    rc = lib.kvs_create_pool(ctypes.byref(cfg), None, None, ctypes.byref(handle))
+    assert rc == kvs.KVS_EINVAL
     fake = 1 << 20   # aligned, never dereferenced: the size check fails first
     bufs = kvs.kvs_buffers(fake, fake, fake, fake, fake, 16, 16, 16, 16, 16)
     assert lib.kvs_create_pool(ctypes.byref(cfg), ctypes.byref(bufs), None,

@@ -44,7 +44,8 @@ def test_graph_replay_equals_eager_and_oracle(mode):
         torch.cuda.synchronize()
         # capture ran nothing: the pool is still empty
         assert pg.read_state(0, 0)["step"] == 0
-        oracle = {(b, l): OracleUnit(wl.context, wl.slots, wl.topk) for b in range(B) for l in range(L)}
+        oracle = {(b, l): OracleUnit(wl.context, wl.slots, wl.topk)
+                  for b in range(B) for l in range(L)}
         for t in range(wl.steps):
             for l in range(L):
                 q = W.queries(wl, l, t)

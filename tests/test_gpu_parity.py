@@ -533,3 +533,17 @@ def test_host_read_probe_reads_every_byte():
         assert np.array_equal(sink.cpu().numpy().view(np.uint32), folded)
     finally:
         host.free()
+
+
+def test_pool_context_manager_releases_and_frees_its_host_pool():
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    wl = W.WORKLOADS["ctx4k_b1_k256"]
+    with kvs.Pool(wl.batch, wl.layers, wl.context, wl.slots, wl.topk, scale=wl.scale) as pool:
+        W.fill_pool(pool.host.array, wl)
+        out = torch.empty((1, 16, 512), dtype=torch.bfloat16, device="cuda")
+        tk = torch.from_numpy(W.topk_streams(wl, 1)[0, 0]).cuda()
+        q = torch.from_numpy(W.queries(wl, 0, 0).view(np.int16)).cuda()
+        pool.step(0, tk, q, out)
+        assert pool.sync_status()[0] == 0
+    assert pool.handle is None and pool.host.ptr is None

@@ -169,7 +169,8 @@ def test_invariants_and_set_algebra(seed):
             assert u.tok2slot[x] >= 0 and u.last_used[u.tok2slot[x]] == t
         # I7: every victim sorts before every non-victim non-hit slot
         hit_slots = {int(s) for s in rec.slot_of if s >= 0}
-        others = [s for s in range(slots) if s not in hit_slots and s not in set(rec.victims.tolist())]
+        vic = set(rec.victims.tolist())
+        others = [s for s in range(slots) if s not in hit_slots and s not in vic]
         for v in rec.victims:
             for s in others:
                 assert (lu_before[v], v) < (lu_before[s], s)
