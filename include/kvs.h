@@ -65,6 +65,7 @@ extern "C" {
 #define KVS_ENOMEM (-12)    /* a caller buffer is smaller than kvs_query_sizes asks */
 #define KVS_ERANGE (-34)    /* device saw a Top-K index outside [0, N) */
 #define KVS_EDUP (-17)      /* device saw a repeated Top-K index within one request */
+#define KVS_ECORRUPT (-74)  /* KVS_FLAG_CHECK found a unit whose state breaks an invariant */
 #define KVS_EHIP_BASE (-1000) /* KVS_EHIP_BASE - e: HIP runtime error e */
 
 /* ---- limits ------------------------------------------------------------ */
@@ -125,6 +126,14 @@ typedef struct kvs_config {
  * abstract: an index-based copy builds the step's data) becomes an indexed
  * read inside attention. */
 #define KVS_FLAG_DIRECT_HOT 4
+/* kvs_config.flags: after the diff of every step, verify each touched unit:
+ * token-to-slot and slot-to-token maps are mutual inverses (all N tokens,
+ * all S slots), the LRU order array holds every slot once in ascending
+ * (last_used_step, slot) order, and no victim of the step is one of its hit
+ * slots.  A violation latches KVS_ECORRUPT for kvs_sync_status.  One extra
+ * launch per step that reads each unit's maps whole (4 B per token and
+ * 10 B per slot): a debugging aid, not for timed runs. */
+#define KVS_FLAG_CHECK 8
 
 /* Bytes each caller buffer must hold (see kvs_buffers). */
 typedef struct kvs_sizes {

@@ -84,7 +84,7 @@ def test_query_sizes_arithmetic():
     dict(batch=0), dict(layers=0), dict(topk=0), dict(slots=100, topk=200),
     dict(context=100, topk=200, slots=300), dict(slots=16385), dict(topk=8193, slots=9000),
     dict(heads=8), dict(head_dim=512), dict(v_dim=576), dict(scale=0.0),
-    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=8), dict(context=2**31),
+    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=16), dict(context=2**31),
     dict(fetch_blocks=-1), dict(fetch_blocks=65536), dict(hit_blocks=-1), dict(hit_blocks=70000),
     dict(attn_splits=33),   # more splits than 64-token tiles (K = 2048 -> 32)
 ])
@@ -133,12 +133,14 @@ def test_null_pool_calls_are_rejected():
 
 def test_padded_flag_accepted():
     cfg = kvs.make_config(batch=2, layers=1, context=4096, slots=512, topk=256,
-                          flags=kvs.KVS_FLAG_PADDED_TOPK | kvs.KVS_FLAG_HITS_FIRST)
+                          flags=kvs.KVS_FLAG_PADDED_TOPK | kvs.KVS_FLAG_HITS_FIRST
+                          | kvs.KVS_FLAG_DIRECT_HOT | kvs.KVS_FLAG_CHECK)
     out = kvs.kvs_sizes()
     assert kvs.lib().kvs_query_sizes(ctypes.byref(cfg), ctypes.byref(out)) == kvs.KVS_OK
 
 
 def test_strerror():
+    assert "state check" in kvs.strerror(kvs.KVS_ECORRUPT)
     assert "duplicate" in kvs.strerror(kvs.KVS_EDUP)
     assert "outside" in kvs.strerror(kvs.KVS_ERANGE)
     assert kvs.strerror(kvs.KVS_OK) == "ok"

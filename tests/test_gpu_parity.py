@@ -547,3 +547,78 @@ def test_pool_context_manager_releases_and_frees_its_host_pool():
         pool.step(0, tk, q, out)
         assert pool.sync_status()[0] == 0
     assert pool.handle is None and pool.host.ptr is None
+
+
+# ---------------------------------------------------------------- state checker
+
+@pytest.mark.parametrize("case", ["small", "padded", "direct", "zipf", "free_refill"])
+def test_state_check_passes_on_valid_runs(case):
+    import token_level_gather_amd as kvs
+    base = W.WORKLOADS["ctx16k_b64_k2048"]
+    flags = kvs.KVS_FLAG_CHECK | (kvs.KVS_FLAG_DIRECT_HOT if case == "direct" else 0)
+    if case == "zipf":
+        wl = W.WORKLOADS["ctx128k_b32_l8_zipf"].shrunk(batch=3, layers=2, context=20000, steps=5)
+    else:
+        wl = base.shrunk(name="check", batch=3, layers=2, context=4000, slots=500, topk=300,
+                         steps=6, fresh_rate=0.4)
+    h = Harness(wl, wl.steps, range(wl.batch), padded=case == "padded", flags=flags)
+    try:
+        if case == "free_refill":
+            for t in range(3):
+                for l in range(wl.layers):
+                    h.check(t, l, *h.device_step(t, l))
+            h.pool.free_request(1)
+            for l in range(wl.layers):
+                h.oracle[(1, l)].reset()
+            for t in range(3, wl.steps):
+                for l in range(wl.layers):
+                    h.check(t, l, *h.device_step(t, l))
+            assert h.pool.sync_status()[0] == 0
+        else:
+            h.run()   # asserts a clean status at the end
+    finally:
+        h.close()
+
+
+def _meta_offsets(pool):
+    # byte offsets of the per-unit arrays inside the pool's meta buffer: the
+    # library lays out tok2slot [U][N] int32, slot2tok [U][S] int32, last_used
+    # [U][S] int32 and the LRU order [U][S] uint16 in that order, each 256-byte
+    # aligned (white-box knowledge, used only to corrupt state on purpose)
+    def up(x):
+        return (x + 255) // 256 * 256
+    U = pool.B * pool.L
+    t2s = 0
+    s2t = up(t2s + U * pool.N * 4)
+    lu = up(s2t + U * pool.S * 4)
+    order = up(lu + U * pool.S * 4)
+    return s2t, lu, order
+
+
+@pytest.mark.parametrize("what", ["maps", "order"])
+def test_state_check_catches_corruption(what):
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="corrupt", batch=2, context=3000, slots=400,
+                                                  topk=200, steps=3, fresh_rate=0.3)
+    h = Harness(wl, wl.steps, [0], flags=kvs.KVS_FLAG_CHECK)
+    try:
+        h.device_step(0, 0)
+        assert h.pool.sync_status()[0] == 0
+        st = h.pool.read_state(0, 0)
+        assert np.array_equal(np.sort(st["lru_order"]), np.arange(wl.slots))
+        s2t_off, _, order_off = _meta_offsets(h.pool)
+        if what == "maps":   # two occupied slots swap tokens: the maps stop being inverses
+            occ = np.flatnonzero(st["slot2tok"] >= 0)[:2]
+            w = h.pool.meta[s2t_off:s2t_off + wl.slots * 4].view(torch.int32)
+            a, b = int(occ[0]), int(occ[1])
+            w[a], w[b] = int(st["slot2tok"][b]), int(st["slot2tok"][a])
+        else:                # the oldest and the newest order entries swap places
+            o = h.pool.meta[order_off:order_off + wl.slots * 2].view(torch.int16)
+            first, last = int(st["lru_order"][0]), int(st["lru_order"][-1])
+            o[0], o[wl.slots - 1] = last, first
+        torch.cuda.synchronize()
+        h.device_step(0, 0)   # the same Top-K again: every entry hits, nothing is evicted
+        assert h.pool.sync_status()[0] == kvs.KVS_ECORRUPT
+    finally:
+        h.close()

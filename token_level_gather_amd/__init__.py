@@ -22,6 +22,7 @@ KVS_EINVAL = -22
 KVS_ENOMEM = -12
 KVS_ERANGE = -34
 KVS_EDUP = -17
+KVS_ECORRUPT = -74
 KVS_EHIP_BASE = -1000
 
 HEADS, HEAD_DIM, V_DIM = 16, 576, 512
@@ -30,6 +31,7 @@ KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine")
 KVS_FLAG_HITS_FIRST = 1
 KVS_FLAG_PADDED_TOPK = 2
 KVS_FLAG_DIRECT_HOT = 4
+KVS_FLAG_CHECK = 8
 PROBE_SINK_WORDS = 65536
 
 # Every exported symbol of include/kvs.h.
@@ -294,7 +296,7 @@ class Pool:
         st = kvs_step_stats()
         rc = lib().kvs_sync_status(self.handle, _stream_ptr(stream, self.device),
                                    ctypes.byref(st))
-        if rc not in (KVS_OK, KVS_ERANGE, KVS_EDUP):
+        if rc not in (KVS_OK, KVS_ERANGE, KVS_EDUP, KVS_ECORRUPT):
             raise KvsError(rc, "kvs_sync_status")
         return rc, st
 

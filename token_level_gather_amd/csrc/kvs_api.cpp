@@ -33,7 +33,8 @@ int make_layout(const kvs_config* c, Layout* lay) {
   if (c->attn_splits < 0 || c->attn_splits > 64) return KVS_EINVAL;
   if (c->fetch_blocks < 0 || c->fetch_blocks > 65535) return KVS_EINVAL;
   if (c->hit_blocks < 0 || c->hit_blocks > 65535) return KVS_EINVAL;
-  if ((c->flags & ~(KVS_FLAG_HITS_FIRST | KVS_FLAG_PADDED_TOPK | KVS_FLAG_DIRECT_HOT)) != 0)
+  if ((c->flags & ~(KVS_FLAG_HITS_FIRST | KVS_FLAG_PADDED_TOPK | KVS_FLAG_DIRECT_HOT |
+                    KVS_FLAG_CHECK)) != 0)
     return KVS_EINVAL;
   if ((int64_t)c->batch * c->layers > 0x7fffffffLL) return KVS_EINVAL;
 
@@ -325,6 +326,8 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
   const DevPtrs& d = p->d;
   // lookup, sparse diff, LRU and map update for every request of the layer
   KVS_TRY_HIP(timed(p, KVS_KERNEL_DIFF_LRU, s, [&] { return launch_diff_lru(L, d, layer, topk, s); }));
+  // optional verification of the updated state (not timed)
+  if (L.flags & KVS_FLAG_CHECK) KVS_TRY_HIP(launch_check_state(L, d, layer, s));
   // index copy: misses over PCIe (fetch + write-back) and hits within HBM
   KVS_TRY_HIP(timed(p, KVS_KERNEL_GATHER, s, [&] { return launch_gather(L, d, layer, topk, s); }));
   // Top-K sparse attention over the compute buffer
@@ -530,6 +533,7 @@ const char* kvs_strerror(int code) {
     case KVS_ENOMEM: return "buffer smaller than kvs_query_sizes requires";
     case KVS_ERANGE: return "Top-K index or append position outside [0, context)";
     case KVS_EDUP: return "duplicate Top-K index within a request";
+    case KVS_ECORRUPT: return "state check failed: maps, LRU order or victims break an invariant";
     default: break;
   }
   if (code <= KVS_EHIP_BASE) return "HIP runtime error (KVS_EHIP_BASE - hipError_t)";

@@ -85,6 +85,7 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, cons
 hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
                           hipStream_t s);
 hipError_t launch_clear_status(const DevPtrs& d, hipStream_t s);
+hipError_t launch_check_state(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s);
 hipError_t launch_host_read_probe(const void* src, long long chunks, uint32_t* sink,
                                   hipStream_t s);
 hipError_t launch_append(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* rows,

@@ -827,6 +827,71 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
       (uint32_t)f32_to_bf16_rne(o2 * il) | ((uint32_t)f32_to_bf16_rne(o3 * il) << 16));
 }
 
+// ------------------------------------------------------------------ state check
+// KVS_FLAG_CHECK: after the diff of `layer`, workgroup b verifies unit
+// (b, layer): slot2tok and tok2slot are mutual inverses over all S slots and
+// all N tokens, the LRU order holds every slot once in strictly ascending
+// (last_used, slot) order (the order the victim choice relies on), and no
+// victim of this step is a hit slot of it.  A violation latches KVS_ECORRUPT.
+constexpr int kCheckThreads = 256;
+
+__global__ __launch_bounds__(kCheckThreads) void check_state_kernel(
+    const int32_t* __restrict__ tok2slot, const int32_t* __restrict__ slot2tok,
+    const int32_t* __restrict__ last_used, const uint16_t* __restrict__ order,
+    const int32_t* __restrict__ slot_of, const int32_t* __restrict__ victims,
+    const int32_t* __restrict__ counts, int32_t* status, long long N, int S, int K, int L,
+    int layer) {
+  extern __shared__ unsigned hitbits[];   // one bit per slot: hit slots of this step
+  __shared__ int bad;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (counts[4 * b + 3] == 0) return;     // invalid input: the unit was left untouched
+  const long long u = (long long)b * L + layer;
+  const int32_t* t2s = tok2slot + u * N;
+  const int32_t* s2t = slot2tok + u * S;
+  const int32_t* lu = last_used + u * S;
+  const uint16_t* ord = order + u * S;
+  const long long bk = (long long)b * K;
+  for (int w = tid; w < (S + 31) / 32; w += kCheckThreads) hitbits[w] = 0u;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  int err = 0;
+  for (int s = tid; s < S; s += kCheckThreads) {          // slot -> token -> slot
+    const int t = s2t[s];
+    if (t < -1 || (t >= 0 && ((long long)t >= N || t2s[t] != s))) err = 1;
+  }
+  for (long long t = tid; t < N; t += kCheckThreads) {    // token -> slot -> token
+    const int s = t2s[t];
+    if (s < -1 || (s >= 0 && (s >= S || s2t[s] != (int)t))) err = 1;
+  }
+  for (int p = tid; p < S; p += kCheckThreads) {          // order: sorted permutation
+    const int s = ord[p];
+    if (s >= S) {
+      err = 1;
+    } else if (p + 1 < S) {
+      const int s2 = ord[p + 1];
+      if (s2 >= S) {
+        err = 1;
+      } else {
+        const int a = lu[s], c = lu[s2];
+        if (!(a < c || (a == c && s < s2))) err = 1;
+      }
+    }
+  }
+  for (int i = tid; i < K; i += kCheckThreads) {
+    const int s = slot_of[bk + i];
+    if (s >= 0 && s < S) atomicOr(&hitbits[s >> 5], 1u << (s & 31));
+  }
+  __syncthreads();
+  const int m = counts[4 * b + 1];
+  for (int j = tid; j < m; j += kCheckThreads) {           // victims are not hit slots
+    const int v = victims[bk + j];
+    if (v < 0 || v >= S || ((hitbits[v >> 5] >> (v & 31)) & 1u)) err = 1;
+  }
+  if (err) atomicOr(&bad, 1);
+  __syncthreads();
+  if (tid == 0 && bad) atomicCAS(status, 0, KVS_ECORRUPT);
+}
+
 // ------------------------------------------------------------------ append
 // Lifecycle "publish" of one decode step's new rows: workgroup b writes row b
 // of `rows` into the host pool at (b, layer, pos[b]) (PCIe writes to the
@@ -1050,6 +1115,14 @@ hipError_t launch_append(const Layout& lay, const DevPtrs& d, int layer, const u
                      reinterpret_cast<u32x4*>(const_cast<uint16_t*>(d.pool)),
                      reinterpret_cast<u32x4*>(d.hot), d.tok2slot, d.status, (long long)lay.N,
                      lay.S, lay.L, layer);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_state(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s) {
+  const size_t lds = (size_t)((lay.S + 31) / 32) * 4;
+  hipLaunchKernelGGL(check_state_kernel, dim3(lay.B), dim3(kCheckThreads), lds, s, d.tok2slot,
+                     d.slot2tok, d.last_used, d.order, d.slot_of, d.victims, d.counts, d.status,
+                     (long long)lay.N, lay.S, lay.K, lay.L, layer);
   return hipGetLastError();
 }
 
