@@ -15,7 +15,9 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvs.so")
+# KVS_LIB selects another build of the same library (e.g. the host-sanitizer
+# build of the CPU tests); the default is the in-tree libkvs.so
+LIB_PATH = os.environ.get("KVS_LIB") or os.path.join(HERE, "libkvs.so")
 
 KVS_OK = 0
 KVS_EINVAL = -22

@@ -4,6 +4,16 @@ Compiles the gfx950 kernels and the C-ABI host runtime into
 ``token_level_gather_amd/libkvs.so`` with hipcc.  Every HIP translation unit
 gets ``-Xclang -target-feature -Xclang -packed-fp32-ops`` (no packed fp32 VALU
 instructions are emitted).
+
+``--host-sanitizers`` builds ``_build/hostsan/libkvs.so`` instead, with
+AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (each
+``-fsanitize`` behind ``-Xarch_host``; device code is built as usual), for
+running the CPU tests of the host runtime::
+
+    python -m token_level_gather_amd._build --host-sanitizers
+    LD_PRELOAD=$(hipcc --print-file-name=libclang_rt.asan-x86_64.so) \
+        ASAN_OPTIONS=detect_leaks=0 KVS_LIB=_build/hostsan/libkvs.so \
+        python -m pytest tests/test_abi.py
 """
 from __future__ import annotations
 
@@ -37,18 +47,28 @@ def compile_flags():
     ]
 
 
-def build(verbose: bool = False, out: str = LIB) -> str:
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+
+
+def build(verbose: bool = False, out: str = LIB, host_sanitizers: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
-    build_dir = os.path.join(ROOT, "_build")
+    build_dir = os.path.join(ROOT, "_build", "hostsan" if host_sanitizers else "")
     os.makedirs(build_dir, exist_ok=True)
+    if host_sanitizers and out == LIB:
+        out = os.path.join(build_dir, "libkvs.so")
+    extra = HOST_SANITIZE + ["-Xarch_host", "-fno-omit-frame-pointer", "-g"] \
+        if host_sanitizers else []
     objs = []
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc()] + compile_flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc()] + compile_flags() + extra + ["-x", "hip", "-c", os.path.join(CSRC, src),
+                                                     "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
     tmp = out + ".tmp"
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    link = HOST_SANITIZE if host_sanitizers else []
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + link + ["-o", tmp] + objs,
+         verbose)
     os.replace(tmp, out)
     return out
 
@@ -66,4 +86,4 @@ def _run(cmd, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, host_sanitizers="--host-sanitizers" in sys.argv))
