@@ -67,8 +67,8 @@ def build(verbose: bool = False, out: str = LIB, host_sanitizers: bool = False) 
         objs.append(obj)
     tmp = out + ".tmp"
     link = HOST_SANITIZE if host_sanitizers else []
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + link + ["-o", tmp] + objs,
-         verbose)
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + link + ["-o", tmp] + objs
+         + ["-lrocprofiler-sdk-roctx"], verbose)
     os.replace(tmp, out)
     return out
 

@@ -7,10 +7,13 @@
 // publish = kvs_publish, fetch + write-back = kvs_step, free = kvs_free_request.
 #include <math.h>
 #include <stdlib.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <new>
 #include <vector>
+
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include "kvs_internal.h"
 
@@ -121,6 +124,7 @@ struct kvs_pool {
   int prof_steps;    // kvs_step calls recorded
   int prof_max_steps;
   uint32_t prof_mask;  // kernels recorded (1 << KVS_KERNEL_*)
+  bool roctx;          // KVS_ROCTX=1 at creation: a named range around every kvs_step
 };
 
 static int hip_err(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP_BASE - (int)e; }
@@ -249,6 +253,8 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
   p->prof_steps = 0;
   p->prof_max_steps = 0;
   p->host_pool = (uint8_t*)const_cast<void*>(bufs->host_pool);
+  const char* rx = getenv("KVS_ROCTX");
+  p->roctx = rx != nullptr && rx[0] == '1';
 
   uint8_t* meta = (uint8_t*)bufs->meta;
   uint8_t* scr = (uint8_t*)bufs->scratch;
@@ -324,6 +330,19 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
   KVS_TRY(check_device(p, s));
   const Layout& L = p->lay;
   const DevPtrs& d = p->d;
+  // a host-side range for rocprofv3 --marker-trace (enqueue time, not GPU time)
+  struct Range {
+    bool on;
+    Range(bool enable, int layer) : on(enable) {
+      if (!on) return;
+      char name[32];
+      snprintf(name, sizeof(name), "kvs_step layer %d", layer);
+      roctxRangePushA(name);
+    }
+    ~Range() {
+      if (on) roctxRangePop();
+    }
+  } range(p->roctx, layer);
   // lookup, sparse diff, LRU and map update for every request of the layer
   KVS_TRY_HIP(timed(p, KVS_KERNEL_DIFF_LRU, s, [&] { return launch_diff_lru(L, d, layer, topk, s); }));
   // optional verification of the updated state (not timed)
