@@ -622,3 +622,33 @@ def test_state_check_catches_corruption(what):
         assert h.pool.sync_status()[0] == kvs.KVS_ECORRUPT
     finally:
         h.close()
+
+
+# ---------------------------------------------------------------- random small configurations
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_small_configs_every_unit(seed):
+    # seeded draws of shape, miss rate, padding, direct mode, split count and
+    # workgroup order; every unit checked against the oracle after every step
+    import token_level_gather_amd as kvs
+    rng = np.random.default_rng(9000 + seed)
+    K = int(rng.choice([1, 7, 64, 65, 200, 513, 1024]))
+    S = int(K + rng.integers(0, 3 * K + 64))
+    S = min(S, 16384)   # the slot limit
+    N = int(max(S, K) + rng.integers(0, 4000))
+    B = int(rng.integers(1, 6))
+    L = int(rng.integers(1, 3))
+    ntiles = (K + 63) // 64
+    splits = int(rng.integers(1, min(ntiles, 64) + 1)) if rng.random() < 0.5 else 0
+    flags = 0
+    if rng.random() < 0.5:
+        flags |= kvs.KVS_FLAG_DIRECT_HOT
+    if rng.random() < 0.3:
+        flags |= kvs.KVS_FLAG_HITS_FIRST
+    padded = bool(rng.random() < 0.4)
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(
+        name=f"rand{seed}", batch=B, layers=L, context=N, slots=S, topk=K, steps=4,
+        fresh_rate=float(rng.choice([0.0, 0.2, 0.6, 1.0])), seed=20261300 + seed)
+    print(f"random config {seed}: B={B} L={L} N={N} S={S} K={K} splits={splits} "
+          f"flags={flags} padded={padded} fresh={wl.fresh_rate}", flush=True)
+    _case(wl, wl.steps, range(B), padded=padded, flags=flags, attn_splits=splits)
