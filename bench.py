@@ -291,7 +291,9 @@ def main():
     tokens_per_step = B * L * K
     value = tokens_per_step / (ms_step * 1e-3)
     splits = pool.sizes.attn_splits
-    part_bytes = B * splits * 16 * (512 + 2) * 4
+    # split partials (written by attention, read by the combine); with one
+    # split the attention writes the bf16 output itself and no combine runs
+    part_bytes = B * splits * 16 * (512 + 2) * 4 if splits > 1 else B * 16 * 512 * 2
 
     def algorithmic(hit_l, miss_l):
         """Algorithmic bytes (and flops) of one kvs_step call, per kernel.
@@ -309,7 +311,8 @@ def main():
             "attention": {"bound": "hbm",
                           "bytes": B * (K * ROW + 16 * 576 * 2) + part_bytes + attn_idx,
                           "flop": B * 2 * 16 * K * (576 + 512)},
-            "combine": {"bound": "hbm", "bytes": part_bytes + B * 16 * 512 * 2},
+            "combine": {"bound": "hbm",
+                        "bytes": part_bytes + B * 16 * 512 * 2 if splits > 1 else 0},
         }
 
     def kernel_stats(kt, alg, names):

@@ -652,3 +652,34 @@ def test_random_small_configs_every_unit(seed):
     print(f"random config {seed}: B={B} L={L} N={N} S={S} K={K} splits={splits} "
           f"flags={flags} padded={padded} fresh={wl.fresh_rate}", flush=True)
     _case(wl, wl.steps, range(B), padded=padded, flags=flags, attn_splits=splits)
+
+
+@pytest.mark.parametrize("direct", [False, True])
+def test_invalid_topk_single_split_writes_zero_output(direct):
+    # one split: the attention writes out / lse itself (no combine), also for a
+    # request whose Top-K is rejected
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(batch=3, context=3000, slots=500, topk=200,
+                                                  steps=4)
+    h = Harness(wl, wl.steps, range(3), attn_splits=1, flags=_direct() if direct else 0)
+    try:
+        assert h.pool.sizes.attn_splits == 1
+        for t in range(2):
+            h.check(t, 0, *h.device_step(t, 0))
+        bad = h.topk[2, 0].copy()
+        bad[1, 5] = wl.context
+        h.out.fill_(1.0)
+        h.lse.fill_(1.0)
+        h.device_step(2, 0, topk=bad)
+        assert h.pool.sync_status()[0] == kvs.KVS_ERANGE
+        assert not torch.any(h.out[1].float() != 0).item()
+        assert torch.isinf(h.lse[1]).all().item() and (h.lse[1] < 0).all().item()
+        for b in (0, 2):   # the valid requests were finished by the attention itself
+            rec = h.oracle[(b, 0)].step(bad[b], h.pool.host.array[b, 0], h.q[b], wl.scale)
+            got = _bf16_to_f64(_u16(h.out)[b])
+            assert np.abs(got - rec.out).max() <= MAX_ABS
+        h.check_reqs = [1]
+        h.check(3, 0, *h.device_step(3, 0))
+    finally:
+        h.close()

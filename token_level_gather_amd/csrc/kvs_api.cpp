@@ -23,6 +23,10 @@ static uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 // Attention workgroups resident at once: one per compute unit of an MI355X.
 constexpr int kAttnWorkgroupsPerRound = 256;
+// A workgroup's start-up (its first two tiles arriving during the all-CU
+// burst), in tile-times: fitted to measured split sweeps at 4, 32, 64 and 192
+// requests x 2048 selected tokens.
+constexpr int kAttnStartupTiles = 4;
 
 int make_layout(const kvs_config* c, Layout* lay) {
   if (c == nullptr || lay == nullptr) return KVS_EINVAL;
@@ -47,15 +51,16 @@ int make_layout(const kvs_config* c, Layout* lay) {
   int splits = c->attn_splits;
   if (splits == 0) {
     // An attention workgroup holds one CU (its LDS tile), so a launch runs in
-    // rounds of 256 workgroups.  Pick the split count with the fewest
-    // tile-times: rounds x tiles per split; ties go to fewer splits (less to
-    // merge).
+    // rounds of 256 workgroups, and every workgroup first waits for its first
+    // two tiles.  Pick the split count with the fewest tile-times, rounds x
+    // (tiles per split + that start-up); ties go to fewer splits (less to
+    // merge; one split needs no merge at all).
     long long best = -1;
     const int max_s = ntiles < 64 ? ntiles : 64;
     for (int sp = 1; sp <= max_s; ++sp) {
       const long long rounds = ((long long)B * sp + kAttnWorkgroupsPerRound - 1) /
                                kAttnWorkgroupsPerRound;
-      const long long cost = rounds * ((ntiles + sp - 1) / sp);
+      const long long cost = rounds * ((ntiles + sp - 1) / sp + kAttnStartupTiles);
       if (best < 0 || cost < best) {
         best = cost;
         splits = sp;
@@ -351,10 +356,12 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
   KVS_TRY_HIP(timed(p, KVS_KERNEL_GATHER, s, [&] { return launch_gather(L, d, layer, topk, s); }));
   // Top-K sparse attention over the compute buffer
   KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s, [&] {
-    return launch_attention(L, d, layer, (const uint16_t*)q, p->cfg.scale, s);
+    return launch_attention(L, d, layer, (const uint16_t*)q, p->cfg.scale, (uint16_t*)out, lse,
+                            s);
   }));
-  KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
-                    [&] { return launch_combine(L, d, (uint16_t*)out, lse, s); }));
+  if (L.splits > 1)
+    KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
+                      [&] { return launch_combine(L, d, (uint16_t*)out, lse, s); }));
   if (p->prof_steps < p->prof_max_steps) ++p->prof_steps;
   return KVS_OK;
 }

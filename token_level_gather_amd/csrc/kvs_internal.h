@@ -80,8 +80,9 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer,
                            const int32_t* topk, hipStream_t s);
 hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
                          hipStream_t s);
+// With a single split the attention writes out / lse itself and no combine runs.
 hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* q,
-                            float scale, hipStream_t s);
+                            float scale, uint16_t* out, float* lse, hipStream_t s);
 hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
                           hipStream_t s);
 hipError_t launch_clear_status(const DevPtrs& d, hipStream_t s);

@@ -528,6 +528,8 @@ struct AttnArgs {
   int K, splits, S, L, layer;
   int padded;               // 1: mask the empty entries of a padded Top-K
   float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units
+  uint16_t* out;            // [B][16][512] bf16 when splits == 1 (no combine), else null
+  float* lse;               // [B][16] or null; written here only when out is
 };
 
 // One workgroup = (split sp, request b): the tiles [tb, te) of request b's
@@ -554,8 +556,17 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) int vmark[kTile];   // the tile's empty-entry marks
 
   const int b = blockIdx.y, sp = blockIdx.x;
-  // invalid input, or no entry at all (padded): combine writes the zero output
-  if (a.counts[4 * b + 3] == 0 || a.counts[4 * b + 0] + a.counts[4 * b + 1] == 0) return;
+  // invalid input, or no entry at all (padded): zero output, lse -inf (written
+  // here with a single split, by the combine otherwise)
+  if (a.counts[4 * b + 3] == 0 || a.counts[4 * b + 0] + a.counts[4 * b + 1] == 0) {
+    if (a.out != nullptr) {
+      u32x4* ob = reinterpret_cast<u32x4*>(a.out + (long long)b * kHeads * kVDim);
+      for (int i = threadIdx.x; i < kHeads * kVDim / 8; i += kAttnThreads)
+        ob[i] = u32x4{0u, 0u, 0u, 0u};
+      if (a.lse != nullptr && threadIdx.x < kHeads) a.lse[b * kHeads + threadIdx.x] = -INFINITY;
+    }
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int tt = wave & 3, kh = wave >> 2;
@@ -758,7 +769,29 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     if (tile < te) compute(tile);   // odd tile count: LDS holds the last tile
   }
 
-  // partials: acc lane holds O[h = 4g + j][e = 64w + 16nt + r16]
+  // acc lane holds O[h = 4g + j][e = 64w + 16nt + r16]
+  if (a.out != nullptr) {
+    // single split: this workgroup saw every token, so it finishes the request
+    // with the combine's arithmetic (weight 2^(m - m) = 1): out = O / l,
+    // lse = (m + log2 l) ln 2
+    __shared__ float inv_l[kHeads];
+    if (sm_on && (tid & 15) == 0) {
+      const int h = tid >> 4;
+      inv_l[h] = 1.f / l_run;
+      if (a.lse != nullptr) a.lse[b * kHeads + h] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    }
+    __syncthreads();
+    uint16_t* ob = a.out + (long long)b * kHeads * kVDim;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ob[(4 * g + j) * kVDim + wave * 64 + nt * 16 + r16] =
+            f32_to_bf16_rne((0.f + acc[nt][j]) * inv_l[4 * g + j]);   // 0 + x: the
+                                                                      // combine's zero sign
+    return;
+  }
+  // partials for the combine
   const long long part = (long long)b * a.splits + sp;
   float* po = a.part_o + part * kHeads * kVDim;
 #pragma unroll
@@ -1083,7 +1116,7 @@ hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const i
 }
 
 hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* q,
-                            float scale, hipStream_t s) {
+                            float scale, uint16_t* out, float* lse, hipStream_t s) {
   AttnArgs a;
   a.cbuf = d.cbuf;
   a.hot = d.hot;
@@ -1099,6 +1132,8 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, cons
   a.L = lay.L;
   a.layer = layer;
   a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
+  a.out = lay.splits == 1 ? out : nullptr;
+  a.lse = lay.splits == 1 ? lse : nullptr;
   const bool direct = (lay.flags & KVS_FLAG_DIRECT_HOT) != 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   if (direct)
