@@ -65,7 +65,8 @@ extern "C" {
 #define KVS_ENOMEM (-12)    /* a caller buffer is smaller than kvs_query_sizes asks */
 #define KVS_ERANGE (-34)    /* device saw a Top-K index outside [0, N) */
 #define KVS_EDUP (-17)      /* device saw a repeated Top-K index within one request */
-#define KVS_ECORRUPT (-74)  /* KVS_FLAG_CHECK found a unit whose state breaks an invariant */
+#define KVS_ECORRUPT (-74)  /* a unit's state breaks an invariant: a token-to-slot entry
+                               outside [-1, S) seen by a step, or a KVS_FLAG_CHECK failure */
 #define KVS_EHIP_BASE (-1000) /* KVS_EHIP_BASE - e: HIP runtime error e */
 
 /* ---- limits ------------------------------------------------------------ */
@@ -219,7 +220,14 @@ int kvs_host_free(void* ptr);
 
 /* Create a pool over caller buffers and initialise its state on `stream`:
  * every unit empty (maps -1, last_used -1, LRU order 0..S-1), step counters,
- * stats and status 0.  Does not synchronise. */
+ * stats and status 0.  Does not synchronise.
+ * Checked first, with no GPU work: the configuration (KVS_EINVAL), NULL
+ * buffers (KVS_EINVAL), stated capacities (KVS_ENOMEM) and alignment (hot and
+ * cbuf 16 bytes, meta and scratch 256 bytes; KVS_EINVAL).  Then, through the
+ * HIP runtime: host_pool must be pinned and GPU-mapped, and hot, meta, scratch
+ * and cbuf must be device memory of the current device (KVS_EINVAL), each
+ * allocation reaching at least kvs_query_sizes' bytes past the pointer
+ * (KVS_ENOMEM). */
 int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream,
                     kvs_pool** out);
 
@@ -256,16 +264,22 @@ int kvs_append(kvs_pool* pool, int32_t layer, const void* rows, const int64_t* p
                void* stream);
 
 /* Lifecycle "fetch + write-back" and the Top-K attention of one layer for all
- * B requests: four kernel launches on `stream`, no host synchronisation, no
- * device-to-host copy, no other stream.
- *   topk [B][K] int32, device: request b's Top-K token indices, unique, in [0, N)
- *        (with KVS_FLAG_PADDED_TOPK also -1 = empty entry; see there).
- *   q    [B][16][576] bf16, device: queries.
- *   out  [B][16][512] bf16, device: attention output.
- *   lse  [B][16] fp32, device, or NULL: natural-log log-sum-exp of the scores.
+ * B requests: kernel launches on `stream` only (diff, gather, attention, and a
+ * merge of the attention's token splits when kvs_sizes.attn_splits > 1), no
+ * host synchronisation, no device-to-host copy, no other stream.
+ *   topk [B][K] int32, device, 4-byte aligned: request b's Top-K token indices,
+ *        unique, in [0, N) (with KVS_FLAG_PADDED_TOPK also -1 = empty entry).
+ *   q    [B][16][576] bf16, device, 16-byte aligned: queries.
+ *   out  [B][16][512] bf16, device, 16-byte aligned: attention output.
+ *   lse  [B][16] fp32, device, 4-byte aligned, or NULL: natural-log
+ *        log-sum-exp of the scores.
+ * KVS_EINVAL (nothing enqueued) for a NULL or misaligned pointer, a bad layer
+ * or a stream of another device.
  * The compute buffer receives request b's rows at cbuf[b][i] = row of topk[b][i].
- * A request whose Top-K is invalid is skipped: its state is unchanged, its out
- * row is zero and its lse is -inf; the error is latched for kvs_sync_status.
+ * A request whose Top-K is invalid (KVS_ERANGE, KVS_EDUP), or whose map holds a
+ * slot outside [-1, S) for one of its tokens (KVS_ECORRUPT), is skipped: its
+ * state is unchanged, its out row is zero and its lse is -inf; the error is
+ * latched for kvs_sync_status.  Other requests proceed.
  * Calls for one layer must be in decode order; cbuf is reused by every call. */
 int kvs_step(kvs_pool* pool, int32_t layer, const int32_t* topk, const void* q,
              void* out, float* lse, void* stream);
@@ -275,7 +289,8 @@ int kvs_step(kvs_pool* pool, int32_t layer, const int32_t* topk, const void* q,
 int kvs_free_request(kvs_pool* pool, int32_t req, void* stream);
 
 /* Synchronise `stream`, then return the first device-detected error
- * (KVS_ERANGE / KVS_EDUP) since the last call, or KVS_OK, and clear it.
+ * (KVS_ERANGE / KVS_EDUP / KVS_ECORRUPT) since the last call, or KVS_OK, and
+ * clear it.
  * `stats` (may be NULL) receives the running totals. */
 int kvs_sync_status(kvs_pool* pool, void* stream, kvs_step_stats* stats);
 

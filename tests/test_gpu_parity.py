@@ -62,9 +62,10 @@ class Harness:
         if fill == "all":
             W.fill_pool(host, wl)
         else:   # only the checked requests need real rows; other units read whatever is there
-            for b in self.check_reqs:
-                for l in range(wl.layers):
-                    W.fill_unit_rows(host[b, l], wl, b, l)
+            from concurrent.futures import ThreadPoolExecutor
+            units = [(b, l) for b in self.check_reqs for l in range(wl.layers)]
+            with ThreadPoolExecutor(min(16, len(units))) as ex:
+                list(ex.map(lambda u: W.fill_unit_rows(host[u[0], u[1]], wl, u[0], u[1]), units))
         self.topk = W.topk_streams(wl, steps)
         if padded:
             self.topk = W.pad_topk_streams(self.topk, wl.seed)
@@ -74,6 +75,8 @@ class Harness:
         self.lse = torch.empty((wl.batch, 16), dtype=torch.float32, device="cuda")
         self.max_abs = 0.0
         self.max_rel = 0.0
+        # oracle totals over the checked units: unit steps, hits, misses, evictions
+        self.totals = np.zeros(4, dtype=np.int64)
 
     def device_step(self, t, l, topk=None):
         torch = _torch()
@@ -94,6 +97,7 @@ class Harness:
             rec = u.step(tk[b], self.pool.host.array[b, l], q[b], wl.scale, padded=self.padded)
             st = self.pool.read_state(b, l)
             n = rec.n_miss
+            self.totals += [1, rec.n_hit, n, int((rec.evicted >= 0).sum())]
             tag = f"step {t} layer {l} req {b}"
             assert st["counts"].tolist() == [rec.n_hit, n, int((rec.evicted >= 0).sum()), 1], tag
             assert np.array_equal(st["slot_of"], rec.slot_of), tag
@@ -137,7 +141,15 @@ class Harness:
                 self.check(t, l, tk, q)
         rc, stats = self.pool.sync_status()
         assert rc == 0
+        if sorted(self.check_reqs) == list(range(self.wl.batch)):
+            self.check_stats(stats)
         return stats
+
+    def check_stats(self, stats):
+        """The library's running totals equal the oracle's, summed over every unit."""
+        got = [stats.unit_steps, stats.hits, stats.misses, stats.evictions]
+        assert got == self.totals.tolist(), (got, self.totals.tolist())
+        assert stats.host_bytes == 1152 * int(self.totals[2])
 
     def close(self):
         self.pool.release()
@@ -173,6 +185,67 @@ def test_4k_context_single_request_all_steps():
 def test_small_shapes_every_unit(shape):
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="small", steps=6, **shape)
     _case(wl, wl.steps, range(wl.batch))
+
+
+# One shape per instantiation of the diff kernel's per-thread bounds (Top-K
+# entries per thread KPT, slots per thread SPT, each a power of two; 1024
+# threads): every (KPT, SPT) pair that some K <= S within the limits selects.
+# Each shape evicts occupied slots in at least two of its steps.
+DIFF_INSTANTIATIONS = {
+    # (KPT, SPT): (K, S, N, fresh rate, steps)
+    (1, 1): (1000, 1024, 6000, 0.5, 6),
+    (1, 2): (700, 2000, 9000, 1.0, 6),
+    (1, 4): (1024, 4000, 20000, 1.0, 7),
+    (1, 8): (1024, 5000, 40000, 1.0, 8),
+    (1, 16): (1024, 9500, 60000, 1.0, 12),
+    (2, 2): (2048, 2048, 9000, 0.3, 5),
+    (2, 4): (1500, 3000, 12000, 0.8, 5),
+    (2, 8): (2048, 8192, 40000, 1.0, 7),
+    (2, 16): (2048, 12000, 50000, 1.0, 9),
+    (4, 4): (4096, 4096, 20000, 0.3, 5),
+    (4, 8): (3000, 6000, 20000, 0.6, 6),
+    (4, 16): (4096, 16384, 60000, 1.0, 7),
+    (8, 8): (8192, 8192, 30000, 0.2, 5),
+    (8, 16): (6000, 16000, 60000, 0.8, 6),
+}
+
+
+def _per_thread(n):
+    x = (n + 1023) // 1024
+    p = 1
+    while p < x:
+        p *= 2
+    return p
+
+
+def test_diff_instantiation_table_covers_every_pair():
+    # every (KPT, SPT) pair reachable under the limits K <= S <= 16384, K <= 8192
+    reach = {(_per_thread(k), _per_thread(s)) for k in range(1, 8193, 97)
+             for s in range(k, 16385, 89)} | {(8, 16), (8, 8)}
+    assert reach == set(DIFF_INSTANTIATIONS)
+    for (kpt, spt), (k, s, n, f, steps) in DIFF_INSTANTIATIONS.items():
+        assert (_per_thread(k), _per_thread(s)) == (kpt, spt) and k <= s <= n
+
+
+@pytest.mark.parametrize("inst", sorted(DIFF_INSTANTIATIONS), ids=lambda x: f"kpt{x[0]}_spt{x[1]}")
+def test_diff_every_instantiation_evicts(inst):
+    K, S, N, f, steps = DIFF_INSTANTIATIONS[inst]
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name=f"inst{inst[0]}x{inst[1]}", batch=2,
+                                                  layers=1, context=N, slots=S, topk=K,
+                                                  steps=steps, fresh_rate=f)
+    _, stats = _case(wl, wl.steps, range(wl.batch))
+    assert stats.evictions > 0
+
+
+@pytest.mark.parametrize("mode", ["default", "direct", "padded"])
+def test_topk_3000_slots_6000_every_unit(mode):
+    # 2048 < K <= 4096 and 4096 < S <= 8192, with evictions from the third step
+    import token_level_gather_amd as kvs
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="k3000", batch=3, layers=2, context=20000,
+                                                  slots=6000, topk=3000, steps=8, fresh_rate=0.4)
+    flags = kvs.KVS_FLAG_DIRECT_HOT if mode == "direct" else 0
+    _, stats = _case(wl, wl.steps, range(wl.batch), padded=mode == "padded", flags=flags)
+    assert stats.evictions > 0
 
 
 @pytest.mark.parametrize("topk,splits", [
@@ -325,12 +398,16 @@ def test_full_size_16k_direct_hot_sampled():
 
 
 @pytest.mark.parametrize("name,reqs,steps", [
-    ("ctx128k_b32_l8_zipf", [0, 31], 6),
-    ("ctx1m_b4_l4", [3], 6),
+    ("ctx128k_b32_l8_zipf", [0, 31], 16),   # every step; evictions from step ~7
+    # the workload's 16 steps plus 8: with 8192 slots and ~410 fresh tokens a
+    # step, occupied slots are first evicted at step 15
+    ("ctx1m_b4_l4", [0, 3], 24),
 ])
 def test_full_size_long_context_sampled(name, reqs, steps):
     wl = W.WORKLOADS[name]
-    _case(wl, steps, reqs, fill="checked")
+    h, stats = _case(wl, steps, reqs, fill="checked")
+    assert h.totals[3] > 0, "the sampled units never evicted an occupied slot"
+    assert stats.evictions > 0
 
 
 def test_publish_rows_then_fetch():
@@ -626,15 +703,15 @@ def test_state_check_catches_corruption(what):
 
 # ---------------------------------------------------------------- random small configurations
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_small_configs_every_unit(seed):
     # seeded draws of shape, miss rate, padding, direct mode, split count and
     # workgroup order; every unit checked against the oracle after every step
     import token_level_gather_amd as kvs
     rng = np.random.default_rng(9000 + seed)
-    K = int(rng.choice([1, 7, 64, 65, 200, 513, 1024]))
+    K = int(rng.choice([1, 7, 64, 65, 200, 513, 1024, 3000, 4096]))
     S = int(K + rng.integers(0, 3 * K + 64))
-    S = min(S, 16384)   # the slot limit
+    S = min(S, 8192 if K > 1024 else 16384)   # the slot limit; large K stays under 8192
     N = int(max(S, K) + rng.integers(0, 4000))
     B = int(rng.integers(1, 6))
     L = int(rng.integers(1, 3))
@@ -681,5 +758,146 @@ def test_invalid_topk_single_split_writes_zero_output(direct):
             assert np.abs(got - rec.out).max() <= MAX_ABS
         h.check_reqs = [1]
         h.check(3, 0, *h.device_step(3, 0))
+    finally:
+        h.close()
+
+
+# ---------------------------------------------------------------- host-checked arguments
+
+def test_step_rejects_misaligned_pointers_before_any_work():
+    # q and out are accessed in 16-byte vectors, topk and lse as 4-byte words:
+    # a misaligned pointer is rejected on the host and nothing is enqueued
+    import ctypes
+
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(batch=2, context=3000, slots=500, topk=200,
+                                                  steps=2)
+    h = Harness(wl, wl.steps, range(2))
+    try:
+        lib = kvs.lib()
+        B, K = wl.batch, wl.topk
+        tk = torch.from_numpy(h.topk[0, 0]).cuda()
+        q = torch.from_numpy(W.queries(wl, 0, 0).view(np.int16)).cuda()
+        raw_tk = torch.empty(B * K + 4, dtype=torch.int32, device="cuda")
+        raw_tk[1:1 + B * K].copy_(tk.view(-1))
+        raw_q = torch.empty(B * 16 * 576 * 2 + 64, dtype=torch.uint8, device="cuda")
+        raw_out = torch.empty(B * 16 * 512 * 2 + 64, dtype=torch.uint8, device="cuda")
+        raw_lse = torch.empty(B * 16 * 4 + 64, dtype=torch.uint8, device="cuda")
+        s = torch.cuda.current_stream().cuda_stream
+        good = (tk.data_ptr(), q.data_ptr(), h.out.data_ptr(), h.lse.data_ptr())
+        bad_cases = {
+            "topk+4 is aligned": None,
+            "topk+2": (tk.data_ptr() + 2, good[1], good[2], good[3]),
+            "q+8": (good[0], raw_q.data_ptr() + 8, good[2], good[3]),
+            "q+2": (good[0], raw_q.data_ptr() + 2, good[2], good[3]),
+            "out+8": (good[0], good[1], raw_out.data_ptr() + 8, good[3]),
+            "out+2": (good[0], good[1], raw_out.data_ptr() + 2, good[3]),
+            "lse+2": (good[0], good[1], good[2], raw_lse.data_ptr() + 2),
+        }
+        for name, args in bad_cases.items():
+            if args is None:
+                continue
+            rc = lib.kvs_step(h.pool.handle, 0, args[0], args[1], args[2], args[3], s)
+            assert rc == kvs.KVS_EINVAL, name
+            g = ctypes.c_void_p()
+            rc = lib.kvs_graph_capture(h.pool.handle, 0, args[0], args[1], args[2], args[3],
+                                       ctypes.byref(g))
+            assert rc == kvs.KVS_EINVAL and g.value is None, name
+        torch.cuda.synchronize()
+        assert h.pool.read_state(0, 0)["step"] == 0, "a rejected call enqueued work"
+        # an offset that keeps the alignment is accepted: topk at +4 bytes
+        rc = lib.kvs_step(h.pool.handle, 0, raw_tk.data_ptr() + 4, good[1], good[2], good[3], s)
+        assert rc == kvs.KVS_OK
+        torch.cuda.synchronize()
+        assert h.pool.sync_status()[0] == 0
+        h.check_reqs = [0, 1]
+        rec = h.oracle[(0, 0)].step(h.topk[0, 0, 0], h.pool.host.array[0, 0])
+        assert np.array_equal(h.pool.read_state(0, 0)["slot2tok"], h.oracle[(0, 0)].slot2tok)
+        assert rec.t == 0
+    finally:
+        h.close()
+
+
+def test_create_pool_rejects_host_memory_and_short_allocations():
+    import ctypes
+
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    lib = kvs.lib()
+    cfg = kvs.make_config(batch=1, layers=1, context=4096, slots=512, topk=256)
+    sz = kvs.query_sizes(cfg)
+    host = kvs.HostPool(1, 1, 4096)
+    try:
+        def dev(n):
+            return torch.empty(int(n) + 256, dtype=torch.uint8, device="cuda")
+        hot, meta, cbuf, scr = dev(sz.hot_bytes), dev(sz.meta_bytes), dev(sz.cbuf_bytes), \
+            dev(sz.scratch_bytes)
+        ok = [host.ptr, hot.data_ptr(), meta.data_ptr(), cbuf.data_ptr(), scr.data_ptr()]
+        caps = [host.nbytes, hot.numel(), meta.numel(), cbuf.numel(), scr.numel()]
+        s = torch.cuda.current_stream().cuda_stream
+
+        def create(ptrs, capacity):
+            handle = ctypes.c_void_p()
+            bufs = kvs.kvs_buffers(*ptrs, *capacity)
+            rc = lib.kvs_create_pool(ctypes.byref(cfg), ctypes.byref(bufs), s,
+                                     ctypes.byref(handle))
+            if rc == kvs.KVS_OK:
+                assert lib.kvs_release(handle) == kvs.KVS_OK
+            else:
+                assert handle.value is None
+            return rc
+
+        assert create(ok, caps) == kvs.KVS_OK
+        # pinned host memory (GPU-addressable, but not device memory) as a device buffer
+        for i in (1, 2, 3, 4):
+            ptrs = list(ok)
+            ptrs[i] = host.ptr
+            assert create(ptrs, caps) == kvs.KVS_EINVAL, i
+        # a device pointer 4 KiB before the end of its allocation (the caching
+        # allocator's segment, one hipMalloc): the pool's hot buffer does not fit
+        seg = next(sg for sg in torch.cuda.memory_snapshot()
+                   if sg["address"] <= hot.data_ptr() < sg["address"] + sg["total_size"])
+        near_end = seg["address"] + seg["total_size"] - 4096
+        ptrs = list(ok)
+        ptrs[1] = near_end
+        assert create(ptrs, caps) == kvs.KVS_ENOMEM
+    finally:
+        host.free()
+
+
+@pytest.mark.parametrize("bad_slot", ["past_end", "below_minus_one"])
+def test_corrupt_map_entry_latches_ecorrupt(bad_slot):
+    # a token-to-slot entry no step can write (>= S, or < -1) is reported as
+    # corrupted state; that request is skipped (state unchanged, zero output),
+    # the others take the step
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="corrupt_slot", batch=3, context=3000,
+                                                  slots=500, topk=200, steps=4, fresh_rate=0.3)
+    h = Harness(wl, wl.steps, range(3))
+    try:
+        for t in range(2):
+            h.check(t, 0, *h.device_step(t, 0))
+        assert h.pool.sync_status()[0] == 0
+        before = h.pool.read_state(1, 0)
+        # a token of the next step's Top-K for request 1 (unit 1 * L + 0)
+        tok = int(h.topk[2, 0, 1, 7])
+        value = wl.slots + 3 if bad_slot == "past_end" else -5
+        t2s = h.pool.meta[:3 * wl.context * 4].view(torch.int32)   # tok2slot [U][N] comes first
+        t2s[1 * wl.context + tok] = value
+        torch.cuda.synchronize()
+        h.device_step(2, 0)
+        assert h.pool.sync_status()[0] == kvs.KVS_ECORRUPT
+        after = h.pool.read_state(1, 0)
+        for key in ("slot2tok", "last_used", "lru_order", "step"):
+            assert np.array_equal(np.asarray(before[key]), np.asarray(after[key])), key
+        assert after["tok2slot"][tok] == value
+        assert after["counts"][3] == 0
+        assert not torch.any(h.out[1].float() != 0).item()
+        for b in (0, 2):
+            h.oracle[(b, 0)].step(h.topk[2, 0, b], h.pool.host.array[b, 0])
+            assert np.array_equal(h.pool.read_state(b, 0)["slot2tok"], h.oracle[(b, 0)].slot2tok)
+        assert h.pool.sync_status()[0] == 0
     finally:
         h.close()

@@ -1,7 +1,7 @@
 // Host runtime behind the C ABI in include/kvs.h: configuration and buffer
 // validation, host-pool allocation, launch orchestration of one decode step
-// (four kernels on the caller's stream), status and statistics readback, and
-// per-kernel event timing.
+// (three or four kernels on the caller's stream), status and statistics
+// readback, and per-kernel event timing.
 //
 // The request lifecycle follows "XM-Sparse" (HiSparse integration section):
 // publish = kvs_publish, fetch + write-back = kvs_step, free = kvs_free_request.
@@ -163,6 +163,38 @@ static int check_device(const kvs_pool* p, hipStream_t s) {
     if (rc_ != KVS_OK) return rc_; \
   } while (0)
 
+// Pointer arguments of one step: the kernels read q in 16-byte vectors, write
+// out in 16-byte (empty request), 8-byte (merge) and 2-byte stores, and read
+// topk and write lse as 4-byte words.  A misaligned pointer is rejected here
+// instead of faulting the GPU.
+static int check_step_args(const int32_t* topk, const void* q, const void* out,
+                           const float* lse) {
+  if (topk == nullptr || q == nullptr || out == nullptr) return KVS_EINVAL;
+  if (((uintptr_t)q & 15) != 0 || ((uintptr_t)out & 15) != 0) return KVS_EINVAL;
+  if (((uintptr_t)topk & 3) != 0 || ((uintptr_t)lse & 3) != 0) return KVS_EINVAL;
+  return KVS_OK;
+}
+
+// `ptr` must be device memory of `device` with at least `bytes` from `ptr` to
+// the end of its allocation.
+static int check_device_buffer(const void* ptr, uint64_t bytes, int device) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return KVS_EINVAL;
+  }
+  if (at.type != hipMemoryTypeDevice || at.device != device) return KVS_EINVAL;
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return KVS_EINVAL;
+  }
+  const uintptr_t end = (uintptr_t)base + size;
+  if ((uintptr_t)ptr < (uintptr_t)base || (uintptr_t)ptr + bytes > end) return KVS_ENOMEM;
+  return KVS_OK;
+}
+
 // Launch `fn` on `s`, bracketed by timing events when profiling.
 template <typename F>
 static hipError_t timed(kvs_pool* p, int kernel, hipStream_t s, F fn) {
@@ -248,6 +280,14 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
     (void)hipGetLastError();
     return KVS_EINVAL;
   }
+  // the device buffers must be device memory of the current device, each
+  // allocation large enough for the capacity the caller states
+  int device = -1;
+  KVS_TRY_HIP(hipGetDevice(&device));
+  KVS_TRY(check_device_buffer(bufs->hot, need.hot_bytes, device));
+  KVS_TRY(check_device_buffer(bufs->meta, need.meta_bytes, device));
+  KVS_TRY(check_device_buffer(bufs->scratch, need.scratch_bytes, device));
+  if (need.cbuf_bytes != 0) KVS_TRY(check_device_buffer(bufs->cbuf, need.cbuf_bytes, device));
 
   kvs_pool* p = new (std::nothrow) kvs_pool();
   if (p == nullptr) return KVS_ENOMEM;
@@ -284,8 +324,8 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
   d.part_o = (float*)(scr + L.part_o);
   d.part_ml = (float*)(scr + L.part_ml);
 
-  hipError_t e = hipGetDevice(&p->device);
-  if (e == hipSuccess) e = prepare_kernels();
+  p->device = device;
+  hipError_t e = prepare_kernels();
   if (e == hipSuccess)
     e = launch_init_units(L, d, 0, L.B * L.L, /*reset_counters=*/true, (hipStream_t)stream);
   if (e != hipSuccess) {
@@ -329,7 +369,8 @@ int kvs_append(kvs_pool* p, int32_t layer, const void* rows, const int64_t* pos,
 
 int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, void* out,
              float* lse, void* stream) {
-  if (p == nullptr || topk == nullptr || q == nullptr || out == nullptr) return KVS_EINVAL;
+  if (p == nullptr) return KVS_EINVAL;
+  KVS_TRY(check_step_args(topk, q, out, lse));
   if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
   const hipStream_t s = (hipStream_t)stream;
   KVS_TRY(check_device(p, s));
@@ -481,7 +522,8 @@ int kvs_graph_capture(kvs_pool* p, int32_t layer, const int32_t* topk, const voi
                       float* lse, kvs_graph** out_graph) {
   if (out_graph == nullptr) return KVS_EINVAL;
   *out_graph = nullptr;
-  if (p == nullptr || topk == nullptr || q == nullptr || out == nullptr) return KVS_EINVAL;
+  if (p == nullptr) return KVS_EINVAL;
+  KVS_TRY(check_step_args(topk, q, out, lse));
   if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
   hipStream_t cs = nullptr;
   KVS_TRY_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));

@@ -1,6 +1,6 @@
 // gfx950 (MI355X) kernels of the per-decode-step sparse KV assembly path.
 //
-// One kvs_step of layer l runs four launches for the B units (b, l):
+// One kvs_step of layer l runs three or four launches for the B units (b, l):
 //   diff_lru   one workgroup per unit: slot lookup + validation, sparse diff
 //              (misses compacted in Top-K order by a workgroup prefix sum),
 //              hit touch, LRU victim choice from the unit's LRU order array,
@@ -12,7 +12,9 @@
 //   attention  split-K sparse MLA decode over the K gathered rows (or over
 //              the hot buffer through row_slot): v_mfma_f32_16x16x32_bf16 for
 //              Q.K^T and P.V, fp32 online softmax.
-//   combine    merges the split partials, writes bf16 out and fp32 lse.
+//   combine    merges the split partials, writes bf16 out and fp32 lse (only
+//              with more than one split: a single-split attention writes out
+//              and lse itself).
 // Outside the step: init/reset kernels (pool creation, kvs_free_request), the
 // append kernel (kvs_append) and the host-read probe (a measurement helper).
 //
@@ -228,7 +230,8 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   __syncthreads();
 
   // 1b. validation and hit flags.  my_slot: >= 0 hit slot, -1 miss, -2 empty
-  //     entry of a padded Top-K.  A token given twice is resident in one slot
+  //     entry of a padded Top-K; a looked-up slot outside [-1, S) means the
+  //     map was corrupted.  A token given twice is resident in one slot
   //     (the second flag set of that slot reveals it) or in none (misses go
   //     through an LDS open-addressing set of tokens).
 #pragma unroll
@@ -240,8 +243,9 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
         my_slot[j] = -2;
       } else if (tok < 0 || (long long)tok >= a.N) {
         atomicOr(&err_bits, 1);
+      } else if (my_slot[j] < -1 || my_slot[j] >= S) {
+        atomicOr(&err_bits, 4);   // a map entry no step writes: corrupted state
       } else {
-        if (my_slot[j] >= S) my_slot[j] = -1;
         if (my_slot[j] >= 0) {
           const unsigned bit = 1u << ((my_slot[j] & 3) * 8);   // flag byte := 1
           if (atomicOr(&flagw[my_slot[j] >> 2], bit) & bit) atomicOr(&err_bits, 2);
@@ -261,13 +265,14 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     }
   }
   __syncthreads();
-  if (err_bits) {   // invalid Top-K: leave the unit untouched, latch the error
+  if (err_bits) {   // invalid Top-K or map: leave the unit untouched, latch the error
     if (tid == 0) {
       a.counts[4 * b + 0] = 0;
       a.counts[4 * b + 1] = 0;
       a.counts[4 * b + 2] = 0;
       a.counts[4 * b + 3] = 0;
-      atomicCAS(a.status, 0, (err_bits & 1) ? KVS_ERANGE : KVS_EDUP);
+      atomicCAS(a.status, 0,
+                (err_bits & 1) ? KVS_ERANGE : (err_bits & 4) ? KVS_ECORRUPT : KVS_EDUP);
     }
     return;
   }
