@@ -284,6 +284,27 @@ int kvs_append(kvs_pool* pool, int32_t layer, const void* rows, const int64_t* p
 int kvs_step(kvs_pool* pool, int32_t layer, const int32_t* topk, const void* q,
              void* out, float* lse, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid allocation): kvs_step with
+ * its per-step scratch (slot, miss and victim lists, counts and attention
+ * partials) in a static device array of the library, KVS_STATIC_SCRATCH_BYTES
+ * per GPU, instead of the pool's scratch buffer (which this call leaves
+ * untouched).  The array exists once per GPU the library runs on, from the
+ * first kvs_create_pool on that GPU until the process ends.  The call
+ * allocates nothing, host or device.
+ * Same arguments, results and errors as kvs_step, plus KVS_ENOMEM (nothing
+ * enqueued) when the pool's kvs_sizes.scratch_bytes exceed
+ * KVS_STATIC_SCRATCH_BYTES, and KVS_EHIP_* if the array's address could not
+ * be resolved at kvs_create_pool.
+ * Every call on one GPU, from any pool, shares that GPU's array and leaves
+ * the last call's contents in it: calls that may run concurrently on one GPU
+ * (different streams, or graphs replayed on them) race and must be ordered by
+ * the caller.  kvs_debug_read_state reports the lists of a pool's last step
+ * from the buffer that step used. */
+#define KVS_STATIC_SCRATCH_BYTES (32u << 20)
+int kvs_step_static(kvs_pool* pool, int32_t layer, const int32_t* topk, const void* q,
+                    void* out, float* lse, void* stream);
+
 /* Lifecycle "free": empty every layer of request `req` (maps -1, last_used -1,
  * LRU order 0..S-1).  Its step counters keep running.  Enqueued on `stream`. */
 int kvs_free_request(kvs_pool* pool, int32_t req, void* stream);

@@ -42,8 +42,9 @@ EXPORTS = (
     "kvs_step", "kvs_free_request", "kvs_sync_status", "kvs_debug_read_state",
     "kvs_profile_begin", "kvs_profile_end", "kvs_release", "kvs_strerror",
     "kvs_graph_capture", "kvs_graph_launch", "kvs_graph_destroy", "kvs_publish_device",
-    "kvs_append", "kvs_probe_host_read",
+    "kvs_append", "kvs_probe_host_read", "kvs_step_static",
 )
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class kvs_config(ctypes.Structure):
@@ -128,6 +129,7 @@ def lib() -> ctypes.CDLL:
         "kvs_append": [vp, i32, vp, vp, vp],
         "kvs_probe_host_read": [vp, u64, vp, vp],
         "kvs_step": [vp, i32, vp, vp, vp, vp, vp],
+        "kvs_step_static": [vp, i32, vp, vp, vp, vp, vp],
         "kvs_free_request": [vp, i32, vp],
         "kvs_sync_status": [vp, vp, ctypes.POINTER(kvs_step_stats)],
         "kvs_debug_read_state": [vp, i32, i32, vp, ctypes.POINTER(kvs_unit_state)],
@@ -288,6 +290,19 @@ class Pool:
             lse_ptr = lse.data_ptr()
         _check(lib().kvs_step(self.handle, layer, topk.data_ptr(), q.data_ptr(), out.data_ptr(),
                               lse_ptr, _stream_ptr(stream, self.device)), "kvs_step")
+
+    def step_static(self, layer, topk, q, out, lse=None, stream=None):
+        """kvs_step_static: ``step`` with the library's static per-GPU scratch."""
+        self._check_dev(topk, (self.B, self.K), 4)
+        self._check_dev(q, (self.B, HEADS, HEAD_DIM), 2)
+        self._check_dev(out, (self.B, HEADS, V_DIM), 2)
+        lse_ptr = None
+        if lse is not None:
+            self._check_dev(lse, (self.B, HEADS), 4)
+            lse_ptr = lse.data_ptr()
+        _check(lib().kvs_step_static(self.handle, layer, topk.data_ptr(), q.data_ptr(),
+                                     out.data_ptr(), lse_ptr, _stream_ptr(stream, self.device)),
+               "kvs_step_static")
 
     def free_request(self, req, stream=None):
         _check(lib().kvs_free_request(self.handle, req, _stream_ptr(stream, self.device)),

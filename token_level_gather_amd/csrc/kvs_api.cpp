@@ -130,6 +130,11 @@ struct kvs_pool {
   int prof_max_steps;
   uint32_t prof_mask;  // kernels recorded (1 << KVS_KERNEL_*)
   bool roctx;          // KVS_ROCTX=1 at creation: a named range around every kvs_step
+  // the library's static scratch on this pool's device (kvs_step_static), or
+  // null with the error that resolving its address gave
+  void* static_scratch;
+  hipError_t static_scratch_err;
+  DevPtrs last_scratch;  // device pointers of the last step (its lists for kvs_debug_read_state)
 };
 
 static int hip_err(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP_BASE - (int)e; }
@@ -193,6 +198,18 @@ static int check_device_buffer(const void* ptr, uint64_t bytes, int device) {
   const uintptr_t end = (uintptr_t)base + size;
   if ((uintptr_t)ptr < (uintptr_t)base || (uintptr_t)ptr + bytes > end) return KVS_ENOMEM;
   return KVS_OK;
+}
+
+// Points the per-step arrays of `d` into a scratch buffer laid out by `lay`.
+static void bind_scratch(const Layout& lay, uint8_t* scr, DevPtrs* d) {
+  d->slot_of = (int32_t*)(scr + lay.slot_of);
+  d->miss_pos = (int32_t*)(scr + lay.miss_pos);
+  d->victims = (int32_t*)(scr + lay.victims);
+  d->evicted = (int32_t*)(scr + lay.evicted);
+  d->counts = (int32_t*)(scr + lay.counts);
+  d->row_slot = (int32_t*)(scr + lay.row_slot);
+  d->part_o = (float*)(scr + lay.part_o);
+  d->part_ml = (float*)(scr + lay.part_ml);
 }
 
 // Launch `fn` on `s`, bracketed by timing events when profiling.
@@ -315,16 +332,12 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
   d.stepctr = (int32_t*)(meta + L.stepctr);
   d.stats = (long long*)(meta + L.stats);
   d.status = (int32_t*)(meta + L.status);
-  d.slot_of = (int32_t*)(scr + L.slot_of);
-  d.miss_pos = (int32_t*)(scr + L.miss_pos);
-  d.victims = (int32_t*)(scr + L.victims);
-  d.evicted = (int32_t*)(scr + L.evicted);
-  d.counts = (int32_t*)(scr + L.counts);
-  d.row_slot = (int32_t*)(scr + L.row_slot);
-  d.part_o = (float*)(scr + L.part_o);
-  d.part_ml = (float*)(scr + L.part_ml);
+  bind_scratch(L, scr, &d);
+  p->last_scratch = d;
 
   p->device = device;
+  p->static_scratch = nullptr;
+  p->static_scratch_err = static_scratch_address(device, &p->static_scratch);
   hipError_t e = prepare_kernels();
   if (e == hipSuccess)
     e = launch_init_units(L, d, 0, L.B * L.L, /*reset_counters=*/true, (hipStream_t)stream);
@@ -367,15 +380,13 @@ int kvs_append(kvs_pool* p, int32_t layer, const void* rows, const int64_t* pos,
                                (hipStream_t)stream));
 }
 
-int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, void* out,
-             float* lse, void* stream) {
-  if (p == nullptr) return KVS_EINVAL;
-  KVS_TRY(check_step_args(topk, q, out, lse));
-  if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
-  const hipStream_t s = (hipStream_t)stream;
-  KVS_TRY(check_device(p, s));
+// Enqueues one layer step over the device pointers `d` (the pool's own
+// scratch, or the library's static scratch for kvs_step_static).  `trace`
+// allows the optional roctx range (kvs_step_static does without it: the
+// tracer may allocate).
+static int enqueue_step(kvs_pool* p, const DevPtrs& d, int32_t layer, const int32_t* topk,
+                        const void* q, void* out, float* lse, hipStream_t s, bool trace) {
   const Layout& L = p->lay;
-  const DevPtrs& d = p->d;
   // a host-side range for rocprofv3 --marker-trace (enqueue time, not GPU time)
   struct Range {
     bool on;
@@ -388,7 +399,7 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
     ~Range() {
       if (on) roctxRangePop();
     }
-  } range(p->roctx, layer);
+  } range(p->roctx && trace, layer);
   // lookup, sparse diff, LRU and map update for every request of the layer
   KVS_TRY_HIP(timed(p, KVS_KERNEL_DIFF_LRU, s, [&] { return launch_diff_lru(L, d, layer, topk, s); }));
   // optional verification of the updated state (not timed)
@@ -404,7 +415,33 @@ int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, voi
     KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
                       [&] { return launch_combine(L, d, (uint16_t*)out, lse, s); }));
   if (p->prof_steps < p->prof_max_steps) ++p->prof_steps;
+  p->last_scratch = d;
   return KVS_OK;
+}
+
+int kvs_step(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, void* out,
+             float* lse, void* stream) {
+  if (p == nullptr) return KVS_EINVAL;
+  KVS_TRY(check_step_args(topk, q, out, lse));
+  if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
+  const hipStream_t s = (hipStream_t)stream;
+  KVS_TRY(check_device(p, s));
+  return enqueue_step(p, p->d, layer, topk, q, out, lse, s, true);
+}
+
+int kvs_step_static(kvs_pool* p, int32_t layer, const int32_t* topk, const void* q, void* out,
+                    float* lse, void* stream) {
+  if (p == nullptr) return KVS_EINVAL;
+  KVS_TRY(check_step_args(topk, q, out, lse));
+  if (layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
+  if (p->lay.scratch_bytes > (uint64_t)KVS_STATIC_SCRATCH_BYTES) return KVS_ENOMEM;
+  const hipStream_t s = (hipStream_t)stream;
+  KVS_TRY(check_device(p, s));
+  if (p->static_scratch == nullptr) return hip_err(p->static_scratch_err);
+  // the same kernels, with every per-step list and partial in the static array
+  DevPtrs d = p->d;
+  bind_scratch(p->lay, (uint8_t*)p->static_scratch, &d);
+  return enqueue_step(p, d, layer, topk, q, out, lse, s, false);
 }
 
 int kvs_free_request(kvs_pool* p, int32_t req, void* stream) {
@@ -451,6 +488,7 @@ int kvs_debug_read_state(kvs_pool* p, int32_t req, int32_t layer, void* stream,
   const hipStream_t s = (hipStream_t)stream;
   const Layout& L = p->lay;
   const DevPtrs& d = p->d;
+  const DevPtrs& ls = p->last_scratch;   // per-step lists of the last step
   const long long u = (long long)req * L.L + layer;
   auto get = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
     if (dst == nullptr) return hipSuccess;
@@ -459,12 +497,12 @@ int kvs_debug_read_state(kvs_pool* p, int32_t req, int32_t layer, void* stream,
   KVS_TRY_HIP(get(st->tok2slot, d.tok2slot + u * L.N, (size_t)L.N * 4));
   KVS_TRY_HIP(get(st->slot2tok, d.slot2tok + u * L.S, (size_t)L.S * 4));
   KVS_TRY_HIP(get(st->last_used, d.last_used + u * L.S, (size_t)L.S * 4));
-  KVS_TRY_HIP(get(st->slot_of, d.slot_of + (long long)req * L.K, (size_t)L.K * 4));
-  KVS_TRY_HIP(get(st->miss_pos, d.miss_pos + (long long)req * L.K, (size_t)L.K * 4));
-  KVS_TRY_HIP(get(st->victims, d.victims + (long long)req * L.K, (size_t)L.K * 4));
-  KVS_TRY_HIP(get(st->evicted, d.evicted + (long long)req * L.K, (size_t)L.K * 4));
-  KVS_TRY_HIP(get(st->counts, d.counts + 4LL * req, 16));
-  KVS_TRY_HIP(get(st->row_slot, d.row_slot + (long long)req * L.K, (size_t)L.K * 4));
+  KVS_TRY_HIP(get(st->slot_of, ls.slot_of + (long long)req * L.K, (size_t)L.K * 4));
+  KVS_TRY_HIP(get(st->miss_pos, ls.miss_pos + (long long)req * L.K, (size_t)L.K * 4));
+  KVS_TRY_HIP(get(st->victims, ls.victims + (long long)req * L.K, (size_t)L.K * 4));
+  KVS_TRY_HIP(get(st->evicted, ls.evicted + (long long)req * L.K, (size_t)L.K * 4));
+  KVS_TRY_HIP(get(st->counts, ls.counts + 4LL * req, 16));
+  KVS_TRY_HIP(get(st->row_slot, ls.row_slot + (long long)req * L.K, (size_t)L.K * 4));
   std::vector<uint16_t> order(st->lru_order ? L.S : 0);
   KVS_TRY_HIP(get(st->lru_order ? order.data() : nullptr, d.order + u * L.S, (size_t)L.S * 2));
   int32_t step = 0;

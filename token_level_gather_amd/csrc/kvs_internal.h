@@ -49,6 +49,10 @@ int make_layout(const kvs_config* cfg, Layout* lay);
 // Dynamic LDS bytes of the diff/LRU kernel for a layout.
 size_t diff_lds_bytes(int S, int K);
 
+// Device address of the library's static scratch (KVS_STATIC_SCRATCH_BYTES)
+// on `device`, which must be the current device; resolved once per device.
+hipError_t static_scratch_address(int device, void** out);
+
 // Device pointers of one pool, resolved from the caller's buffers.
 struct DevPtrs {
   const uint16_t* pool;  // host pool, device-visible address

@@ -25,9 +25,41 @@
 // 1-3).
 #include <math.h>
 
+#include <mutex>
+
 #include "kvs_internal.h"
 
+// Per-step scratch of kvs_step_static, for callers that cannot allocate: one
+// copy per GPU, created when the library's code object is loaded there and
+// held until the process ends.  Host code never passes this name to a kernel
+// (on the host it is only a stand-in for the symbol); it uses the device
+// address from static_scratch_address().
+static __device__ __align__(256) unsigned char scratch[KVS_STATIC_SCRATCH_BYTES];
+
 namespace kvs {
+
+hipError_t static_scratch_address(int device, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  *out = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  int current = -1;
+  hipError_t e = hipGetDevice(&current);
+  if (e != hipSuccess) return e;
+  if (current != device) return hipErrorInvalidDevice;   // resolved with the device current
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[device] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *out = addr[device];
+  return hipSuccess;
+}
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
