@@ -1,26 +1,36 @@
 """Benchmark of the per-decode-step sparse KV assembly path on one MI355X.
 
 A step is one decode step of the whole hot path for every request and layer of
-the workload: slot lookup + sparse diff + LRU (diff_lru), the index copy
+a workload: slot lookup + sparse diff + LRU (diff_lru), the index copy
 (gather: misses fetched from pinned host memory over PCIe and written back to
 the hot buffer, hits copied within HBM), split-K sparse MLA attention and the
-merge of its partials (combine).
-Inputs (host pool rows, Top-K streams, queries) are seeded and synthetic and
-are resident (pool in pinned host memory, the rest in HBM) before timing.
+merge of its partials (combine, only with more than one split).  Inputs (host
+pool rows, Top-K streams, queries) are seeded and synthetic and are resident
+(pool in pinned host memory, the rest in HBM) before any timing.
 
-Prints one JSON line.  ``value`` is selected KV tokens gathered per second
-(B * L * K per step); decode steps per second, the HBM and host-link
-bandwidth figures, the roofline of the dominant kernel and the CPU oracle
-baseline are fields of the same line.
+Prints one JSON line.  The top-level figures are those of the headline
+workload (``--workload``, default: 32 requests x 8 layers at 128K context):
+``value`` is selected KV tokens gathered per second (B * L * K per decode
+step) over exactly ``--steps`` timed steps after ``--warmup`` untimed ones.
+``configs`` holds the same measurement protocol for every workload: R replays
+of its decode steps, each from freshly freed requests, with the median
+steady-state step and the cold first step reported apart, per-kernel times,
+the hit copy alone with the last-level cache flushed, and a parity check of
+sampled requests against the CPU oracle.  ``cpu_baseline`` is the oracle on P
+host processes.  A failed parity check prints no speed line and exits 1.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import mmap
+import multiprocessing as mp
 import os
+import statistics
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -31,10 +41,13 @@ if ROOT not in sys.path:
 import kvs_workload as W  # noqa: E402
 
 METRIC = "selected KV tokens gathered/sec + decode steps/sec; % of HBM and PCIe peak GB/s"
+HEADLINE = "ctx128k_b32_l8_zipf"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 PCIE_PEAK_GBS = 63.0             # PCIe Gen5 x16, one direction: 32 GT/s * 16 * 128/130 / 8
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+MALL_BYTES = 256 << 20           # MI355X last-level (Infinity) cache
 ROW = W.ROW_BYTES
+KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine")
 # The pages' own figures are system-level (whole models, other hardware and
 # serving stacks); none is a figure for this path, so none is compared.
 PAGES_CONTEXT = {
@@ -48,24 +61,35 @@ PAGES_CONTEXT = {
 }
 
 
+def log(msg):
+    print(f"# [{time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30, help="timed decode steps")
-    p.add_argument("--warmup", type=int, default=2, help="untimed decode steps (step 0 is cold)")
-    p.add_argument("--workload", default=W.BENCH_WORKLOAD, choices=sorted(W.WORKLOADS))
-    p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--steps", type=int, default=20, help="timed decode steps (headline)")
+    p.add_argument("--warmup", type=int, default=5,
+                   help="untimed decode steps before the timed ones (step 0 is cold)")
+    p.add_argument("--workload", default=HEADLINE, choices=sorted(W.WORKLOADS),
+                   help="headline workload")
+    p.add_argument("--configs", default="all",
+                   help="comma-separated workloads measured beside the headline, 'all' "
+                        "(every other workload) or 'none'")
+    p.add_argument("--replays", type=int, default=5,
+                   help="timed replays of each workload's decode steps, each from freed requests")
+    p.add_argument("--time-budget", type=float, default=480.0,
+                   help="seconds after which remaining side workloads are skipped")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle: no CPU baseline and no parity check")
+    p.add_argument("--cpu-workers", type=int, default=0,
+                   help="oracle processes; 0 = the host cores available, at most 16")
     p.add_argument("--parity-requests", type=int, default=2)
-    p.add_argument("--no-profile", action="store_true", help="skip per-kernel HIP events")
-    p.add_argument("--breakdown-steps", type=int, default=8,
-                   help="extra steps after the timed region with events around every kernel")
     p.add_argument("--fetch-blocks", type=int, default=0, help="0 = library's choice")
     p.add_argument("--attn-splits", type=int, default=0, help="0 = library's choice")
     p.add_argument("--hit-blocks", type=int, default=0, help="0 = library's choice")
     p.add_argument("--graph", action="store_true",
-                   help="launch every (step, layer) as a captured HIP graph (inputs in place)")
+                   help="headline timed steps as captured HIP graphs (inputs in place)")
     p.add_argument("--hits-first", action="store_true",
                    help="hit-copy workgroups take the first grid indices of the gather")
     p.add_argument("--direct-hot", action="store_true",
@@ -77,22 +101,39 @@ def parse():
     return p.parse_args()
 
 
-def measure_zero_copy_peak(torch, pool, reps=5):
-    """Best of `reps` zero-copy reads of up to 1 GiB of the pinned pool by a plain
+# ---------------------------------------------------------------- peaks and helpers
+
+def measure_zero_copy_peak(torch, kvs, host, reps=5):
+    """Best of `reps` zero-copy reads of up to 1 GiB of a pinned pool by a plain
     GPU read kernel with the fetch's load pattern (the host link's ceiling for
     GPU-initiated reads), timed with events on the stream it runs on."""
-    import token_level_gather_amd as kvs
-    nbytes = min(pool.host.nbytes, 1 << 30) // 16 * 16
+    nbytes = min(host.nbytes, 1 << 30) // 16 * 16
     sink = torch.empty(kvs.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
     best = 0.0
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        kvs.probe_host_read(pool.host.ptr, nbytes, sink)
+        kvs.probe_host_read(host.ptr, nbytes, sink)
         e1.record()
         e1.synchronize()
         best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    return best
+
+
+def measure_h2d_peak(torch, nbytes=1 << 30, reps=5) -> float:
+    """Best of `reps` hipMemcpyAsync copies of 1 GiB from pinned host memory, GB/s."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src, non_blocking=True)
+        e1.record()
+        e1.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
     return best
 
 
@@ -125,213 +166,207 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def measure_h2d_peak(torch, nbytes=1 << 30, reps=5) -> float:
-    """Best of `reps` hipMemcpyAsync copies of 1 GiB from pinned host memory, GB/s."""
-    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
-    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    best = 0.0
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src, non_blocking=True)
-        e1.record()
-        e1.synchronize()
-        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    del src, dst
-    return best
+def parallel_units(fn, wl, threads=16):
+    units = [(b, l) for b in range(wl.batch) for l in range(wl.layers)]
+    with ThreadPoolExecutor(min(threads, len(units))) as ex:
+        list(ex.map(lambda u: fn(*u), units))
 
 
-def cpu_baseline(wl, host, topk, q, total_steps, seconds, keep_requests):
-    """Time the oracle replaying whole requests on one host thread.
+def cpu_workers_count(args) -> int:
+    if args.cpu_workers > 0:
+        return args.cpu_workers
+    # the host cores this process may use; a one-GPU share of the host is 16
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
-    Requests are replayed in order until `seconds` have passed (at least
-    `keep_requests` of them); the outputs and final maps of the first
-    `keep_requests` are returned for the parity check.
-    """
+
+# ---------------------------------------------------------------- cpu_baseline leg
+# Everything that runs the CPU oracle lives here: the multi-process throughput
+# baseline and the oracle replays of sampled requests that the parity check
+# compares the GPU results with.  The GPU path never calls the oracle.
+
+def _cpu_worker(rank, wl, pool_rows, job_q, res_q, barrier):
+    """Forked oracle process: numpy only, one BLAS thread, never touches the GPU."""
     from threadpoolctl import threadpool_limits
 
     from oracle import OracleUnit
-    units = 0
-    kept = {}
-    b = 0
-    t0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        while b < wl.batch:
-            for l in range(wl.layers):
+        while True:
+            job = job_q.get()
+            if job is None:
+                return
+            reqs, steps = job
+            units = [(b, l) for b in reqs for l in range(wl.layers)]
+            streams = {(b, l): W.unit_topk_stream(wl, b, l, steps) for b, l in units}
+            qs = {(l, t): W.queries(wl, l, t) for l in range(wl.layers) for t in range(steps)}
+            barrier.wait()
+            t0 = time.monotonic()
+            for b, l in units:
                 u = OracleUnit(wl.context, wl.slots, wl.topk)
-                for t in range(total_steps):
-                    r = u.step(topk[t, l, b], host[b, l], q[t, l, b], wl.scale)
-                    if b < keep_requests:
-                        kept[(t, l, b)] = r.out
-                if b < keep_requests:
-                    kept[("state", l, b)] = (u.tok2slot.copy(), u.slot2tok.copy(),
-                                             u.last_used.copy())
-                units += 1
-            b += 1
-            if b >= keep_requests and time.perf_counter() - t0 >= seconds:
-                break
-    dt = time.perf_counter() - t0
-    tokens = units * total_steps * wl.topk
-    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle replay of requests 0..{b - 1} x {wl.layers} layer(s) x "
-                      f"{total_steps} steps (K={wl.topk}) on 1 host thread, {dt:.1f} s"}, kept
+                for t in range(steps):
+                    u.step(streams[(b, l)][t], pool_rows[b, l], qs[(l, t)][b], wl.scale)
+            t1 = time.monotonic()
+            res_q.put((rank, t0, t1, len(units) * steps))
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "bench.py measures one GPU only; run with --gpus 1 (the path "
-                                   "shards by request with no exchange between GPUs, so one "
-                                   "GPU's share at its real shape is the measurement)"}))
-        sys.exit(2)
-    import torch
+class CpuWorkers:
+    """P oracle processes forked before the GPU is touched; they read the
+    workload's pool rows through a shared mapping that the parent filled."""
 
-    if args.copy_calibration:
-        copy_calibration(torch)
-        return
+    def __init__(self, wl, pool_rows, nproc):
+        ctx = mp.get_context("fork")
+        self.wl, self.nproc = wl, nproc
+        self.barrier = ctx.Barrier(nproc)
+        self.res_q = ctx.Queue()
+        self.job_qs = [ctx.Queue() for _ in range(nproc)]
+        self.procs = [ctx.Process(target=_cpu_worker, daemon=True,
+                                  args=(r, wl, pool_rows, self.job_qs[r], self.res_q,
+                                        self.barrier)) for r in range(nproc)]
+        for p in self.procs:
+            p.start()
 
-    import token_level_gather_amd as kvs
-
-    wl = W.WORKLOADS[args.workload]
-    B, L, N, S, K = wl.batch, wl.layers, wl.context, wl.slots, wl.topk
-    breakdown = 0 if args.no_profile else args.breakdown_steps
-    total = args.warmup + args.steps + breakdown
-    torch.cuda.set_device(0)
-    print(f"# workload {wl.name}: B={B} L={L} N={N} S={S} K={K} f={wl.fresh_rate} "
-          f"steps {args.warmup}+{args.steps}+{breakdown}", file=sys.stderr, flush=True)
-
-    pool = kvs.Pool(B, L, N, S, K, scale=wl.scale, attn_splits=args.attn_splits,
-                    fetch_blocks=args.fetch_blocks, hit_blocks=args.hit_blocks,
-                    flags=(kvs.KVS_FLAG_HITS_FIRST if args.hits_first else 0)
-                    | (kvs.KVS_FLAG_DIRECT_HOT if args.direct_hot else 0))
-    W.fill_pool(pool.host.array, wl)
-    topk_np = W.topk_streams(wl, total)
-    topk = torch.from_numpy(topk_np).cuda()                         # [T][L][B][K]
-    q_np = np.stack([np.stack([W.queries(wl, l, t) for l in range(L)]) for t in range(total)])
-    q = torch.from_numpy(q_np.view(np.int16)).cuda().view(torch.bfloat16)  # [T][L][B][16][576]
-    out = torch.empty((total, L, B, 16, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((total, L, B, 16), dtype=torch.float32, device="cuda")
-    print(f"# inputs ready, pool {pool.host.nbytes / 1e9:.2f} GB pinned", file=sys.stderr,
-          flush=True)
-
-    graphs = None
-    if args.graph:
-        # one graph per (step, layer) over that step's own buffers: the inputs are
-        # where a selector would have written them, so a replay is the whole step
-        graphs = [[pool.capture(l, topk[t, l], q[t, l], out[t, l], lse[t, l]) for l in range(L)]
-                  for t in range(total)]
-
-    def eager_step(t):
-        for l in range(L):
-            pool.step(l, topk[t, l], q[t, l], out[t, l], lse[t, l])
-
-    def run_step(t):
-        if graphs is None:
-            eager_step(t)
-        else:
-            for l in range(L):
-                graphs[t][l].launch()
-
-    # Per-kernel HIP events exist only around eager launches (a graph replay has
-    # none), so the steps that time kernels run eagerly in every mode: the
-    # warm-up probe, the breakdown steps and the hit-copy replays.  With
-    # --graph only the timed region replays graphs.
-
-    # warm-up; the last warm-up step is timed per kernel to find the dominant kernel
-    cold = None
-    dominant = "gather"
-    for t in range(args.warmup):
-        probe = (not args.no_profile) and t == args.warmup - 1 and t > 0
-        if probe:
-            pool.profile_begin(L)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        if probe:
-            eager_step(t)
-        else:
-            run_step(t)
-        torch.cuda.synchronize()
-        if t == 0:
-            cold = (time.perf_counter() - t0) * 1e3
-        if probe:
-            kt = pool.profile_end()
-            dominant = max(kvs.KERNEL_NAMES, key=lambda k: kt[k])
-    rc, st0 = pool.sync_status()
-    assert rc == 0, kvs.strerror(rc)
-
-    # timed region: events bracket the dominant kernel only
-    if not args.no_profile:
-        pool.profile_begin(args.steps * L, kernels=(dominant,))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(args.warmup, args.warmup + args.steps):
-        run_step(t)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    tdom = pool.profile_end() if not args.no_profile else None
-    rc, st1 = pool.sync_status()
-    assert rc == 0, kvs.strerror(rc)
-    print(f"# timed {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr, flush=True)
-
-    # per-kernel breakdown after the timed region: events around every kernel
-    ktimes = None
-    if breakdown:
-        pool.profile_begin(breakdown * L)
-        for t in range(args.warmup + args.steps, total):
-            eager_step(t)
-        torch.cuda.synchronize()
-        ktimes = pool.profile_end()
-        rc, st2 = pool.sync_status()
-        assert rc == 0, kvs.strerror(rc)
-
-    ms_step = elapsed * 1e3 / args.steps
-    hits = st1.hits - st0.hits
-    misses = st1.misses - st0.misses
-    miss_rate = misses / max(1, hits + misses)
-    tokens_per_step = B * L * K
-    value = tokens_per_step / (ms_step * 1e-3)
-    splits = pool.sizes.attn_splits
-    # split partials (written by attention, read by the combine); with one
-    # split the attention writes the bf16 output itself and no combine runs
-    part_bytes = B * splits * 16 * (512 + 2) * 4 if splits > 1 else B * 16 * 512 * 2
-
-    def algorithmic(hit_l, miss_l):
-        """Algorithmic bytes (and flops) of one kvs_step call, per kernel.
-
-        The gather is bound by the host link: its roofline bytes are the miss
-        rows read over PCIe; its HBM traffic (hit rows read and written, miss
-        rows written twice; with the rows read in place, only the miss rows
-        written once) is listed beside them.
-        """
-        gather_hbm = ROW * miss_l if args.direct_hot else 2 * ROW * hit_l + 2 * ROW * miss_l
-        attn_idx = 4 * B * K if args.direct_hot else 0     # row_slot reads
+    def run(self, steps, per_proc=2):
+        """Each process replays whole requests (all layers, `steps` steps) through
+        the oracle; the first min(B, per_proc * P) requests, split round-robin."""
+        wl, P = self.wl, self.nproc
+        reqs = list(range(min(wl.batch, per_proc * P)))
+        for r in range(P):
+            self.job_qs[r].put(([b for b in reqs if b % P == r], steps))
+        res = [self.res_q.get(timeout=600) for _ in range(P)]
+        t0 = min(x[1] for x in res)
+        t1 = max(x[2] for x in res)
+        unit_steps = sum(x[3] for x in res)
+        busy = [(x[2] - x[1]) / x[3] for x in res if x[3]]
+        wall = t1 - t0
+        tokens = unit_steps * wl.topk
+        units_per_step = wl.batch * wl.layers
         return {
-            "diff_lru": {"bound": "hbm", "bytes": B * (20 * K + 4 * S) + 32 * miss_l},
-            "gather": {"bound": "pcie", "bytes": ROW * miss_l, "hbm_bytes": gather_hbm},
-            "attention": {"bound": "hbm",
-                          "bytes": B * (K * ROW + 16 * 576 * 2) + part_bytes + attn_idx,
-                          "flop": B * 2 * 16 * K * (576 + 512)},
-            "combine": {"bound": "hbm",
-                        "bytes": part_bytes + B * 16 * 512 * 2 if splits > 1 else 0},
+            "value": round(tokens / wall, 1), "unit": "tokens/s", "cores": P, "kind": "oracle",
+            "sample": f"oracle replay of requests 0..{len(reqs) - 1} x {wl.layers} layer(s) x "
+                      f"{steps} steps of {wl.name} (K={wl.topk}), requests split round-robin "
+                      f"over {P} processes, {wall:.2f} s wall, "
+                      f"{sum(x[2] - x[1] for x in res):.1f} s of CPU work",
+            "oracle_ms_per_decode_step": round(wall / steps * 1e3 * units_per_step
+                                               / (unit_steps / steps), 2),
+            "one_core_ms_per_unit_step": round(1e3 * statistics.mean(busy), 3),
+            "unit_steps": unit_steps,
         }
 
-    def kernel_stats(kt, alg, names):
+    def close(self):
+        for q in self.job_qs:
+            q.put(None)
+        for p in self.procs:
+            p.join(timeout=30)
+
+
+def cpu_baseline_oracle_replay(wl, host, topk_np, q_np, reqs, steps):
+    """Oracle replay of the sampled requests (every layer, `steps` steps): outputs,
+    log-sum-exps and final maps, the reference of the parity check."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import OracleUnit
+    rec = {}
+    with threadpool_limits(limits=1):
+        for b in reqs:
+            for l in range(wl.layers):
+                u = OracleUnit(wl.context, wl.slots, wl.topk)
+                for t in range(steps):
+                    r = u.step(topk_np[t, l, b], host[b, l], q_np[t, l, b], wl.scale)
+                    rec[(t, l, b)] = (r.out, r.lse)
+                rec[("state", l, b)] = (u.tok2slot.copy(), u.slot2tok.copy(),
+                                        u.last_used.copy())
+    return rec
+
+
+# ---------------------------------------------------------------- one workload
+
+class Workload:
+    """Device inputs, pool and the measurement phases of one workload."""
+
+    def __init__(self, torch, kvs, wl, args, steps_total, shared_rows=None):
+        self.torch, self.kvs, self.wl, self.args = torch, kvs, wl, args
+        B, L, N, S, K = wl.batch, wl.layers, wl.context, wl.slots, wl.topk
+        self.flags = (kvs.KVS_FLAG_HITS_FIRST if args.hits_first else 0) | \
+            (kvs.KVS_FLAG_DIRECT_HOT if args.direct_hot else 0)
+        self.pool = kvs.Pool(B, L, N, S, K, scale=wl.scale, attn_splits=args.attn_splits,
+                             fetch_blocks=args.fetch_blocks, hit_blocks=args.hit_blocks,
+                             flags=self.flags)
+        host = self.pool.host.array
+        if shared_rows is not None:
+            parallel_units(lambda b, l: np.copyto(host[b, l], shared_rows[b, l]), wl)
+        else:
+            parallel_units(lambda b, l: W.fill_unit_rows(host[b, l], wl, b, l), wl)
+        self.T = steps_total
+        self.topk_np = W.topk_streams(wl, steps_total)                 # [T][L][B][K]
+        self.q_np = np.stack([np.stack([W.queries(wl, l, t) for l in range(L)])
+                              for t in range(steps_total)])            # [T][L][B][16][576]
+        self.topk = torch.from_numpy(self.topk_np).cuda()
+        self.q = torch.from_numpy(self.q_np.view(np.int16)).cuda().view(torch.bfloat16)
+        self.out = torch.empty((steps_total, L, B, 16, 512), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((steps_total, L, B, 16), dtype=torch.float32, device="cuda")
+        self.graphs = None
+        self.last_t = None   # the last step run: its Top-K is all resident afterwards
+
+    def step(self, t):
+        for l in range(self.wl.layers):
+            self.pool.step(l, self.topk[t, l], self.q[t, l], self.out[t, l], self.lse[t, l])
+        self.last_t = t
+
+    def sync_ok(self):
+        rc, st = self.pool.sync_status()
+        if rc != 0:
+            raise RuntimeError(f"{self.wl.name}: device status {self.kvs.strerror(rc)}")
+        return st
+
+    def free_all(self):
+        for b in range(self.wl.batch):
+            self.pool.free_request(b)
+
+    def close(self):
+        if self.graphs is not None:
+            for row in self.graphs:
+                for g in row:
+                    g.destroy()
+        self.pool.release()
+        self.pool.host.free()
+
+    # -- algorithmic bytes of one kvs_step call -------------------------------
+    def algorithmic(self, hits_per_call, misses_per_call):
+        wl, direct = self.wl, self.args.direct_hot
+        B, S, K = wl.batch, wl.slots, wl.topk
+        splits = self.pool.sizes.attn_splits
+        # split partials (written by attention, read by the combine); with one
+        # split the attention writes the bf16 output itself and no combine runs
+        part = B * splits * 16 * (512 + 2) * 4 if splits > 1 else B * 16 * 512 * 2
+        gather_hbm = ROW * misses_per_call if direct else \
+            2 * ROW * hits_per_call + 2 * ROW * misses_per_call
+        return {
+            "diff_lru": {"bound": "hbm", "bytes": B * (20 * K + 4 * S) + 32 * misses_per_call},
+            "gather": {"bound": "pcie", "bytes": ROW * misses_per_call, "hbm_bytes": gather_hbm},
+            "attention": {"bound": "hbm",
+                          "bytes": B * (K * ROW + 16 * 576 * 2) + part + (4 * B * K if direct
+                                                                           else 0),
+                          "flop": B * 2 * 16 * K * (576 + 512)},
+            "combine": {"bound": "hbm", "bytes": part + B * 16 * 512 * 2 if splits > 1 else 0},
+        }
+
+    def kernel_stats(self, kt, alg, names, zc_gbs=None):
         res = {}
-        calls = max(1, kt["steps"]) * 1
+        calls = max(1, kt["steps"])
         for name in names:
             a = alg[name]
             launches = kt["launches"][name]
             if launches == 0:
                 continue
-            per_call = launches / calls                    # launches per kvs_step call
-            avg_ms = kt[name] / launches                   # average launch duration
-            b_launch = a["bytes"] / per_call               # algorithmic bytes per launch
+            per_call = launches / calls
+            avg_ms = kt[name] / launches
+            b_launch = a["bytes"] / per_call
             gbs = b_launch / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
             peak = PCIE_PEAK_GBS if a["bound"] == "pcie" else HBM_PEAK_GBS
             k = {"avg_ms": round(avg_ms, 5), "launches_per_call": round(per_call, 3),
-                 "ms_per_call": round(kt[name] / calls, 5), "bound": a["bound"],
-                 "bytes_per_launch": int(b_launch), "achieved_gbs": round(gbs, 2),
-                 "peak_gbs": peak, "frac": round(gbs / peak, 4)}
+                 "bound": a["bound"], "bytes_per_launch": int(b_launch),
+                 "achieved_gbs": round(gbs, 2), "peak_gbs": peak, "frac": round(gbs / peak, 4)}
+            if a["bound"] == "pcie" and zc_gbs:
+                k["frac_of_zero_copy_peak"] = round(gbs / zc_gbs, 4)
             if "flop" in a:
                 tf = a["flop"] / per_call / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
                 k["tflops"] = round(tf, 2)
@@ -342,92 +377,352 @@ def main():
             res[name] = k
         return res
 
-    calls_timed = args.steps * L
-    alg = algorithmic(hits / calls_timed, misses / calls_timed)
-    dom = kernel_stats(tdom, alg, (dominant,)).get(dominant) if tdom is not None else None
-    kernels = None
-    if ktimes is not None:
-        calls_b = breakdown * L
-        alg_b = algorithmic((st2.hits - st1.hits) / calls_b, (st2.misses - st1.misses) / calls_b)
-        kernels = kernel_stats(ktimes, alg_b, kvs.KERNEL_NAMES)
-    dom_source = "timed region"
-    if dom is None and kernels and dominant in kernels:
-        dom, dom_source = kernels[dominant], "breakdown steps (eager; the timed region replays graphs)"
+    # -- phases ---------------------------------------------------------------
+    def contract_run(self, warmup, steps, graph=False):
+        """`warmup` untimed steps from a fresh pool (the first is cold), then exactly
+        `steps` timed steps bracketed by device synchronisation; HIP events on the
+        launch stream bracket the dominant kernel's launches inside the timed region."""
+        torch, pool, L = self.torch, self.pool, self.wl.layers
+        if graph:
+            self.graphs = [[pool.capture(l, self.topk[t, l], self.q[t, l], self.out[t, l],
+                                         self.lse[t, l]) for l in range(L)]
+                           for t in range(warmup, warmup + steps)]
+        cold = None
+        dominant = "gather"
+        for t in range(warmup):
+            probe = t == warmup - 1 and t > 0
+            if probe:
+                pool.profile_begin(L)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            self.step(t)
+            torch.cuda.synchronize()
+            if t == 0:
+                cold = (time.perf_counter() - t0) * 1e3
+            if probe:
+                kt = pool.profile_end()
+                dominant = max(KERNEL_NAMES, key=lambda k: kt[k])
+        st0 = self.sync_ok()
+        pool.profile_begin(steps * L, kernels=(dominant,))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(warmup, warmup + steps):
+            if graph:
+                for g in self.graphs[t - warmup]:
+                    g.launch()
+            else:
+                self.step(t)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        tdom = pool.profile_end()
+        st1 = self.sync_ok()
+        return {"elapsed": elapsed, "cold_ms": cold, "dominant": dominant, "tdom": tdom,
+                "hits": st1.hits - st0.hits, "misses": st1.misses - st0.misses}
 
-    h2d = measure_h2d_peak(torch)
-    zc = measure_zero_copy_peak(torch, pool)
-    roofline = None
-    if dom is not None:
-        roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved_gbs"],
-                    "peak": dom["peak_gbs"], "unit": "GB/s", "frac": dom["frac"],
-                    "traffic": load_traffic(dominant, wl.name), "avg_ms": dom["avg_ms"],
-                    "bytes_per_launch": dom["bytes_per_launch"], "avg_ms_from": dom_source}
-        if dom["bound"] == "pcie":
-            roofline["frac_of_measured_h2d"] = round(dom["achieved_gbs"] / h2d, 4)
-            roofline["frac_of_zero_copy_peak"] = round(dom["achieved_gbs"] / zc, 4)
-        if "hbm_bytes" in alg[dominant]:
-            # what the HBM counters should read if nothing is re-read: the kernel's
-            # algorithmic HBM bytes plus the host rows it pulls through the L2
-            alg_hbm = alg[dominant]["hbm_bytes"] + alg[dominant]["bytes"]
-            roofline["algorithmic_traffic"] = int(alg_hbm / dom["launches_per_call"])
+    def replays(self, R, steps):
+        """R replays of steps 0..steps-1, each from freed requests, every step
+        bracketed by events on the launch stream.  Returns per-replay step times."""
+        torch = self.torch
+        times = []
+        for _ in range(R):
+            self.free_all()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            ev[0].record()
+            for t in range(steps):
+                self.step(t)
+                ev[t + 1].record()
+            ev[-1].synchronize()
+            times.append([ev[t].elapsed_time(ev[t + 1]) for t in range(steps)])
+        self.sync_ok()
+        return times
 
-    # parity of sampled requests against the oracle, plus the CPU baseline
-    cpu = None
-    parity = None
-    if not args.no_cpu_baseline:
-        host = pool.host.array
-        npar = min(args.parity_requests, B)
-        cpu, rec = cpu_baseline(wl, host, topk_np, q_np, total, args.cpu_seconds, npar)
-        out_np = out.view(torch.int16).cpu().numpy().view(np.uint16)
-        max_abs = max_rel = 0.0
+    def breakdown(self, steps, zc_gbs):
+        """One more replay from freed requests; events around every kernel of the
+        steady steps 1..steps-1."""
+        pool, L = self.pool, self.wl.layers
+        self.free_all()
+        self.step(0)
+        sa = self.sync_ok()
+        pool.profile_begin((steps - 1) * L)
+        for t in range(1, steps):
+            self.step(t)
+        self.torch.cuda.synchronize()
+        kt = pool.profile_end()
+        sb = self.sync_ok()
+        calls = (steps - 1) * L
+        hits, misses = sb.hits - sa.hits, sb.misses - sa.misses
+        alg = self.algorithmic(hits / calls, misses / calls)
+        return self.kernel_stats(kt, alg, KERNEL_NAMES, zc_gbs), hits, misses, alg
+
+    def hit_copy(self, reps=3):
+        """The hit copy alone, with a working set well above the 256 MB Infinity
+        Cache.  Two all-hit Top-K sets per unit are replayed in turn, layer after
+        layer: A = the last step's Top-K and B = K other resident tokens (every
+        slot is occupied by then, and S >= 2K in every workload).  All of each
+        set is resident, so every entry is a hit and the gather launch is the HBM
+        hit copy only: 1152 B read + 1152 B written per row.  Between two reads
+        of a hot row come the reads of every other unit's two sets."""
+        if self.args.direct_hot:
+            return None
+        torch, pool, wl, t = self.torch, self.pool, self.wl, self.last_t
+        B, L, K = wl.batch, wl.layers, wl.topk
+        set_a = self.topk[t]                                     # [L][B][K]
+        set_b = torch.empty_like(set_a)
+        for l in range(L):
+            for b in range(B):
+                st = pool.read_state(b, l)
+                res = st["slot2tok"][st["slot2tok"] >= 0]
+                other = np.setdiff1d(res, self.topk_np[t, l, b])
+                if other.size < K:
+                    return None
+                set_b[l, b] = torch.from_numpy(other[:K].astype(np.int32))
+        sets = (set_a, set_b)
+        self.sync_ok()
+        _, sa = pool.sync_status()
+        pool.profile_begin(reps * 2 * L, kernels=("gather",))
+        for _ in range(reps):
+            for tk in sets:
+                for l in range(L):
+                    pool.step(l, tk[l], self.q[t, l], self.out[t, l], self.lse[t, l])
+        kh = pool.profile_end()
+        sb = self.sync_ok()
+        launches = kh["launches"]["gather"]
+        assert launches == reps * 2 * L, launches
+        assert sb.misses == sa.misses, "the hit-copy replay fetched rows"
+        rows = (sb.hits - sa.hits) / launches
+        avg_ms = kh["gather"] / launches
+        gbs = 2 * ROW * rows / (avg_ms * 1e-3) / 1e9
+        working_set = (2 * L * B * K + B * K) * ROW    # both sets' hot rows + the compute buffer
+        return {"rows_per_launch": int(rows), "bytes_per_launch": int(2 * ROW * rows),
+                "avg_ms": round(avg_ms, 5), "achieved_gbs": round(gbs, 1),
+                "peak_gbs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "working_set_mb": round(working_set / 1e6, 1),
+                "note": "two disjoint all-hit Top-K sets per unit replayed in turn over every "
+                        "layer; working set = both sets' hot rows + the compute buffer"}
+
+    def parity(self, steps, reqs, rec):
+        """GPU outputs of steps 0..steps-1 and final maps of the sampled requests
+        against the oracle replay (every layer)."""
+        torch, wl = self.torch, self.wl
+        out = self.out[:steps].view(torch.int16).cpu().numpy().view(np.uint16)
+        lse = self.lse[:steps].cpu().numpy()
+        max_abs = max_rel = max_lse = 0.0
         state_ok = True
-        for b in range(npar):
-            for l in range(L):
-                for t in range(total):
-                    ref = rec[(t, l, b)]
-                    got = ((out_np[t, l, b].astype(np.uint32) << 16).view(np.float32)
+        for b in reqs:
+            for l in range(wl.layers):
+                for t in range(steps):
+                    ref, ref_lse = rec[(t, l, b)]
+                    got = ((out[t, l, b].astype(np.uint32) << 16).view(np.float32)
                            .astype(np.float64))
                     err = got - ref
                     max_abs = max(max_abs, float(np.abs(err).max()))
                     max_rel = max(max_rel, float(np.linalg.norm(err) / np.linalg.norm(ref)))
-                st = pool.read_state(b, l)
+                    max_lse = max(max_lse, float(np.abs(lse[t, l, b] - ref_lse).max()))
+                st = self.pool.read_state(b, l)
                 t2s, s2t, lu = rec[("state", l, b)]
                 state_ok &= bool(np.array_equal(st["tok2slot"], t2s) and
                                  np.array_equal(st["slot2tok"], s2t) and
                                  np.array_equal(st["last_used"], lu))
-        parity = {"requests_checked": npar, "steps_checked": total, "state_bit_exact": state_ok,
-                  "attn_max_abs": round(max_abs, 6), "attn_max_rel_l2": round(max_rel, 6),
-                  "pass": bool(state_ok and max_abs <= 2e-2 and max_rel <= 1e-2)}
+        ok = bool(state_ok and max_abs <= 2e-2 and max_rel <= 1e-2 and max_lse <= 2e-3)
+        return {"requests_checked": list(reqs), "layers_checked": wl.layers,
+                "steps_checked": steps, "state_bit_exact": state_ok,
+                "attn_max_abs": round(max_abs, 6), "attn_max_rel_l2": round(max_rel, 6),
+                "lse_max_abs": round(max_lse, 6), "pass": ok}
 
-    # The hit copy alone.  Inside a step it shares the gather launch with the
-    # PCIe fetch; replaying the last step's Top-K (which that step left
-    # resident) makes every entry a hit, so the gather launch is then the HBM
-    # hit copy only: 1152 B read + 1152 B written per row.  Runs after the
-    # parity read-back; it only restamps the same slots.
-    hit_gather = None
-    if not args.no_profile and not args.direct_hot:
-        reps = 3
-        rc, sa = pool.sync_status()
-        pool.profile_begin(reps * L, kernels=("gather",))
-        for _ in range(reps):
-            eager_step(total - 1)
-        torch.cuda.synchronize()
-        kh = pool.profile_end()
-        rc, sb = pool.sync_status()
-        assert rc == 0, kvs.strerror(rc)
-        launches = kh["launches"]["gather"]
-        assert launches == reps * L, launches
-        rows = (sb.hits - sa.hits) / launches
-        avg_ms = kh["gather"] / launches
-        gbs = 2 * ROW * rows / (avg_ms * 1e-3) / 1e9
-        hit_gather = {"rows_per_launch": int(rows), "misses": int(sb.misses - sa.misses),
-                      "avg_ms": round(avg_ms, 5), "achieved_gbs": round(gbs, 1),
-                      "peak_gbs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
-                      "note": "last step's Top-K replayed (all hits): the gather launch is the "
-                              "hit copy alone, 2 x 1152 B of HBM traffic per row"}
 
+def summarize(wlo, times, kernels, hits, misses, hit_copy, parity, zc_gbs, wall):
+    """Per-workload results of the measurement protocol."""
+    wl = wlo.wl
+    steady = [statistics.mean(r[1:]) for r in times]
+    cold = [r[0] for r in times]
+    ms = statistics.median(steady)
+    tokens = wl.batch * wl.layers * wl.topk
+    res = {
+        "batch": wl.batch, "layers": wl.layers, "context": wl.context, "slots": wl.slots,
+        "topk": wl.topk, "fresh_rate": wl.fresh_rate, "fresh_dist": wl.dist,
+        "steps": len(times[0]), "replays": len(times),
+        "attn_splits": wlo.pool.sizes.attn_splits,
+        "ms_per_step": round(ms, 5),
+        "ms_per_step_replays": [round(x, 5) for x in steady],
+        "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+        "decode_steps_per_s": round(1e3 / ms, 2),
+        "cold_step_ms": round(statistics.median(cold), 4),
+        "miss_rate": round(misses / max(1, hits + misses), 5),
+        "host_link_gbs_step": round(ROW * misses / (len(times[0]) - 1) / (ms * 1e-3) / 1e9, 3),
+        "kernels": kernels,
+        "hit_copy": hit_copy,
+        "parity": parity,
+        "wall_s": round(wall, 1),
+    }
+    g = kernels.get("gather")
+    if g:
+        res["gather_frac_of_63gbs"] = g["frac"]
+        res["gather_frac_of_zero_copy_peak"] = round(g["achieved_gbs"] / zc_gbs, 4)
+    a = kernels.get("attention")
+    if a:
+        res["attention_hbm_frac"] = a["frac"]
+        res["attention_mfma_frac"] = a.get("mfma_frac")
+    link_s = ROW * misses / (len(times[0]) - 1) / (zc_gbs * 1e9)
+    res["link_ceiling_frac"] = round(link_s * 1e3 / ms, 4)   # step time if only the PCIe bytes
+    return res
+
+
+def parity_reqs(wl, n):
+    reqs = sorted({0, wl.batch - 1} if n >= 2 else {0})
+    return reqs[:max(1, n)]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "bench.py measures one GPU only; run with --gpus 1 (the path "
+                                   "shards by request with no exchange between GPUs, so one "
+                                   "GPU's share at its real shape is the measurement)"}))
+        sys.exit(2)
+    t_start = time.perf_counter()
+    head = W.WORKLOADS[args.workload]
+    if args.configs == "all":
+        side = [n for n in W.WORKLOADS if n != head.name]
+    elif args.configs == "none":
+        side = []
+    else:
+        side = [n for n in args.configs.split(",") if n and n != head.name]
+        for n in side:
+            if n not in W.WORKLOADS:
+                raise SystemExit(f"unknown workload {n}")
+    steps_head = max(head.steps, args.warmup + args.steps)
+
+    # The headline pool is filled into a shared mapping and the oracle processes
+    # are forked from it before anything touches the GPU (no torch import yet).
+    workers = shared = shared_rows = None
+    if not args.no_cpu_baseline and not args.copy_calibration:
+        P = cpu_workers_count(args)
+        log(f"filling {head.pool_bytes / 1e9:.2f} GB of pool rows for {head.name} "
+            f"(shared with {P} oracle processes)")
+        shared = mmap.mmap(-1, head.pool_bytes, flags=mmap.MAP_SHARED | mmap.MAP_ANONYMOUS)
+        shared_rows = np.frombuffer(shared, dtype=np.uint16).reshape(
+            head.batch, head.layers, head.context, head.head_dim)
+        parallel_units(lambda b, l: W.fill_unit_rows(shared_rows[b, l], head, b, l), head)
+        workers = CpuWorkers(head, shared_rows, P)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    import token_level_gather_amd as kvs
+
+    torch.cuda.set_device(0)
+    results = {}
+    failed = []
+
+    # ---- headline
+    t0 = time.perf_counter()
+    log(f"headline {head.name}: B={head.batch} L={head.layers} N={head.context} "
+        f"S={head.slots} K={head.topk}; warmup {args.warmup} + timed {args.steps}")
+    wo = Workload(torch, kvs, head, args, steps_head, shared_rows)
+    log(f"inputs ready, pool {wo.pool.host.nbytes / 1e9:.2f} GB pinned")
+    h2d = measure_h2d_peak(torch)
+    zc = measure_zero_copy_peak(torch, kvs, wo.pool.host)
+    log(f"H2D copy peak {h2d:.1f} GB/s, zero-copy read peak {zc:.1f} GB/s")
+    cr = wo.contract_run(args.warmup, args.steps, graph=args.graph)
+    log(f"timed {args.steps} steps in {cr['elapsed'] * 1e3:.2f} ms")
+    parity = None
+    if workers is not None:
+        reqs = parity_reqs(head, args.parity_requests)
+        rec = cpu_baseline_oracle_replay(head, wo.pool.host.array, wo.topk_np, wo.q_np, reqs,
+                                         args.warmup + args.steps)
+        parity = wo.parity(args.warmup + args.steps, reqs, rec)
+        del rec
+        log(f"parity {parity}")
+        if not parity["pass"]:
+            failed.append(head.name)
+    times = wo.replays(args.replays, head.steps)
+    kernels, hits_b, misses_b, _ = wo.breakdown(head.steps, zc)
+    hit_copy = wo.hit_copy()
+    results[head.name] = summarize(wo, times, kernels, hits_b, misses_b, hit_copy, parity, zc,
+                                   time.perf_counter() - t0)
+    log(f"{head.name}: {results[head.name]['ms_per_step']} ms/step median of replays")
+
+    ms_step = cr["elapsed"] * 1e3 / args.steps
+    L = head.layers
+    calls_timed = args.steps * L
+    alg = wo.algorithmic(cr["hits"] / calls_timed, cr["misses"] / calls_timed)
+    dom = wo.kernel_stats(cr["tdom"], alg, (cr["dominant"],), zc).get(cr["dominant"])
+    roofline = None
+    if dom is not None:
+        roofline = {"kernel": cr["dominant"], "bound": dom["bound"],
+                    "achieved": dom["achieved_gbs"], "peak": dom["peak_gbs"], "unit": "GB/s",
+                    "frac": dom["frac"], "traffic": load_traffic(cr["dominant"], head.name),
+                    "avg_ms": dom["avg_ms"], "bytes_per_launch": dom["bytes_per_launch"],
+                    "avg_ms_from": "HIP events on the launch stream around every launch of "
+                                   "this kernel in the timed region"}
+        if dom["bound"] == "pcie":
+            roofline["frac_of_measured_h2d"] = round(dom["achieved_gbs"] / h2d, 4)
+            roofline["frac_of_zero_copy_peak"] = round(dom["achieved_gbs"] / zc, 4)
+        if "hbm_bytes" in alg[cr["dominant"]]:
+            # what the HBM counters should read if nothing is re-read: the kernel's
+            # algorithmic HBM bytes plus the host rows it pulls through the L2
+            a = alg[cr["dominant"]]
+            roofline["algorithmic_traffic"] = int((a["hbm_bytes"] + a["bytes"])
+                                                  / dom["launches_per_call"])
+    misses = cr["misses"]
     hbm_bytes_step = (alg["diff_lru"]["bytes"] + alg["gather"]["hbm_bytes"]
                       + alg["attention"]["bytes"] + alg["combine"]["bytes"]) * L
+    wo.close()
+    del wo
+    cpu = None
+    if workers is not None:
+        log(f"cpu baseline: {workers.nproc} oracle processes")
+        cpu = workers.run(head.steps)
+        workers.close()
+        log(f"cpu baseline {cpu}")
+    shared_rows = None
+    if shared is not None:
+        shared.close()
+
+    # ---- the other workloads, same protocol
+    for name in side:
+        if time.perf_counter() - t_start > args.time_budget:
+            results[name] = {"skipped": f"time budget of {args.time_budget:.0f} s reached"}
+            log(f"{name}: skipped (time budget)")
+            continue
+        wl = W.WORKLOADS[name]
+        t0 = time.perf_counter()
+        log(f"{name}: B={wl.batch} L={wl.layers} N={wl.context} S={wl.slots} K={wl.topk} "
+            f"f={wl.fresh_rate}")
+        wo = Workload(torch, kvs, wl, args, wl.steps)
+        pr = None
+        if not args.no_cpu_baseline:
+            # replay 0 from a fresh pool, outputs checked against the oracle
+            for t in range(wl.steps):
+                wo.step(t)
+            wo.sync_ok()
+            reqs = parity_reqs(wl, args.parity_requests)
+            rec = cpu_baseline_oracle_replay(wl, wo.pool.host.array, wo.topk_np, wo.q_np, reqs,
+                                             wl.steps)
+            pr = wo.parity(wl.steps, reqs, rec)
+            del rec
+            if not pr["pass"]:
+                failed.append(name)
+        times = wo.replays(args.replays, wl.steps)
+        kernels, hits_b, misses_b, _ = wo.breakdown(wl.steps, zc)
+        hit_copy = wo.hit_copy()
+        results[name] = summarize(wo, times, kernels, hits_b, misses_b, hit_copy, pr, zc,
+                                  time.perf_counter() - t0)
+        log(f"{name}: {results[name]['ms_per_step']} ms/step, parity "
+            f"{None if pr is None else pr['pass']}, {results[name]['wall_s']} s")
+        wo.close()
+        del wo
+
+    if failed:
+        print(json.dumps({"error": "parity check failed; no speed reported", "failed": failed,
+                          "parity": {n: results[n].get("parity") for n in failed}}),
+              file=sys.stderr, flush=True)
+        sys.exit(1)
+
+    hr = results[head.name]
+    value = head.batch * L * head.topk / (ms_step * 1e-3)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -441,15 +736,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": B, "layers": L, "context": N, "slots": S,
-                   "topk": K, "fresh_rate": wl.fresh_rate, "fresh_dist": wl.dist,
-                   "heads": 16, "head_dim": 576, "v_dim": 512, "attn_splits": splits,
-                   "fetch_blocks": pool.sizes.fetch_blocks, "hit_blocks": args.hit_blocks,
+        "config": {"workload": head.name, "batch": head.batch, "layers": L,
+                   "context": head.context, "slots": head.slots, "topk": head.topk,
+                   "fresh_rate": head.fresh_rate, "fresh_dist": head.dist, "heads": 16,
+                   "head_dim": 576, "v_dim": 512, "attn_splits": hr["attn_splits"],
+                   "fetch_blocks": args.fetch_blocks, "hit_blocks": args.hit_blocks,
                    "hits_first": bool(args.hits_first), "hip_graph": bool(args.graph),
                    "direct_hot": bool(args.direct_hot)},
         "decode_steps_per_s": round(1e3 / ms_step, 2),
-        "cold_step_ms": None if cold is None else round(cold, 4),
-        "miss_rate": round(miss_rate, 5),
+        "cold_step_ms": round(cr["cold_ms"], 4),
+        "miss_rate": round(misses / max(1, cr["hits"] + misses), 5),
         "host_link_gbs_step": round(ROW * misses / args.steps / (ms_step * 1e-3) / 1e9, 3),
         "hbm_gbs_step": round(hbm_bytes_step / (ms_step * 1e-3) / 1e9, 2),
         "h2d_peak_measured_gbs": round(h2d, 2),
@@ -458,22 +754,17 @@ def main():
         "steps_per_s_link_ceiling": {
             "pcie_gen5_x16_63gbs": round(63.0e9 / max(1.0, ROW * misses / args.steps), 1),
             "measured_zero_copy": round(zc * 1e9 / max(1.0, ROW * misses / args.steps), 1)},
-        "pages_context": PAGES_CONTEXT,
-        "kernels": kernels,
-        "kernels_note": f"per-kernel HIP events around every launch over {breakdown} extra steps "
-                        "after the timed region; inside the timed region only the dominant "
-                        "kernel is bracketed",
         "roofline": roofline,
-        "hit_gather": hit_gather,
         "cpu_baseline": cpu,
         "parity": parity,
+        "kernels": hr["kernels"],
+        "hit_gather": hr["hit_copy"],
+        "protocol": {k: hr[k] for k in ("steps", "replays", "ms_per_step", "ms_per_step_replays",
+                                        "cold_step_ms", "miss_rate")},
+        "configs": results,
+        "pages_context": PAGES_CONTEXT,
+        "wall_s": round(time.perf_counter() - t_start, 1),
     }
-    if graphs is not None:
-        for row in graphs:
-            for g in row:
-                g.destroy()
-    pool.release()
-    pool.host.free()
     print(json.dumps(line), flush=True)
 
 
