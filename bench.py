@@ -47,7 +47,7 @@ PCIE_PEAK_GBS = 63.0             # PCIe Gen5 x16, one direction: 32 GT/s * 16 * 
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 MALL_BYTES = 256 << 20           # MI355X last-level (Infinity) cache
 ROW = W.ROW_BYTES
-KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine")
+KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine", "assemble")
 # The pages' own figures are system-level (whole models, other hardware and
 # serving stacks); none is a figure for this path, so none is compared.
 PAGES_CONTEXT = {
@@ -95,6 +95,9 @@ def parse():
     p.add_argument("--direct-hot", action="store_true",
                    help="attention reads the selected rows in place from the hot buffer (no "
                         "compute buffer; the gather only fetches misses)")
+    p.add_argument("--separate", action="store_true",
+                   help="index copy and attention as separate launches (gather, attention over "
+                        "the complete compute buffer, merge) instead of one assembling launch")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (the known-size "
                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -286,7 +289,8 @@ class Workload:
         self.torch, self.kvs, self.wl, self.args = torch, kvs, wl, args
         B, L, N, S, K = wl.batch, wl.layers, wl.context, wl.slots, wl.topk
         self.flags = (kvs.KVS_FLAG_HITS_FIRST if args.hits_first else 0) | \
-            (kvs.KVS_FLAG_DIRECT_HOT if args.direct_hot else 0)
+            (kvs.KVS_FLAG_DIRECT_HOT if args.direct_hot else 0) | \
+            (kvs.KVS_FLAG_SEPARATE_ATTENTION if args.separate else 0)
         self.pool = kvs.Pool(B, L, N, S, K, scale=wl.scale, attn_splits=args.attn_splits,
                              fetch_blocks=args.fetch_blocks, hit_blocks=args.hit_blocks,
                              flags=self.flags)
@@ -305,6 +309,11 @@ class Workload:
         self.lse = torch.empty((steps_total, L, B, 16), dtype=torch.float32, device="cuda")
         self.graphs = None
         self.last_t = None   # the last step run: its Top-K is all resident afterwards
+        # attention partials per request of the assembling launch: hit splits +
+        # fetch workgroups per request (the library's rule, restated)
+        ntiles = (K + 63) // 64
+        fpr = min(ntiles, -(-self.pool.sizes.fetch_blocks // B))
+        self.parts = self.pool.sizes.attn_splits + fpr
 
     def step(self, t):
         for l in range(self.wl.layers):
@@ -331,32 +340,53 @@ class Workload:
 
     # -- algorithmic bytes of one kvs_step call -------------------------------
     def algorithmic(self, hits_per_call, misses_per_call):
+        """Algorithmic bytes (and flops) of one kvs_step call, per kernel.
+
+        gather and assemble are bound by the host link: their roofline bytes
+        are the miss rows read over PCIe, their HBM traffic is listed beside
+        them (hit rows read; rows written to the compute buffer and, for
+        misses, to the victim slots; with rows read in place no compute buffer).
+        """
         wl, direct = self.wl, self.args.direct_hot
         B, S, K = wl.batch, wl.slots, wl.topk
-        splits = self.pool.sizes.attn_splits
-        # split partials (written by attention, read by the combine); with one
-        # split the attention writes the bf16 output itself and no combine runs
-        part = B * splits * 16 * (512 + 2) * 4 if splits > 1 else B * 16 * 512 * 2
-        gather_hbm = ROW * misses_per_call if direct else \
-            2 * ROW * hits_per_call + 2 * ROW * misses_per_call
-        return {
-            "diff_lru": {"bound": "hbm", "bytes": B * (20 * K + 4 * S) + 32 * misses_per_call},
-            "gather": {"bound": "pcie", "bytes": ROW * misses_per_call, "hbm_bytes": gather_hbm},
-            "attention": {"bound": "hbm",
-                          "bytes": B * (K * ROW + 16 * 576 * 2) + part + (4 * B * K if direct
-                                                                           else 0),
-                          "flop": B * 2 * 16 * K * (576 + 512)},
-            "combine": {"bound": "hbm", "bytes": part + B * 16 * 512 * 2 if splits > 1 else 0},
-        }
+        h, m = hits_per_call, misses_per_call
+        flop = B * 2 * 16 * K * (576 + 512)
+        q_bytes = B * 16 * 576 * 2
+        out_bytes = B * 16 * 512 * 2
+        part_one = 16 * (512 + 2) * 4
+        copy_hbm = ROW * m if direct else 2 * ROW * h + 2 * ROW * m
+        alg = {"diff_lru": {"bound": "hbm", "bytes": B * (24 * K + 4 * S) + 40 * m}}
+        if self.args.separate:
+            splits = self.pool.sizes.attn_splits
+            # split partials (written by attention, read by the combine); with one
+            # split the attention writes the bf16 output itself and no combine runs
+            part = B * splits * part_one if splits > 1 else out_bytes
+            alg["gather"] = {"bound": "pcie", "bytes": ROW * m, "hbm_bytes": copy_hbm}
+            alg["attention"] = {"bound": "hbm",
+                                "bytes": B * K * ROW + q_bytes + part + (4 * B * K if direct
+                                                                         else 0),
+                                "flop": flop}
+            alg["combine"] = {"bound": "hbm",
+                              "bytes": part + out_bytes if splits > 1 else 0}
+        else:
+            part = B * self.parts * part_one
+            # hit rows are read once from the hot buffer (and written to the
+            # compute buffer); miss rows arrive over PCIe and are written to the
+            # victim slot (and the compute buffer); then the partials
+            hbm = (ROW * h if direct else 2 * ROW * h + 2 * ROW * m) + q_bytes + part
+            alg["assemble"] = {"bound": "pcie", "bytes": ROW * m, "hbm_bytes": hbm,
+                               "flop": flop}
+            alg["combine"] = {"bound": "hbm", "bytes": part + out_bytes}
+        return alg
 
     def kernel_stats(self, kt, alg, names, zc_gbs=None):
         res = {}
         calls = max(1, kt["steps"])
         for name in names:
-            a = alg[name]
             launches = kt["launches"][name]
-            if launches == 0:
+            if launches == 0 or name not in alg:
                 continue
+            a = alg[name]
             per_call = launches / calls
             avg_ms = kt[name] / launches
             b_launch = a["bytes"] / per_call
@@ -477,28 +507,31 @@ class Workload:
                     return None
                 set_b[l, b] = torch.from_numpy(other[:K].astype(np.int32))
         sets = (set_a, set_b)
+        kname = "gather" if self.args.separate else "assemble"
         self.sync_ok()
         _, sa = pool.sync_status()
-        pool.profile_begin(reps * 2 * L, kernels=("gather",))
+        pool.profile_begin(reps * 2 * L, kernels=(kname,))
         for _ in range(reps):
             for tk in sets:
                 for l in range(L):
                     pool.step(l, tk[l], self.q[t, l], self.out[t, l], self.lse[t, l])
         kh = pool.profile_end()
         sb = self.sync_ok()
-        launches = kh["launches"]["gather"]
+        launches = kh["launches"][kname]
         assert launches == reps * 2 * L, launches
         assert sb.misses == sa.misses, "the hit-copy replay fetched rows"
         rows = (sb.hits - sa.hits) / launches
-        avg_ms = kh["gather"] / launches
+        avg_ms = kh[kname] / launches
         gbs = 2 * ROW * rows / (avg_ms * 1e-3) / 1e9
         working_set = (2 * L * B * K + B * K) * ROW    # both sets' hot rows + the compute buffer
         return {"rows_per_launch": int(rows), "bytes_per_launch": int(2 * ROW * rows),
                 "avg_ms": round(avg_ms, 5), "achieved_gbs": round(gbs, 1),
                 "peak_gbs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
-                "working_set_mb": round(working_set / 1e6, 1),
+                "working_set_mb": round(working_set / 1e6, 1), "kernel": kname,
                 "note": "two disjoint all-hit Top-K sets per unit replayed in turn over every "
-                        "layer; working set = both sets' hot rows + the compute buffer"}
+                        "layer; working set = both sets' hot rows + the compute buffer"
+                        + ("" if self.args.separate else
+                           "; the assembling launch also attends over the rows it copies")}
 
     def parity(self, steps, reqs, rec):
         """GPU outputs of steps 0..steps-1 and final maps of the sampled requests
@@ -554,13 +587,15 @@ def summarize(wlo, times, kernels, hits, misses, hit_copy, parity, zc_gbs, wall)
         "parity": parity,
         "wall_s": round(wall, 1),
     }
-    g = kernels.get("gather")
+    g = kernels.get("gather") or kernels.get("assemble")
     if g:
         res["gather_frac_of_63gbs"] = g["frac"]
         res["gather_frac_of_zero_copy_peak"] = round(g["achieved_gbs"] / zc_gbs, 4)
     a = kernels.get("attention")
     if a:
         res["attention_hbm_frac"] = a["frac"]
+    a = a or kernels.get("assemble")
+    if a:
         res["attention_mfma_frac"] = a.get("mfma_frac")
     link_s = ROW * misses / (len(times[0]) - 1) / (zc_gbs * 1e9)
     res["link_ceiling_frac"] = round(link_s * 1e3 / ms, 4)   # step time if only the PCIe bytes
@@ -667,8 +702,8 @@ def main():
             roofline["algorithmic_traffic"] = int((a["hbm_bytes"] + a["bytes"])
                                                   / dom["launches_per_call"])
     misses = cr["misses"]
-    hbm_bytes_step = (alg["diff_lru"]["bytes"] + alg["gather"]["hbm_bytes"]
-                      + alg["attention"]["bytes"] + alg["combine"]["bytes"]) * L
+    hbm_bytes_step = sum(k.get("hbm_bytes", k["bytes"] if k["bound"] == "hbm" else 0)
+                         for k in alg.values()) * L
     wo.close()
     del wo
     cpu = None
@@ -742,7 +777,8 @@ def main():
                    "head_dim": 576, "v_dim": 512, "attn_splits": hr["attn_splits"],
                    "fetch_blocks": args.fetch_blocks, "hit_blocks": args.hit_blocks,
                    "hits_first": bool(args.hits_first), "hip_graph": bool(args.graph),
-                   "direct_hot": bool(args.direct_hot)},
+                   "direct_hot": bool(args.direct_hot),
+                   "separate_attention": bool(args.separate)},
         "decode_steps_per_s": round(1e3 / ms_step, 2),
         "cold_step_ms": round(cr["cold_ms"], 4),
         "miss_rate": round(misses / max(1, cr["hits"] + misses), 5),

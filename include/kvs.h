@@ -81,8 +81,10 @@ extern "C" {
 #define KVS_KERNEL_GATHER 1     /* index copy: misses host -> compute buffer + hot buffer
                                    (PCIe) and hits hot buffer -> compute buffer (HBM) */
 #define KVS_KERNEL_ATTENTION 2  /* split-K sparse MLA decode (MFMA) */
-#define KVS_KERNEL_COMBINE 3    /* merge of the split-K partials */
-#define KVS_NUM_KERNELS 4
+#define KVS_KERNEL_COMBINE 3    /* merge of the attention partials */
+#define KVS_KERNEL_ASSEMBLE 4   /* index copy and attention in one launch (default): misses
+                                   over PCIe, hits within HBM, one partial per workgroup */
+#define KVS_NUM_KERNELS 5
 
 /*
  * Shape of a pool.  B requests x L layers = B*L units; each unit has its own
@@ -98,9 +100,15 @@ typedef struct kvs_config {
   int32_t head_dim;     /* must be KVS_HEAD_DIM */
   int32_t v_dim;        /* must be KVS_V_DIM */
   float scale;          /* softmax scale > 0, e.g. 1/sqrt(576) */
-  int32_t attn_splits;  /* token splits per request in attention, 1..64; 0 = library's choice */
-  int32_t fetch_blocks; /* workgroups that fetch misses over PCIe, 1..65535; 0 = library's choice */
-  int32_t hit_blocks;   /* workgroups that copy hits within HBM, 1..65535; 0 = library's choice */
+  int32_t attn_splits;  /* token splits per request in attention, 1..64 and at most ceil(K/64):
+                           the hit workgroups per request of the assembling launch (each
+                           attends over its share of the hits), or the attention's splits
+                           with KVS_FLAG_SEPARATE_ATTENTION; 0 = library's choice */
+  int32_t fetch_blocks; /* workgroups that fetch misses over PCIe, 1..65535, spread evenly over
+                           the requests (assembling launch: at most ceil(K/64) per request);
+                           0 = library's choice */
+  int32_t hit_blocks;   /* KVS_FLAG_SEPARATE_ATTENTION: workgroups that copy hits within HBM,
+                           1..65535; 0 = library's choice.  Unused otherwise. */
   int32_t flags;        /* KVS_FLAG_* bits; 0 = default */
 } kvs_config;
 
@@ -135,6 +143,14 @@ typedef struct kvs_config {
  * launch per step that reads each unit's maps whole (4 B per token and
  * 10 B per slot): a debugging aid, not for timed runs. */
 #define KVS_FLAG_CHECK 8
+/* kvs_config.flags: run the index copy and the attention as separate launches
+ * (gather, then attention over the complete compute buffer, then the merge of
+ * its token splits).  By default one assembling launch does both: workgroups
+ * that fetch misses over PCIe attend over the rows they fetched, workgroups
+ * that copy hits attend over the hits while the host link delivers the
+ * misses, and a merge launch combines their partials.  Results are identical
+ * within rounding; the compute buffer holds the same bytes either way. */
+#define KVS_FLAG_SEPARATE_ATTENTION 16
 
 /* Bytes each caller buffer must hold (see kvs_buffers). */
 typedef struct kvs_sizes {
@@ -144,7 +160,7 @@ typedef struct kvs_sizes {
   uint64_t cbuf_bytes;      /* B*K*576*2: compute buffer of one step, device (0 with
                                KVS_FLAG_DIRECT_HOT) */
   uint64_t scratch_bytes;   /* per-step lists and attention partials, device */
-  int32_t attn_splits;      /* the split count these sizes assume */
+  int32_t attn_splits;      /* the resolved kvs_config.attn_splits these sizes assume */
   int32_t fetch_blocks;     /* resolved kvs_config.fetch_blocks */
 } kvs_sizes;
 
@@ -264,9 +280,10 @@ int kvs_append(kvs_pool* pool, int32_t layer, const void* rows, const int64_t* p
                void* stream);
 
 /* Lifecycle "fetch + write-back" and the Top-K attention of one layer for all
- * B requests: kernel launches on `stream` only (diff, gather, attention, and a
- * merge of the attention's token splits when kvs_sizes.attn_splits > 1), no
- * host synchronisation, no device-to-host copy, no other stream.
+ * B requests: kernel launches on `stream` only (diff, the assembling launch and
+ * the merge of its partials; with KVS_FLAG_SEPARATE_ATTENTION diff, gather,
+ * attention, and a merge when kvs_sizes.attn_splits > 1), no host
+ * synchronisation, no device-to-host copy, no other stream.
  *   topk [B][K] int32, device, 4-byte aligned: request b's Top-K token indices,
  *        unique, in [0, N) (with KVS_FLAG_PADDED_TOPK also -1 = empty entry).
  *   q    [B][16][576] bf16, device, 16-byte aligned: queries.

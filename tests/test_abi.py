@@ -71,10 +71,17 @@ def test_query_sizes_arithmetic():
     # maps: tok2slot + slot2tok + last_used + order (+ small counters)
     assert s.meta_bytes >= 64 * (16384 * 4 + 4096 * 10)
     assert s.meta_bytes < 64 * (16384 * 4 + 4096 * 10) + 64 * 64 + 4096
-    assert s.attn_splits == 4
-    # slot_of, miss_pos, victims, evicted, row_slot [B][K] int32; counts; partials
-    per = 5 * 64 * 2048 * 4 + 64 * 16 + 64 * 4 * 16 * (512 + 2) * 4
-    assert per <= s.scratch_bytes < per + 8 * 256
+    # assembling launch (default): 128 hit and 128 fetch workgroups in all, so
+    # 2 of each per request and 4 partials per request
+    assert s.attn_splits == 2 and s.fetch_blocks == 128
+    # slot_of, miss_pos, victims, evicted, row_slot, hit_pos, hit_slot,
+    # miss_tok [B][K] int32; counts; partials
+    per = 8 * 64 * 2048 * 4 + 64 * 16 + 64 * 4 * 16 * (512 + 2) * 4
+    assert per <= s.scratch_bytes < per + 12 * 256
+    sep = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096,
+                                          topk=2048, flags=kvs.KVS_FLAG_SEPARATE_ATTENTION))
+    assert sep.attn_splits == 4 and sep.fetch_blocks == 256   # the separate path's split fit
+    assert per <= sep.scratch_bytes < per + 12 * 256
     d = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096,
                                         topk=2048, flags=kvs.KVS_FLAG_DIRECT_HOT))
     assert d.cbuf_bytes == 0 and d.hot_bytes == s.hot_bytes
@@ -84,7 +91,7 @@ def test_query_sizes_arithmetic():
     dict(batch=0), dict(layers=0), dict(topk=0), dict(slots=100, topk=200),
     dict(context=100, topk=200, slots=300), dict(slots=16385), dict(topk=8193, slots=9000),
     dict(heads=8), dict(head_dim=512), dict(v_dim=576), dict(scale=0.0),
-    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=16), dict(context=2**31),
+    dict(scale=float("inf")), dict(attn_splits=65), dict(flags=32), dict(context=2**31),
     dict(fetch_blocks=-1), dict(fetch_blocks=65536), dict(hit_blocks=-1), dict(hit_blocks=70000),
     dict(attn_splits=33),   # more splits than 64-token tiles (K = 2048 -> 32)
 ])
@@ -134,7 +141,8 @@ def test_null_pool_calls_are_rejected():
 def test_padded_flag_accepted():
     cfg = kvs.make_config(batch=2, layers=1, context=4096, slots=512, topk=256,
                           flags=kvs.KVS_FLAG_PADDED_TOPK | kvs.KVS_FLAG_HITS_FIRST
-                          | kvs.KVS_FLAG_DIRECT_HOT | kvs.KVS_FLAG_CHECK)
+                          | kvs.KVS_FLAG_DIRECT_HOT | kvs.KVS_FLAG_CHECK
+                          | kvs.KVS_FLAG_SEPARATE_ATTENTION)
     out = kvs.kvs_sizes()
     assert kvs.lib().kvs_query_sizes(ctypes.byref(cfg), ctypes.byref(out)) == kvs.KVS_OK
 
@@ -149,10 +157,28 @@ def test_strerror():
 
 def test_fetch_blocks_resolve():
     s = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096, topk=2048))
-    assert s.fetch_blocks == 256
-    s = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096, topk=2048,
-                                        fetch_blocks=128))
     assert s.fetch_blocks == 128
+    s = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096, topk=2048,
+                                        fetch_blocks=300))
+    assert s.fetch_blocks == 300
+    s = kvs.query_sizes(kvs.make_config(batch=64, layers=1, context=16384, slots=4096, topk=2048,
+                                        flags=kvs.KVS_FLAG_SEPARATE_ATTENTION))
+    assert s.fetch_blocks == 256
+
+
+@pytest.mark.parametrize("batch,topk,hit_splits", [
+    (1, 256, 4),      # 128 hit workgroups wanted, but only 4 tiles of 64
+    (4, 2048, 32),    # 32 per request = 32 tiles
+    (32, 2048, 4),
+    (64, 2048, 2),
+    (192, 2048, 1),
+    (3, 8192, 43),    # ceil(128 / 3)
+    (1, 8192, 64),    # at most 64
+])
+def test_default_hit_splits(batch, topk, hit_splits):
+    s = kvs.query_sizes(kvs.make_config(batch=batch, layers=1, context=20000, slots=topk,
+                                        topk=topk))
+    assert s.attn_splits == hit_splits
 
 
 def test_graph_calls_reject_null():

@@ -248,6 +248,23 @@ def test_topk_3000_slots_6000_every_unit(mode):
     assert stats.evictions > 0
 
 
+# ---------------------------------------------------------------- separate launches
+
+@pytest.mark.parametrize("mode", ["default", "direct", "padded", "padded_direct"])
+@pytest.mark.parametrize("shape", [
+    dict(batch=3, layers=1, context=5000, slots=700, topk=300, fresh_rate=0.3),
+    dict(batch=2, layers=3, context=3000, slots=1100, topk=1025, fresh_rate=0.2),
+    dict(batch=3, layers=2, context=20000, slots=6000, topk=3000, fresh_rate=0.4),
+], ids=["k300", "k1025_l3", "k3000"])
+def test_separate_attention_every_unit(shape, mode):
+    # gather, attention over the complete compute buffer and merge as separate
+    # launches: the same results as the assembling launch, checked the same way
+    import token_level_gather_amd as kvs
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="separate", steps=6, **shape)
+    flags = kvs.KVS_FLAG_SEPARATE_ATTENTION | (_direct() if "direct" in mode else 0)
+    _case(wl, wl.steps, range(wl.batch), padded="padded" in mode, flags=flags)
+
+
 @pytest.mark.parametrize("topk,splits", [
     (300, 1),    # 5 tiles in one split: two full pairs and an odd tail
     (300, 2),    # 2 + 3 tiles
@@ -272,6 +289,20 @@ def test_padded_topk_every_unit(shape):
     # requests cycle through tail / scatter / all-empty / no padding
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="padded", steps=6, **shape)
     _case(wl, wl.steps, range(wl.batch), padded=True)
+
+
+@pytest.mark.parametrize("fetch_blocks,splits", [
+    (1, 1),      # fewer fetch workgroups than requests: still one per request
+    (3, 2),      # one per request
+    (64, 17),    # capped at ceil(K / 64) = 17 per request; many hit splits with no tile
+    (7, 5),      # 3 per request; passes x, x + 3, ...
+])
+def test_assemble_fetch_and_hit_counts(fetch_blocks, splits):
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="assemble_counts", batch=3, context=4000,
+                                                  slots=1100, topk=1025, steps=5,
+                                                  fresh_rate=0.6)
+    h, _ = _case(wl, wl.steps, range(wl.batch), fetch_blocks=fetch_blocks, attn_splits=splits)
+    assert h.pool.sizes.attn_splits == splits
 
 
 def test_padded_topk_explicit_splits():
@@ -722,6 +753,8 @@ def test_random_small_configs_every_unit(seed):
         flags |= kvs.KVS_FLAG_DIRECT_HOT
     if rng.random() < 0.3:
         flags |= kvs.KVS_FLAG_HITS_FIRST
+    if rng.random() < 0.3:
+        flags |= kvs.KVS_FLAG_SEPARATE_ATTENTION
     padded = bool(rng.random() < 0.4)
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(
         name=f"rand{seed}", batch=B, layers=L, context=N, slots=S, topk=K, steps=4,
@@ -731,15 +764,17 @@ def test_random_small_configs_every_unit(seed):
     _case(wl, wl.steps, range(B), padded=padded, flags=flags, attn_splits=splits)
 
 
+@pytest.mark.parametrize("separate", [False, True])
 @pytest.mark.parametrize("direct", [False, True])
-def test_invalid_topk_single_split_writes_zero_output(direct):
-    # one split: the attention writes out / lse itself (no combine), also for a
-    # request whose Top-K is rejected
+def test_invalid_topk_single_split_writes_zero_output(direct, separate):
+    # one split: with separate launches the attention writes out / lse itself
+    # (no combine), also for a request whose Top-K is rejected
     import token_level_gather_amd as kvs
     torch = _torch()
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(batch=3, context=3000, slots=500, topk=200,
                                                   steps=4)
-    h = Harness(wl, wl.steps, range(3), attn_splits=1, flags=_direct() if direct else 0)
+    flags = (_direct() if direct else 0) | (kvs.KVS_FLAG_SEPARATE_ATTENTION if separate else 0)
+    h = Harness(wl, wl.steps, range(3), attn_splits=1, flags=flags)
     try:
         assert h.pool.sizes.attn_splits == 1
         for t in range(2):

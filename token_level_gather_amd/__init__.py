@@ -29,11 +29,12 @@ KVS_EHIP_BASE = -1000
 
 HEADS, HEAD_DIM, V_DIM = 16, 576, 512
 ROW_BYTES = HEAD_DIM * 2
-KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine")
+KERNEL_NAMES = ("diff_lru", "gather", "attention", "combine", "assemble")
 KVS_FLAG_HITS_FIRST = 1
 KVS_FLAG_PADDED_TOPK = 2
 KVS_FLAG_DIRECT_HOT = 4
 KVS_FLAG_CHECK = 8
+KVS_FLAG_SEPARATE_ATTENTION = 16
 PROBE_SINK_WORDS = 65536
 
 # Every exported symbol of include/kvs.h.

@@ -23,6 +23,10 @@ static uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 // Attention workgroups resident at once: one per compute unit of an MI355X.
 constexpr int kAttnWorkgroupsPerRound = 256;
+// Assembling launch defaults: fetch workgroups (512 threads, spread over the
+// requests) and hit workgroups in total.
+constexpr int kAssembleFetchBlocks = 128;
+constexpr int kAssembleHitBlocks = 128;
 // A workgroup's start-up (its first two tiles arriving during the all-CU
 // burst), in tile-times: fitted to measured split sweeps at 4, 32, 64 and 192
 // requests x 2048 selected tokens.
@@ -41,15 +45,32 @@ int make_layout(const kvs_config* c, Layout* lay) {
   if (c->fetch_blocks < 0 || c->fetch_blocks > 65535) return KVS_EINVAL;
   if (c->hit_blocks < 0 || c->hit_blocks > 65535) return KVS_EINVAL;
   if ((c->flags & ~(KVS_FLAG_HITS_FIRST | KVS_FLAG_PADDED_TOPK | KVS_FLAG_DIRECT_HOT |
-                    KVS_FLAG_CHECK)) != 0)
+                    KVS_FLAG_CHECK | KVS_FLAG_SEPARATE_ATTENTION)) != 0)
     return KVS_EINVAL;
   if ((int64_t)c->batch * c->layers > 0x7fffffffLL) return KVS_EINVAL;
 
   const uint64_t B = c->batch, L = c->layers, N = c->context, S = c->slots, K = c->topk;
   const uint64_t U = B * L;
   const int ntiles = (int)((K + 63) / 64);
+  const bool separate = (c->flags & KVS_FLAG_SEPARATE_ATTENTION) != 0;
   int splits = c->attn_splits;
-  if (splits == 0) {
+  int fetch_blocks, fetch_per_req = 0, parts;
+  if (!separate) {
+    // one assembling launch: fetch workgroups (one CU each for the whole
+    // fetch) and hit workgroups (one CU each, several rounds); each writes
+    // one attention partial
+    fetch_blocks = c->fetch_blocks == 0 ? kAssembleFetchBlocks : c->fetch_blocks;
+    fetch_per_req = (int)((fetch_blocks + B - 1) / B);
+    if (fetch_per_req > ntiles) fetch_per_req = ntiles;
+    if (splits == 0) {
+      splits = (int)((kAssembleHitBlocks + B - 1) / B);
+      if (splits > ntiles) splits = ntiles;
+      if (splits > 64) splits = 64;
+    } else if (splits > ntiles) {
+      return KVS_EINVAL;
+    }
+    parts = splits + fetch_per_req;
+  } else if (splits == 0) {
     // An attention workgroup holds one CU (its LDS tile), so a launch runs in
     // rounds of 256 workgroups, and every workgroup first waits for its first
     // two tiles.  Pick the split count with the fewest tile-times, rounds x
@@ -69,9 +90,12 @@ int make_layout(const kvs_config* c, Layout* lay) {
   } else if (splits > ntiles) {
     return KVS_EINVAL;
   }
-  // 256 fetch workgroups (1 per CU) keep the host link saturated; more only
-  // add outstanding PCIe reads, which slow the HBM traffic beside them
-  const int fetch_blocks = c->fetch_blocks == 0 ? 256 : c->fetch_blocks;
+  if (separate) {
+    // 256 fetch workgroups (1 per CU) keep the host link saturated; more only
+    // add outstanding PCIe reads, which slow the HBM traffic beside them
+    fetch_blocks = c->fetch_blocks == 0 ? 256 : c->fetch_blocks;
+    parts = splits;
+  }
 
   lay->B = c->batch;
   lay->L = c->layers;
@@ -79,7 +103,9 @@ int make_layout(const kvs_config* c, Layout* lay) {
   lay->K = c->topk;
   lay->N = c->context;
   lay->splits = splits;
+  lay->parts = parts;
   lay->fetch_blocks = fetch_blocks;
+  lay->fetch_per_req = fetch_per_req;
   lay->hit_blocks = c->hit_blocks;
   lay->flags = c->flags;
 
@@ -105,8 +131,11 @@ int make_layout(const kvs_config* c, Layout* lay) {
   lay->evicted = take(B * K * 4);
   lay->counts = take(B * 16);
   lay->row_slot = take(B * K * 4);
-  lay->part_o = take(B * (uint64_t)splits * kHeads * kVDim * 4);
-  lay->part_ml = take(B * (uint64_t)splits * kHeads * 2 * 4);
+  lay->hit_pos = take(B * K * 4);
+  lay->hit_slot = take(B * K * 4);
+  lay->miss_tok = take(B * K * 4);
+  lay->part_o = take(B * (uint64_t)parts * kHeads * kVDim * 4);
+  lay->part_ml = take(B * (uint64_t)parts * kHeads * 2 * 4);
   lay->scratch_bytes = o;
   return KVS_OK;
 }
@@ -208,6 +237,9 @@ static void bind_scratch(const Layout& lay, uint8_t* scr, DevPtrs* d) {
   d->evicted = (int32_t*)(scr + lay.evicted);
   d->counts = (int32_t*)(scr + lay.counts);
   d->row_slot = (int32_t*)(scr + lay.row_slot);
+  d->hit_pos = (int32_t*)(scr + lay.hit_pos);
+  d->hit_slot = (int32_t*)(scr + lay.hit_slot);
+  d->miss_tok = (int32_t*)(scr + lay.miss_tok);
   d->part_o = (float*)(scr + lay.part_o);
   d->part_ml = (float*)(scr + lay.part_ml);
 }
@@ -404,14 +436,23 @@ static int enqueue_step(kvs_pool* p, const DevPtrs& d, int32_t layer, const int3
   KVS_TRY_HIP(timed(p, KVS_KERNEL_DIFF_LRU, s, [&] { return launch_diff_lru(L, d, layer, topk, s); }));
   // optional verification of the updated state (not timed)
   if (L.flags & KVS_FLAG_CHECK) KVS_TRY_HIP(launch_check_state(L, d, layer, s));
-  // index copy: misses over PCIe (fetch + write-back) and hits within HBM
-  KVS_TRY_HIP(timed(p, KVS_KERNEL_GATHER, s, [&] { return launch_gather(L, d, layer, topk, s); }));
-  // Top-K sparse attention over the compute buffer
-  KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s, [&] {
-    return launch_attention(L, d, layer, (const uint16_t*)q, p->cfg.scale, (uint16_t*)out, lse,
-                            s);
-  }));
-  if (L.splits > 1)
+  if (L.flags & KVS_FLAG_SEPARATE_ATTENTION) {
+    // index copy: misses over PCIe (fetch + write-back) and hits within HBM
+    KVS_TRY_HIP(timed(p, KVS_KERNEL_GATHER, s,
+                      [&] { return launch_gather(L, d, layer, topk, s); }));
+    // Top-K sparse attention over the compute buffer
+    KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s, [&] {
+      return launch_attention(L, d, layer, (const uint16_t*)q, p->cfg.scale, (uint16_t*)out,
+                              lse, s);
+    }));
+  } else {
+    // index copy (misses over PCIe with write-back, hits within HBM) and the
+    // attention over both, one partial per workgroup
+    KVS_TRY_HIP(timed(p, KVS_KERNEL_ASSEMBLE, s, [&] {
+      return launch_assemble(L, d, layer, (const uint16_t*)q, p->cfg.scale, s);
+    }));
+  }
+  if (L.parts > 1 || !(L.flags & KVS_FLAG_SEPARATE_ATTENTION))
     KVS_TRY_HIP(timed(p, KVS_KERNEL_COMBINE, s,
                       [&] { return launch_combine(L, d, (uint16_t*)out, lse, s); }));
   if (p->prof_steps < p->prof_max_steps) ++p->prof_steps;

@@ -17,8 +17,12 @@ constexpr int kVDim = KVS_V_DIM;                 // 512
 
 // Byte offsets of every array inside the caller's meta and scratch buffers.
 struct Layout {
-  int32_t B, L, S, K, splits;
+  int32_t B, L, S, K;
+  int32_t splits;        // attention token splits per request: the hit splits of the
+                         // assembling launch, or the splits of the separate attention
+  int32_t parts;         // attention partials per request merged by the combine
   int32_t fetch_blocks;  // miss-fetch workgroups of the gather launch
+  int32_t fetch_per_req; // assembling launch: fetch workgroups per request
   int32_t hit_blocks;    // hit-copy workgroups of the gather launch (0 = one per 32 positions)
   int32_t flags;
   int64_t N;
@@ -38,8 +42,11 @@ struct Layout {
   uint64_t evicted;    // int32 [B][K]
   uint64_t counts;     // int32 [B][4]: n_hit, n_miss, n_evict, valid
   uint64_t row_slot;   // int32 [B][K]: slot of position i's row after the step, -1 empty
-  uint64_t part_o;     // float [B][splits][16][512]
-  uint64_t part_ml;    // float [B][splits][16][2]: running max (log2 units), sum
+  uint64_t hit_pos;    // int32 [B][K]: Top-K positions of the hits, Top-K order
+  uint64_t hit_slot;   // int32 [B][K]: their slots
+  uint64_t miss_tok;   // int32 [B][K]: tokens of the misses, Top-K order
+  uint64_t part_o;     // float [B][parts][16][512]
+  uint64_t part_ml;    // float [B][parts][16][2]: running max (log2 units), sum
   uint64_t scratch_bytes;
 };
 
@@ -71,6 +78,9 @@ struct DevPtrs {
   int32_t* evicted;
   int32_t* counts;
   int32_t* row_slot;
+  int32_t* hit_pos;
+  int32_t* hit_slot;
+  int32_t* miss_tok;
   float* part_o;
   float* part_ml;
 };
@@ -89,6 +99,10 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, cons
                             float scale, uint16_t* out, float* lse, hipStream_t s);
 hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
                           hipStream_t s);
+// The index copy and the attention in one launch (default): fetch workgroups
+// attend over the misses they fetch, hit workgroups over the resident hits.
+hipError_t launch_assemble(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* q,
+                           float scale, hipStream_t s);
 hipError_t launch_clear_status(const DevPtrs& d, hipStream_t s);
 hipError_t launch_check_state(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s);
 hipError_t launch_host_read_probe(const void* src, long long chunks, uint32_t* sink,

@@ -153,6 +153,9 @@ struct DiffArgs {
   int32_t* evicted;        // [B][K]
   int32_t* counts;         // [B][4]
   int32_t* row_slot;       // [B][K]: slot of position i's row after the step, -1 empty
+  int32_t* hit_pos;        // [B][K]: Top-K positions of the hits, in Top-K order
+  int32_t* hit_slot;       // [B][K]: their slots
+  int32_t* miss_tok;       // [B][K]: tokens of the misses, in Top-K order
   long long N;
   int S, K, L, layer, hash_bits;
   int padded;              // 1: a Top-K entry of -1 is empty
@@ -209,12 +212,14 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   const int p0 = tid * spt;
 
   // LDS: per-slot flag [S] u8 (1 = hit, 2 = victim) | token hash set [H] i32,
-  //      reused after validation as miss list [K] + victims [K]
+  //      reused after validation as miss positions [K] + victims [K] + miss
+  //      tokens [K] (the region holds max(H, 3K) words)
   uint8_t* flag = smem;
   unsigned* flagw = reinterpret_cast<unsigned*>(smem);   // the same flags, 4 per word
   int32_t* hash = reinterpret_cast<int32_t*>(smem + ((S + 15) & ~15));
   int32_t* lmiss = hash;
   int32_t* lvict = hash + K;
+  int32_t* lmtok = hash + 2 * K;
 
   int32_t* tok2slot = a.tok2slot + u * a.N;
   int32_t* slot2tok = a.slot2tok + u * S;
@@ -339,7 +344,10 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
-    if (j < kpt && i < K && my_slot[j] == -1) lmiss[r++] = i;
+    if (j < kpt && i < K && my_slot[j] == -1) {
+      lmiss[r] = i;
+      lmtok[r++] = my_tok[j];
+    }
   }
 
   // 3. victims: the first m non-hit slots of the LRU order, evicted here; the
@@ -374,19 +382,34 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   __syncthreads();
 
   // 4. the n_hit + m touched slots (hits and victims, all stamped t) close the
-  //    order, ascending by slot
+  //    order, ascending by slot.  The same scan counts the empty entries
+  //    (high 16 bits), which places each thread's hits in the hit list.
   cnt = 0;
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
     const int s = p0 + q;
     if (q < spt && s < S && flag[s] != 0) ++cnt;
   }
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (j < kpt && i0 + j < K && my_slot[j] == -2) cnt += 1 << 16;
   int n_touched;
-  r = S - (n_hit + m) + wg_exclusive_scan(cnt, wtot, n_touched);
+  const int ex2 = wg_exclusive_scan(cnt, wtot, n_touched);
+  r = S - (n_hit + m) + (ex2 & 0xffff);
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
     const int s = p0 + q;
     if (q < spt && s < S && flag[s] != 0) gorder[r++] = (uint16_t)s;
+  }
+  // hits in Top-K order: entries before this thread's, less its misses and empties
+  r = i0 - (ex & 0xffff) - (ex2 >> 16);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = i0 + j;
+    if (j < kpt && i < K && my_slot[j] >= 0) {
+      a.hit_pos[bk + r] = i;
+      a.hit_slot[bk + r++] = my_slot[j];
+    }
   }
   if (tid == 0) {   // n_evict is final after the barriers inside the scan
     a.counts[4 * b + 0] = n_hit;
@@ -404,12 +427,13 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   // 5. map update: the j-th miss takes the j-th victim
   for (int j = tid; j < m; j += kDiffThreads) {
     const int i = lmiss[j];
-    const int tok = topk[i];
+    const int tok = lmtok[j];
     const int v = lvict[j];
     slot2tok[v] = tok;
     tok2slot[tok] = v;
     lu[v] = t;
     a.miss_pos[bk + j] = i;
+    a.miss_tok[bk + j] = tok;
     a.victims[bk + j] = v;
     a.row_slot[bk + i] = v;
   }
@@ -534,7 +558,7 @@ constexpr int kAttnItems = kRowChunks / 8;      // 9 chunks / thread, 8 threads 
 constexpr int kKSteps = kRowElems / 32;         // 18 MFMA k-steps over 576 dims
 constexpr int kKHalf = kKSteps / 2;             // each Q.K^T wave takes half of them
 constexpr int kPRow = kTile + 8;                // bf16 P row stride (144 B)
-constexpr int kMaxSplits = 64;
+constexpr int kMaxParts = 256;   // attention partials per request merged by the combine
 // Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: data format
 // 32 bits, everything else zero.  Untyped loads ignore the format, but a zero
 // format would mark the resource invalid.
@@ -569,19 +593,125 @@ struct AttnArgs {
   float* lse;               // [B][16] or null; written here only when out is
 };
 
-// One workgroup = (split sp, request b): the tiles [tb, te) of request b's
-// gathered rows.  MFMA operand layout used (v_mfma_f32_16x16x32_bf16): lane l
-// supplies row (l % 16) of A and column (l % 16) of B with 8 consecutive
-// k-values selected by l / 16; the result lane l holds rows 4*(l/16)+j,
-// column l % 16.  Both operands of each product take their k-values through
-// the same (l/16, j) -> k assignment, so the sum is over the intended k.
-//
-// Wave roles per 64-token tile:
+// One 64-row tile in LDS: scores of the 16 heads against every row, the
+// online softmax update and P.V.  Rows at or past n_valid, and rows whose mark
+// equals pad_mark, score -inf.  Starts after the barrier that published the
+// tile and ends with a barrier after which the tile may be overwritten.
+// MFMA operand layout used (v_mfma_f32_16x16x32_bf16): lane l supplies row
+// (l % 16) of A and column (l % 16) of B with 8 consecutive k-values selected
+// by l / 16; the result lane l holds rows 4*(l/16)+j, column l % 16.  Both
+// operands of each product take their k-values through the same
+// (l/16, j) -> k assignment, so the sum is over the intended k.
+// Wave roles:
 //   Q.K^T   wave w: tokens 16*(w % 4) .. +16, k-steps 9*(w / 4) .. +9 (two
 //           partial score tiles per token block, summed in the softmax);
 //   softmax waves 0..3: 16 lanes (one DPP row) per head, 4 tokens each;
 //   P.V     wave w: value columns 64*w .. +64 (4 MFMA column tiles), the
 //           value operand through transpose LDS reads.
+// State per thread: qf (Q fragments, head r16, this wave's k-half), m_run /
+// l_run (running max in log2 units and sum of its head, replicated over the
+// head's 16 softmax threads), acc (O[h = 4g + j][e = 64w + 16nt + r16]).
+__device__ __forceinline__ void attend_tile(unsigned char* kv, float* sc, uint16_t* pb,
+                                            float* alpha_s, const int* vmark,
+                                            const bf16x8 (&qf)[kKHalf], float& m_run,
+                                            float& l_run, f32x4 (&acc)[4], int n_valid,
+                                            int pad_mark, float scale_log2) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int tt = wave & 3, kh = wave >> 2;
+  const bool sm_on = tid < kHeads * 16;
+  const int c4 = (tid & 15) * 4;
+  // partial scores of 16 tokens over half of the 576 dims
+  {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    const int krow_i = tt * 16 + r16;
+    const unsigned char* krow = kv + krow_i * kLdsRow;
+    const int ksw = lds_swz(krow_i);
+#pragma unroll
+    for (int ks = 0; ks < kKHalf; ++ks) {
+      const int chunk = (kh * kKHalf + ks) * 4 + g;   // dims chunk*8 .. +7
+      const bf16x8 kf =
+          as_bf16x8(*reinterpret_cast<const u32x4*>(krow + (chunk ^ ksw) * 16));
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kf, s, 0, 0, 0);
+    }
+    float* sck = sc + kh * kHeads * kTile;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sck[(4 * g + j) * kTile + tt * 16 + r16] = s[j];
+  }
+  __syncthreads();
+
+  // online softmax: head h = tid / 16 (threads 0..255, whole waves), tokens
+  // c4 .. c4 + 3; rows past n_valid and empty entries score -inf.  The max and
+  // the sum stay inside one 16-lane DPP row.
+  if (sm_on) {
+    const int h = tid >> 4;
+    const float4 s0 = *reinterpret_cast<const float4*>(sc + h * kTile + c4);
+    const float4 s1 = *reinterpret_cast<const float4*>(sc + kHeads * kTile + h * kTile + c4);
+    const float z[4] = {s0.x + s1.x, s0.y + s1.y, s0.z + s1.z, s0.w + s1.w};
+    const int4 mk = *reinterpret_cast<const int4*>(vmark + c4);
+    const int mks[4] = {mk.x, mk.y, mk.z, mk.w};
+    float x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      x[k] = c4 + k < n_valid && mks[k] != pad_mark ? z[k] * scale_log2 : -INFINITY;
+    const float m_new = fmaxf(m_run, row16_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))));
+    // no scored token yet (empty entries only): keep every weight at 0
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_ref);
+    float p[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = exp2f(x[k] - m_ref);
+    l_run = l_run * alpha + row16_sum((p[0] + p[1]) + (p[2] + p[3]));
+    m_run = m_new;
+    *reinterpret_cast<uint2*>(pb + h * kPRow + c4) =
+        make_uint2((uint32_t)f32_to_bf16_rne(p[0]) | ((uint32_t)f32_to_bf16_rne(p[1]) << 16),
+                   (uint32_t)f32_to_bf16_rne(p[2]) | ((uint32_t)f32_to_bf16_rne(p[3]) << 16));
+    if ((tid & 15) == 0) alpha_s[h] = alpha;
+  }
+  __syncthreads();
+
+  // P.V: wave w owns value columns [64w, 64w + 64) as 4 MFMA column tiles
+  {
+    float al[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) al[j] = alpha_s[4 * g + j];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[nt][j] *= al[j];
+    // B operand by transpose reads (ds_read_b64_tr_b16): within each
+    // 16-lane block, lane c receives element c % 4 of the 8-byte row piece
+    // addressed by lane 4j + c / 4, for j = 0..3.  Lane a = r16 of block g
+    // therefore addresses V[row0 + a / 4][n0 + 4 (a % 4) .. +3], and lane
+    // (g, r16) receives V[row0 + j][n0 + r16], j = 0..3: four consecutive
+    // k-values of column n0 + r16.  Two reads (rows +0 and +4) give the 8
+    // k-values 8g .. 8g + 7 of the MFMA's B operand.
+    const int tr_row = g * 8 + (r16 >> 2);
+    const int tr_sub = (r16 & 1) * 8;            // byte offset inside the 16-byte chunk
+#pragma unroll
+    for (int kk = 0; kk < kTile / 32; ++kk) {
+      const bf16x8 pf =
+          as_bf16x8(*reinterpret_cast<const u32x4*>(pb + r16 * kPRow + kk * 32 + g * 8));
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int chunk = wave * 8 + nt * 2 + ((r16 & 3) >> 1);   // column (n0 + 4(a%4)) / 8
+        const int r0 = kk * 32 + tr_row, r1 = r0 + 4;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(kv + r0 * kLdsRow + ((chunk ^ lds_swz(r0)) * 16) + tr_sub));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(kv + r1 * kLdsRow + ((chunk ^ lds_swz(r1)) * 16) + tr_sub));
+        const u16x8 vv = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                          (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            pf, __builtin_bit_cast(bf16x8, vv), acc[nt], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// One workgroup = (split sp, request b): the tiles [tb, te) of request b's
+// gathered rows, each through attend_tile.
 // DIRECT: rows read in place from the hot buffer at row_slot (a separate
 // instantiation, so the assembled-buffer path carries no slot loads at all).
 template <bool DIRECT>
@@ -606,7 +736,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int tt = wave & 3, kh = wave >> 2;
+  const int kh = wave >> 2;
   const int K = a.K;
   const int ntiles = (K + kTile - 1) / kTile;
   const int tb = (int)((long long)sp * ntiles / a.splits);
@@ -650,9 +780,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
       (void*)((DIRECT ? a.row_slot : a.slot_of) + (long long)b * K), (short)0,
       a.padded ? K * 4 : 0, kBufRsrcWord3);
   const int pad_mark = DIRECT ? -1 : -2;
-  // softmax: threads 0..255, 16 lanes per head (one DPP row), tokens c4 .. c4 + 3
+  // softmax: threads 0..255, 16 lanes per head (one DPP row)
   const bool sm_on = tid < kHeads * 16;
-  const int c4 = (tid & 15) * 4;
   auto load_slot = [&](int tile) -> int {
     if (!DIRECT) return 0;
     return __builtin_amdgcn_raw_buffer_load_b32(
@@ -681,94 +810,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   // one tile from LDS: scores, online softmax, P.V; ends with a barrier after
   // which the LDS tile may be overwritten
   auto compute = [&](int tile) {
-    // partial scores of 16 tokens over half of the 576 dims
-    {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      const int krow_i = tt * 16 + r16;
-      const unsigned char* krow = kv + krow_i * kLdsRow;
-      const int ksw = lds_swz(krow_i);
-#pragma unroll
-      for (int ks = 0; ks < kKHalf; ++ks) {
-        const int chunk = (kh * kKHalf + ks) * 4 + g;   // dims chunk*8 .. +7
-        const bf16x8 kf =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(krow + (chunk ^ ksw) * 16));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kf, s, 0, 0, 0);
-      }
-      float* sck = sc + kh * kHeads * kTile;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sck[(4 * g + j) * kTile + tt * 16 + r16] = s[j];
-    }
-    __syncthreads();
-
-    // online softmax: head h = tid / 16 (threads 0..255, whole waves), tokens
-    // c4 .. c4 + 3; tokens past K and empty entries score -inf.  The max and
-    // the sum stay inside one 16-lane DPP row.
-    if (sm_on) {
-      const int h = tid >> 4;
-      const int tok0 = tile * kTile + c4;
-      const float4 s0 = *reinterpret_cast<const float4*>(sc + h * kTile + c4);
-      const float4 s1 = *reinterpret_cast<const float4*>(sc + kHeads * kTile + h * kTile + c4);
-      const float z[4] = {s0.x + s1.x, s0.y + s1.y, s0.z + s1.z, s0.w + s1.w};
-      const int4 mk = *reinterpret_cast<const int4*>(vmark + c4);
-      const int mks[4] = {mk.x, mk.y, mk.z, mk.w};
-      float x[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        x[k] = tok0 + k < K && mks[k] != pad_mark ? z[k] * a.scale_log2 : -INFINITY;
-      const float m_new = fmaxf(m_run, row16_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))));
-      // no scored token yet (empty entries only): keep every weight at 0
-      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_ref);
-      float p[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) p[k] = exp2f(x[k] - m_ref);
-      l_run = l_run * alpha + row16_sum((p[0] + p[1]) + (p[2] + p[3]));
-      m_run = m_new;
-      *reinterpret_cast<uint2*>(pb + h * kPRow + c4) =
-          make_uint2((uint32_t)f32_to_bf16_rne(p[0]) | ((uint32_t)f32_to_bf16_rne(p[1]) << 16),
-                     (uint32_t)f32_to_bf16_rne(p[2]) | ((uint32_t)f32_to_bf16_rne(p[3]) << 16));
-      if ((tid & 15) == 0) alpha_s[h] = alpha;
-    }
-    __syncthreads();
-
-    // P.V: wave w owns value columns [64w, 64w + 64) as 4 MFMA column tiles
-    {
-      float al[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = alpha_s[4 * g + j];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[nt][j] *= al[j];
-      // B operand by transpose reads (ds_read_b64_tr_b16): within each
-      // 16-lane block, lane c receives element c % 4 of the 8-byte row piece
-      // addressed by lane 4j + c / 4, for j = 0..3.  Lane a = r16 of block g
-      // therefore addresses V[row0 + a / 4][n0 + 4 (a % 4) .. +3], and lane
-      // (g, r16) receives V[row0 + j][n0 + r16], j = 0..3: four consecutive
-      // k-values of column n0 + r16.  Two reads (rows +0 and +4) give the 8
-      // k-values 8g .. 8g + 7 of the MFMA's B operand.
-      const int tr_row = g * 8 + (r16 >> 2);
-      const int tr_sub = (r16 & 1) * 8;            // byte offset inside the 16-byte chunk
-#pragma unroll
-      for (int kk = 0; kk < kTile / 32; ++kk) {
-        const bf16x8 pf =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(pb + r16 * kPRow + kk * 32 + g * 8));
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int chunk = wave * 8 + nt * 2 + ((r16 & 3) >> 1);   // column (n0 + 4(a%4)) / 8
-          const int r0 = kk * 32 + tr_row, r1 = r0 + 4;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(kv + r0 * kLdsRow + ((chunk ^ lds_swz(r0)) * 16) + tr_sub));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(kv + r1 * kLdsRow + ((chunk ^ lds_swz(r1)) * 16) + tr_sub));
-          const u16x8 vv = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
-                            (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              pf, __builtin_bit_cast(bf16x8, vv), acc[nt], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();
+    attend_tile(kv, sc, pb, alpha_s, vmark, qf, m_run, l_run, acc, K - tile * kTile, pad_mark,
+                a.scale_log2);
   };
 
   // tiles two at a time so the register buffers alternate without copies:
@@ -843,15 +886,239 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
 
 }
 
-// Merge of the split partials of (request b, head h):
+// ------------------------------------------------------------------ assemble + attend
+// The index copy and the attention of one layer in one launch.  Two roles:
+//  fetch  workgroup (b, x), x < fetch_per_req: passes of 64 misses of request
+//         b (pass x, x + fetch_per_req, ...): each row read straight from
+//         pinned host memory over PCIe (each wave instruction reads 1 KB of
+//         consecutive host memory), written to cbuf[b][miss_pos_j] and to the
+//         victim slot hot[b][l][v_j], and attended from LDS; partial x + hits.
+//  hits   workgroup (b, x), x < hit_per_req: the x-th share of request b's hit
+//         tiles (64 hits each, Top-K order), read from the hot buffer, written
+//         to cbuf[b][hit_pos_j] and attended; partial x.
+// Hit rows are resident before the step, so their attention runs while the
+// host link delivers the misses; the combine merges every partial of a
+// request.  Hit slots and victim slots are disjoint, so the roles never touch
+// the same hot row.
+struct AssembleArgs {
+  const u32x4* pool;        // host pool (pinned, GPU-mapped) [B][L][N] rows
+  uint16_t* hot;            // [B*L][S][576]
+  uint16_t* cbuf;           // [B][K][576], or null when rows are read in place
+  const uint16_t* q;        // [B][16][576]
+  const int32_t* slot_of;   // [B][K]: -2 marks an empty entry of a padded Top-K
+  const int32_t* hit_pos;   // [B][K]: Top-K positions of the hits, first n_hit valid
+  const int32_t* hit_slot;  // [B][K]: their slots
+  const int32_t* miss_pos;  // [B][K]: Top-K positions of the misses, first n_miss valid
+  const int32_t* miss_tok;  // [B][K]: their tokens
+  const int32_t* victims;   // [B][K]: their victim slots
+  const int32_t* counts;    // [B][4]
+  float* part_o;            // [B][parts][16][512]
+  float* part_ml;           // [B][parts][16][2]
+  long long N;
+  int S, K, L, layer;
+  int fetch_per_req, hit_per_req, parts;   // parts = hit_per_req + fetch_per_req
+  int fetch_wgs;            // fetch_per_req * B
+  int hits_first;           // 1: the hit workgroups take the first grid indices
+  int padded;               // 1: zero the compute-buffer rows of empty entries
+  float scale_log2;
+};
+
+__global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char kv[kTile * kLdsRow];
+  __shared__ float sc[2 * kHeads * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t pb[kHeads * kPRow];
+  __shared__ float alpha_s[kHeads];
+  __shared__ __attribute__((aligned(16))) int vmark[kTile];   // all 0: every listed row is valid
+
+  const int n_wgs = (int)gridDim.x;
+  const int id = a.hits_first ? ((int)blockIdx.x + a.fetch_wgs) % n_wgs : (int)blockIdx.x;
+  const bool fetch = id < a.fetch_wgs;
+  int b, x;
+  if (fetch) {
+    b = id / a.fetch_per_req;
+    x = id - b * a.fetch_per_req;
+  } else {
+    const int h = id - a.fetch_wgs;
+    b = h / a.hit_per_req;
+    x = h - b * a.hit_per_req;
+  }
+  if (a.counts[4 * b + 3] == 0) return;   // invalid Top-K: nothing to copy; the combine zeroes out
+  const int n_hit = a.counts[4 * b + 0], n_miss = a.counts[4 * b + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15, kh = wave >> 2;
+  const int K = a.K;
+  const long long u = (long long)b * a.L + a.layer;
+  const long long bk = (long long)b * K;
+
+  bf16x8 qf[kKHalf];   // Q fragments: head r16, dims (kh*9 + ks)*32 + g*8 .. +7
+  {
+    const u32x4* qh =
+        reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
+#pragma unroll
+    for (int ks = 0; ks < kKHalf; ++ks) qf[ks] = as_bf16x8(qh[(kh * kKHalf + ks) * 4 + g]);
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (tid < kTile) vmark[tid] = 0;
+
+  if (fetch) {
+    // chunk c = 512 jj + tid of the pass's 64 x 72 chunks: row c / 72, column c % 72
+    u32x4* hot = reinterpret_cast<u32x4*>(a.hot);
+    u32x4* cbuf = reinterpret_cast<u32x4*>(a.cbuf);
+    for (int j0 = x * kTile; j0 < n_miss; j0 += a.fetch_per_req * kTile) {
+      u32x4 v[kAttnItems];
+      int pos[kAttnItems], vic[kAttnItems];
+#pragma unroll
+      for (int jj = 0; jj < kAttnItems; ++jj) {
+        const int c = jj * kAttnThreads + tid;
+        const int r = c / kRowChunks;
+        const int col = c - r * kRowChunks;
+        const int jm = j0 + r;
+        v[jj] = u32x4{0u, 0u, 0u, 0u};   // rows past the last miss stay zero in LDS
+        pos[jj] = -1;
+        if (jm < n_miss) {
+          const int tok = a.miss_tok[bk + jm];
+          v[jj] = a.pool[(u * a.N + tok) * kRowChunks + col];
+          pos[jj] = a.miss_pos[bk + jm];
+          vic[jj] = a.victims[bk + jm];
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kAttnItems; ++jj) {
+        const int c = jj * kAttnThreads + tid;
+        const int r = c / kRowChunks;
+        const int col = c - r * kRowChunks;
+        if (pos[jj] >= 0) {
+          hot[(u * a.S + vic[jj]) * kRowChunks + col] = v[jj];
+          if (cbuf != nullptr) cbuf[(bk + pos[jj]) * kRowChunks + col] = v[jj];
+        }
+        *reinterpret_cast<u32x4*>(kv + r * kLdsRow + ((col ^ lds_swz(r)) * 16)) = v[jj];
+      }
+      __syncthreads();
+      attend_tile(kv, sc, pb, alpha_s, vmark, qf, m_run, l_run, acc, n_miss - j0, -1,
+                  a.scale_log2);
+    }
+  } else {
+    // compute-buffer rows of empty entries (padded Top-K) are zero: this
+    // workgroup's share of the positions, 8 threads per row
+    if (a.padded && a.cbuf != nullptr) {
+      const int lo = (int)((long long)x * K / a.hit_per_req);
+      const int hi = (int)((long long)(x + 1) * K / a.hit_per_req);
+      u32x4* cb = reinterpret_cast<u32x4*>(a.cbuf) + bk * kRowChunks;
+      for (int i = lo + (tid >> 3); i < hi; i += kAttnThreads / 8)
+        if (a.slot_of[bk + i] == -2)
+#pragma unroll
+          for (int j = 0; j < kAttnItems; ++j)
+            cb[(long long)i * kRowChunks + (tid & 7) + 8 * j] = u32x4{0u, 0u, 0u, 0u};
+    }
+    const int ntiles = (n_hit + kTile - 1) / kTile;
+    const int tb = (int)((long long)x * ntiles / a.hit_per_req);
+    const int te = (int)((long long)(x + 1) * ntiles / a.hit_per_req);
+    // 8 threads per row: thread (row tid / 8, sub tid % 8) moves chunks sub + 8j.
+    // Rows are read through a buffer resource over the unit's S hot rows and
+    // written through one over request b's K compute-buffer rows (none when
+    // rows are read in place): the hardware range check turns the loads of
+    // rows past the hit list into zeros and drops the stores of rows that are
+    // not there, so every load and store is issued unconditionally and each
+    // path through the loop has the same memory operations in flight.
+    const int lrow = tid >> 3, lsub = tid & 7;
+    const int hot_bytes = a.S * kRowBytes;
+    const int cb_bytes = a.cbuf != nullptr ? K * kRowBytes : 0;
+    const __amdgpu_buffer_rsrc_t hsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.hot + u * a.S * kRowElems), (short)0, hot_bytes, kBufRsrcWord3);
+    const __amdgpu_buffer_rsrc_t csrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.cbuf != nullptr ? a.cbuf + bk * kRowElems : a.hot), (short)0, cb_bytes,
+        kBufRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.hit_slot + bk), (short)0, n_hit * 4, kBufRsrcWord3);
+    const __amdgpu_buffer_rsrc_t psrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.hit_pos + bk), (short)0, n_hit * 4, kBufRsrcWord3);
+    // slot and position of this thread's row of `tile`, loaded a tile ahead of the row
+    auto load_meta = [&](int tile, int& slot, int& pos) {
+      const int off = tile < te ? (tile * kTile + lrow) * 4 : n_hit * 4;
+      slot = __builtin_amdgcn_raw_buffer_load_b32(ssrc, off, 0, 0);
+      pos = __builtin_amdgcn_raw_buffer_load_b32(psrc, off, 0, 0);
+    };
+    auto load_tile = [&](u32x4 (&dst)[kAttnItems], int tile, int slot) {
+      const bool in = tile < te && tile * kTile + lrow < n_hit;
+      const int off = in ? slot * kRowBytes + lsub * 16 : hot_bytes;
+#pragma unroll
+      for (int j = 0; j < kAttnItems; ++j)
+        dst[j] = __builtin_amdgcn_raw_buffer_load_b128(hsrc, off + j * 128, 0, 0);
+    };
+    const int lsw = lds_swz(lrow);
+    auto store_tile = [&](const u32x4 (&src)[kAttnItems], int tile, int pos) {
+      unsigned char* d = kv + lrow * kLdsRow + ((lsub ^ lsw) * 16);
+      const bool in = tile < te && tile * kTile + lrow < n_hit;
+      const int coff = in ? pos * kRowBytes + lsub * 16 : cb_bytes;
+#pragma unroll
+      for (int j = 0; j < kAttnItems; ++j) {
+        *reinterpret_cast<u32x4*>(d + j * 128) = src[j];
+        __builtin_amdgcn_raw_buffer_store_b128(src[j], csrc, coff + j * 128, 0, 0);
+      }
+    };
+    auto compute = [&](int tile) {
+      attend_tile(kv, sc, pb, alpha_s, vmark, qf, m_run, l_run, acc, n_hit - tile * kTile, -1,
+                  a.scale_log2);
+    };
+    if (tb < te) {
+      u32x4 ra[kAttnItems], rb[kAttnItems];
+      int sa, sb, pa, pbv, pa2, pb2;
+      load_meta(tb, sa, pa);
+      load_meta(tb + 1, sb, pbv);
+      load_tile(ra, tb, sa);
+      load_meta(tb + 2, sa, pa2);
+      load_tile(rb, tb + 1, sb);
+      store_tile(ra, tb, pa);
+      __syncthreads();
+      // full pairs, as in the attention kernel: at the top of each iteration
+      // LDS holds `tile`, rb holds tile + 1 (position pbv) and the metadata of
+      // tile + 2 is in flight (sa, pa2)
+      int tile = tb;
+      for (; tile + 1 < te; tile += 2) {
+        load_meta(tile + 3, sb, pb2);
+        load_tile(ra, tile + 2, sa);
+        compute(tile);
+        store_tile(rb, tile + 1, pbv);
+        __syncthreads();
+        load_meta(tile + 4, sa, pa);
+        load_tile(rb, tile + 3, sb);
+        compute(tile + 1);
+        store_tile(ra, tile + 2, pa2);
+        __syncthreads();
+        pa2 = pa;
+        pbv = pb2;
+      }
+      if (tile < te) compute(tile);   // odd tile count: LDS holds the last tile
+    }
+  }
+
+  // partial of this workgroup: hit partials first, then fetch partials
+  const long long part = (long long)b * a.parts + (fetch ? a.hit_per_req + x : x);
+  float* po = a.part_o + part * kHeads * kVDim;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) po[(4 * g + j) * kVDim + wave * 64 + nt * 16 + r16] = acc[nt][j];
+  if (tid < kHeads * 16 && (tid & 15) == 0) {
+    const int h = tid >> 4;
+    a.part_ml[(part * kHeads + h) * 2 + 0] = m_run;
+    a.part_ml[(part * kHeads + h) * 2 + 1] = l_run;
+  }
+}
+
+// Merge of the attention partials of (request b, head h):
 // out = sum_s 2^(m_s - M) O_s / L, L = sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2.
-// One workgroup of 128 threads per (h, b), 4 outputs per thread.
+// A partial that saw no row has m_s = -inf and weight 0.  One workgroup of
+// 128 threads per (h, b), 4 outputs per thread.
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const int32_t* __restrict__ counts,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse, int splits) {
-  __shared__ float w[kMaxSplits];
+  __shared__ float w[kMaxParts];
   __shared__ float inv_l;
   const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   uint2* ob = reinterpret_cast<uint2*>(out + ((long long)b * kHeads + h) * kVDim);
@@ -1023,7 +1290,8 @@ __global__ __launch_bounds__(kProbeThreads) void host_read_probe_kernel(const u3
 size_t diff_lds_bytes(int S, int K) {
   int hb = 1;
   while ((1 << hb) < 2 * K) ++hb;
-  return (size_t)((S + 15) & ~15) + (size_t)4 * (1u << hb);
+  const size_t words = (1u << hb) > 3u * K ? (1u << hb) : 3u * K;
+  return (size_t)((S + 15) & ~15) + 4 * words;
 }
 
 static int hash_bits_for(int K) {
@@ -1078,7 +1346,7 @@ static_assert(KVS_MAX_TOPK <= 8 * kDiffThreads && KVS_MAX_SLOTS <= 16 * kDiffThr
               "diff_lru instantiations cover the limits");
 
 hipError_t prepare_kernels() {
-  // the diff kernel's dynamic LDS can exceed the 64 KiB default (up to 80 KiB)
+  // the diff kernel's dynamic LDS can exceed the 64 KiB default (up to 112 KiB)
   const int max_lds = (int)diff_lds_bytes(KVS_MAX_SLOTS, KVS_MAX_TOPK);
   for (int kpt = 1; kpt <= 8; kpt *= 2)
     for (int spt = 1; spt <= 16; spt *= 2) {
@@ -1108,6 +1376,9 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const
   a.evicted = d.evicted;
   a.counts = d.counts;
   a.row_slot = d.row_slot;
+  a.hit_pos = d.hit_pos;
+  a.hit_slot = d.hit_slot;
+  a.miss_tok = d.miss_tok;
   a.N = lay.N;
   a.S = lay.S;
   a.K = lay.K;
@@ -1180,6 +1451,39 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, cons
   return hipGetLastError();
 }
 
+hipError_t launch_assemble(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* q,
+                           float scale, hipStream_t s) {
+  AssembleArgs a;
+  a.pool = reinterpret_cast<const u32x4*>(d.pool);
+  a.hot = d.hot;
+  a.cbuf = (lay.flags & KVS_FLAG_DIRECT_HOT) ? nullptr : d.cbuf;
+  a.q = q;
+  a.slot_of = d.slot_of;
+  a.hit_pos = d.hit_pos;
+  a.hit_slot = d.hit_slot;
+  a.miss_pos = d.miss_pos;
+  a.miss_tok = d.miss_tok;
+  a.victims = d.victims;
+  a.counts = d.counts;
+  a.part_o = d.part_o;
+  a.part_ml = d.part_ml;
+  a.N = lay.N;
+  a.S = lay.S;
+  a.K = lay.K;
+  a.L = lay.L;
+  a.layer = layer;
+  a.fetch_per_req = lay.fetch_per_req;
+  a.hit_per_req = lay.splits;
+  a.parts = lay.parts;
+  a.fetch_wgs = lay.fetch_per_req * lay.B;
+  a.hits_first = (lay.flags & KVS_FLAG_HITS_FIRST) != 0;
+  a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const long long grid = (long long)(lay.fetch_per_req + lay.splits) * lay.B;
+  hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)grid), dim3(kAttnThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* rows,
                          const int64_t* pos, hipStream_t s) {
   hipLaunchKernelGGL(append_kernel, dim3(lay.B), dim3(kAppendThreads), 0, s,
@@ -1208,7 +1512,7 @@ hipError_t launch_host_read_probe(const void* src, long long chunks, uint32_t* s
 hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
                           hipStream_t s) {
   hipLaunchKernelGGL(combine_kernel, dim3(kHeads, lay.B), dim3(128), 0, s, d.part_o, d.part_ml,
-                     d.counts, out, lse, lay.splits);
+                     d.counts, out, lse, lay.parts);
   return hipGetLastError();
 }
 
