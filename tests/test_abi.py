@@ -166,19 +166,19 @@ def test_fetch_blocks_resolve():
     assert s.fetch_blocks == 256
 
 
-@pytest.mark.parametrize("batch,topk,hit_splits", [
-    (1, 256, 4),      # 128 hit workgroups wanted, but only 4 tiles of 64
-    (4, 2048, 32),    # 32 per request = 32 tiles
-    (32, 2048, 4),
-    (64, 2048, 2),
-    (192, 2048, 1),
-    (3, 8192, 43),    # ceil(128 / 3)
-    (1, 8192, 64),    # at most 64
+@pytest.mark.parametrize("batch,topk,hit_splits,fetch_blocks", [
+    (1, 256, 4, 64),      # 8 hit workgroups wanted, but only 4 tiles of 64
+    (4, 2048, 8, 64),     # at most 8 per request; at least 64 fetch workgroups
+    (32, 2048, 4, 64),
+    (48, 2048, 3, 96),    # two fetch workgroups per request
+    (64, 2048, 2, 128),
+    (192, 2048, 1, 128),  # at most 128 fetch workgroups (still one per request)
+    (3, 8192, 8, 64),
 ])
-def test_default_hit_splits(batch, topk, hit_splits):
+def test_default_assemble_counts(batch, topk, hit_splits, fetch_blocks):
     s = kvs.query_sizes(kvs.make_config(batch=batch, layers=1, context=20000, slots=topk,
                                         topk=topk))
-    assert s.attn_splits == hit_splits
+    assert s.attn_splits == hit_splits and s.fetch_blocks == fetch_blocks
 
 
 def test_graph_calls_reject_null():

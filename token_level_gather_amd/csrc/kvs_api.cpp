@@ -23,10 +23,13 @@ static uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 // Attention workgroups resident at once: one per compute unit of an MI355X.
 constexpr int kAttnWorkgroupsPerRound = 256;
-// Assembling launch defaults: fetch workgroups (512 threads, spread over the
-// requests) and hit workgroups in total.
-constexpr int kAssembleFetchBlocks = 128;
-constexpr int kAssembleHitBlocks = 128;
+// Assembling launch defaults, from sweeps at 4, 32, 64 and 192 requests:
+// about two fetch workgroups (512 threads) per request, 64 to 128 in all
+// (more outstanding PCIe reads lower the link's throughput and take CUs from
+// the hit workgroups; fewer leave each request's misses to one workgroup's
+// serial passes), and up to 8 hit workgroups per request, 128 in all.
+constexpr int kAssembleFetchMin = 64, kAssembleFetchMax = 128;
+constexpr int kAssembleHitBlocks = 128, kAssembleHitMaxPerReq = 8;
 // A workgroup's start-up (its first two tiles arriving during the all-CU
 // burst), in tile-times: fitted to measured split sweeps at 4, 32, 64 and 192
 // requests x 2048 selected tokens.
@@ -59,13 +62,20 @@ int make_layout(const kvs_config* c, Layout* lay) {
     // one assembling launch: fetch workgroups (one CU each for the whole
     // fetch) and hit workgroups (one CU each, several rounds); each writes
     // one attention partial
-    fetch_blocks = c->fetch_blocks == 0 ? kAssembleFetchBlocks : c->fetch_blocks;
+    if (c->fetch_blocks != 0) {
+      fetch_blocks = c->fetch_blocks;
+    } else {
+      const uint64_t two_per_req = 2 * B;
+      fetch_blocks = two_per_req < (uint64_t)kAssembleFetchMin   ? kAssembleFetchMin
+                     : two_per_req > (uint64_t)kAssembleFetchMax ? kAssembleFetchMax
+                                                                 : (int)two_per_req;
+    }
     fetch_per_req = (int)((fetch_blocks + B - 1) / B);
     if (fetch_per_req > ntiles) fetch_per_req = ntiles;
     if (splits == 0) {
       splits = (int)((kAssembleHitBlocks + B - 1) / B);
+      if (splits > kAssembleHitMaxPerReq) splits = kAssembleHitMaxPerReq;
       if (splits > ntiles) splits = ntiles;
-      if (splits > 64) splits = 64;
     } else if (splits > ntiles) {
       return KVS_EINVAL;
     }

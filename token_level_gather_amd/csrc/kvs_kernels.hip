@@ -161,16 +161,27 @@ struct DiffArgs {
   int padded;              // 1: a Top-K entry of -1 is empty
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave: within each row of 16
+// lanes by DPP row shifts (a lane whose source lies outside its row reads 0),
+// then the totals of rows 0..2 (read into scalars) added to the rows above.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
 // Exclusive prefix sum of `v` over the workgroup in thread order; `total`
-// receives the workgroup sum.  Must be reached by every thread.
+// receives the workgroup sum.  Must be reached by every thread.  `wtot` holds
+// the wave totals; each call site has its own, so one barrier suffices.
 __device__ __forceinline__ int wg_exclusive_scan(int v, int* wtot, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) wtot[wave] = x;
   __syncthreads();
   int off = 0, tot = 0;
@@ -180,7 +191,6 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wtot, int& total) {
     off += (w < wave) ? y : 0;
     tot += y;
   }
-  __syncthreads();
   total = tot;
   return off + x - v;
 }
@@ -197,7 +207,7 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wtot, int& total) {
 template <int KPT, int SPT>
 __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int wtot[kDiffWaves];
+  __shared__ int wtot[2][kDiffWaves];   // wave totals of the two workgroup scans
   __shared__ int err_bits;
   __shared__ int n_evict;
 
@@ -337,7 +347,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     if (q < spt && p < S && flag[my_ord[q]] == 0) cnt += 1 << 16;
   }
   int packed;
-  const int ex = wg_exclusive_scan(cnt, wtot, packed);
+  const int ex = wg_exclusive_scan(cnt, wtot[0], packed);
   const int m = packed & 0xffff;
   const int n_hit = S - (packed >> 16);
   int r = ex & 0xffff;
@@ -378,7 +388,10 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
       }
     }
   }
-  if (my_evict) atomicAdd(&n_evict, my_evict);
+  // one LDS atomic per wave (the wave's sum sits in its last lane): an
+  // atomic per thread on the one word serialises up to 1024 updates
+  const int wave_evict = wave_inclusive_scan(my_evict);
+  if ((tid & 63) == 63 && wave_evict != 0) atomicAdd(&n_evict, wave_evict);
   __syncthreads();
 
   // 4. the n_hit + m touched slots (hits and victims, all stamped t) close the
@@ -394,7 +407,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   for (int j = 0; j < KPT; ++j)
     if (j < kpt && i0 + j < K && my_slot[j] == -2) cnt += 1 << 16;
   int n_touched;
-  const int ex2 = wg_exclusive_scan(cnt, wtot, n_touched);
+  const int ex2 = wg_exclusive_scan(cnt, wtot[1], n_touched);
   r = S - (n_hit + m) + (ex2 & 0xffff);
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
@@ -411,7 +424,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
       a.hit_slot[bk + r++] = my_slot[j];
     }
   }
-  if (tid == 0) {   // n_evict is final after the barriers inside the scan
+  if (tid == 0) {   // n_evict is final after the barrier that follows the victims
     a.counts[4 * b + 0] = n_hit;
     a.counts[4 * b + 1] = m;
     a.counts[4 * b + 2] = n_evict;
