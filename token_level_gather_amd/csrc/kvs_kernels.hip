@@ -25,6 +25,7 @@
 // 1-3).
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kvs_internal.h"
@@ -221,12 +222,16 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   const int i0 = tid * kpt;
   const int p0 = tid * spt;
 
-  // LDS: per-slot flag [S] u8 (1 = hit, 2 = victim) | token hash set [H] i32,
-  //      reused after validation as miss positions [K] + victims [K] + miss
-  //      tokens [K] (the region holds max(H, 3K) words)
+  // LDS: per-slot flag [S] u8 (1 = hit, 2 = victim) | with S <= 4096 the
+  //      token of every slot [S] i32 | token hash set [H] i32, reused after
+  //      validation as miss positions [K] + victims [K] + miss tokens [K] (the
+  //      region holds max(H, 3K) words)
+  constexpr bool kLdsTok = SPT <= 4;
   uint8_t* flag = smem;
   unsigned* flagw = reinterpret_cast<unsigned*>(smem);   // the same flags, 4 per word
-  int32_t* hash = reinterpret_cast<int32_t*>(smem + ((S + 15) & ~15));
+  int32_t* s2t = reinterpret_cast<int32_t*>(smem + ((S + 15) & ~15));
+  int32_t* hash = reinterpret_cast<int32_t*>(smem + ((S + 15) & ~15) +
+                                             (kLdsTok ? ((4 * S + 15) & ~15) : 0));
   int32_t* lmiss = hash;
   int32_t* lvict = hash + K;
   int32_t* lmtok = hash + 2 * K;
@@ -251,13 +256,19 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
 #pragma unroll
   for (int q = 0; q < SPT; ++q) my_ord[q] = (int)gorder[min(p0 + q, S - 1)];
   const int t = a.stepctr[u];
-  // the token held by the slot at each of this thread's order positions (the
-  // order array is a permutation of the slots, so my_ord is in range)
+  // The token each victim's slot held.  With S <= 4096 each thread reads the
+  // tokens of its own slots [p0, p0 + spt) (contiguous, not waiting for the
+  // order) and puts them in LDS before the first scan: the gather below must
+  // wait for the order loads and held up the start of the kernel by 1.2 us at
+  // 4096 slots.  Otherwise it reads the token of the slot at each of its order
+  // positions (the order array is a permutation of the slots, so my_ord is in
+  // range); at 8192 slots over a 1M-token map the map lookups bound the start
+  // and the LDS copy gained nothing.
   int my_old[SPT];
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
     const int p = p0 + q;
-    my_old[q] = slot2tok[my_ord[q]];
+    my_old[q] = kLdsTok ? slot2tok[min(p, S - 1)] : slot2tok[my_ord[q]];
     if (q < spt && p < S) flag[p] = 0;
   }
   // 1a. slot lookup of every entry, issued before the first barrier and not
@@ -345,6 +356,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   for (int q = 0; q < SPT; ++q) {
     const int p = p0 + q;
     if (q < spt && p < S && flag[my_ord[q]] == 0) cnt += 1 << 16;
+    if (kLdsTok && q < spt && p < S) s2t[p] = my_old[q];   // read after the scan's barrier
   }
   int packed;
   const int ex = wg_exclusive_scan(cnt, wtot[0], packed);
@@ -375,7 +387,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
         if (r < m) {
           lvict[r] = s;
           flag[s] = 2;
-          const int old = my_old[q];
+          const int old = kLdsTok ? s2t[s] : my_old[q];
           a.evicted[bk + r] = old;
           if (old >= 0) {
             tok2slot[old] = -1;   // evicted tokens are outside the Top-K set
@@ -1304,7 +1316,8 @@ size_t diff_lds_bytes(int S, int K) {
   int hb = 1;
   while ((1 << hb) < 2 * K) ++hb;
   const size_t words = (1u << hb) > 3u * K ? (1u << hb) : 3u * K;
-  return (size_t)((S + 15) & ~15) + 4 * words;
+  const size_t tok = S <= 4 * kDiffThreads ? (size_t)((4 * S + 15) & ~15) : 0;   // slot tokens
+  return (size_t)((S + 15) & ~15) + tok + 4 * words;
 }
 
 static int hash_bits_for(int K) {
@@ -1360,7 +1373,8 @@ static_assert(KVS_MAX_TOPK <= 8 * kDiffThreads && KVS_MAX_SLOTS <= 16 * kDiffThr
 
 hipError_t prepare_kernels() {
   // the diff kernel's dynamic LDS can exceed the 64 KiB default (up to 112 KiB)
-  const int max_lds = (int)diff_lds_bytes(KVS_MAX_SLOTS, KVS_MAX_TOPK);
+  const int max_lds = (int)std::max(diff_lds_bytes(4 * kDiffThreads, 4 * kDiffThreads),
+                                    diff_lds_bytes(KVS_MAX_SLOTS, KVS_MAX_TOPK));
   for (int kpt = 1; kpt <= 8; kpt *= 2)
     for (int spt = 1; spt <= 16; spt *= 2) {
       const hipError_t e = hipFuncSetAttribute(
