@@ -1,12 +1,15 @@
 """Benchmark of the per-decode-step sparse KV assembly path on one MI355X.
 
 A step is one decode step of the whole hot path for every request and layer of
-a workload: slot lookup + sparse diff + LRU (diff_lru), the index copy
-(gather: misses fetched from pinned host memory over PCIe and written back to
-the hot buffer, hits copied within HBM), split-K sparse MLA attention and the
-merge of its partials (combine, only with more than one split).  Inputs (host
-pool rows, Top-K streams, queries) are seeded and synthetic and are resident
-(pool in pinned host memory, the rest in HBM) before any timing.
+a workload: slot lookup + sparse diff + LRU (diff_lru), then the assembling
+launch (assemble: misses fetched from pinned host memory over PCIe, written to
+the compute buffer and back to the hot buffer, hits copied within HBM, and the
+sparse MLA attention over every row it moves, one partial per workgroup) and
+the merge of the partials (combine).  ``--separate`` times the earlier
+sequence instead (gather, split-K attention over the complete compute buffer,
+combine).  Inputs (host pool rows, Top-K streams, queries) are seeded and
+synthetic and are resident (pool in pinned host memory, the rest in HBM)
+before any timing.
 
 Prints one JSON line.  The top-level figures are those of the headline
 workload (``--workload``, default: 32 requests x 8 layers at 128K context):
@@ -15,9 +18,10 @@ step) over exactly ``--steps`` timed steps after ``--warmup`` untimed ones.
 ``configs`` holds the same measurement protocol for every workload: R replays
 of its decode steps, each from freshly freed requests, with the median
 steady-state step and the cold first step reported apart, per-kernel times,
-the hit copy alone with the last-level cache flushed, and a parity check of
-sampled requests against the CPU oracle.  ``cpu_baseline`` is the oracle on P
-host processes.  A failed parity check prints no speed line and exits 1.
+the hit copy alone (all-hit steps that cycle two disjoint Top-K sets, with
+the working set stated), and a parity check of sampled requests against the
+CPU oracle.  ``cpu_baseline`` is the oracle on P host processes.  A failed
+parity check prints no speed line and exits 1.
 """
 from __future__ import annotations
 

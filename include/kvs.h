@@ -48,6 +48,17 @@
  *  - A pool's buffers live on the device current at kvs_create_pool; calls
  *    that enqueue work take a stream of that device (NULL = that device's
  *    default stream while it is current) and return KVS_EINVAL otherwise.
+ *
+ * Builds: libkvs.so, and libkvs_checked.so, the same library with device-side
+ * bounds checks (a debugging aid, slower).  In the checked build every index
+ * a kernel takes from the Top-K, the maps, the LRU order or the step's slot,
+ * miss, victim and hit lists is compared with the extent of the array it
+ * addresses before the access; a failure skips the access and latches
+ * KVS_EBOUNDS, and kvs_step_stats.fault_site / fault_index name the access
+ * (KVS_SITE_*) and the index.  State the normal build trusts (the LRU order is
+ * a permutation of the slots, every slot-to-token entry lies in [-1, N)) is
+ * verified before a step uses it; such a request is skipped untouched, like
+ * an invalid Top-K.
  */
 #ifndef KVS_H_
 #define KVS_H_
@@ -67,6 +78,7 @@ extern "C" {
 #define KVS_EDUP (-17)      /* device saw a repeated Top-K index within one request */
 #define KVS_ECORRUPT (-74)  /* a unit's state breaks an invariant: a token-to-slot entry
                                outside [-1, S) seen by a step, or a KVS_FLAG_CHECK failure */
+#define KVS_EBOUNDS (-14)   /* a device-side bounds check failed (libkvs_checked.so only) */
 #define KVS_EHIP_BASE (-1000) /* KVS_EHIP_BASE - e: HIP runtime error e */
 
 /* ---- limits ------------------------------------------------------------ */
@@ -85,6 +97,15 @@ extern "C" {
 #define KVS_KERNEL_ASSEMBLE 4   /* index copy and attention in one launch (default): misses
                                    over PCIe, hits within HBM, one partial per workgroup */
 #define KVS_NUM_KERNELS 5
+
+/* Accesses checked by libkvs_checked.so (kvs_step_stats.fault_site). */
+#define KVS_SITE_LRU_ORDER 1   /* diff: an LRU order entry >= S, or a slot listed twice */
+#define KVS_SITE_SLOT_TOKEN 2  /* diff: a slot-to-token entry outside [-1, N) */
+#define KVS_SITE_DIFF_LIST 3   /* diff: a write position of the order, miss or hit lists */
+#define KVS_SITE_MISS 4        /* copy: a miss's token, Top-K position or victim slot */
+#define KVS_SITE_HIT 5         /* copy: a hit's slot or Top-K position */
+#define KVS_SITE_ROW_SLOT 6    /* attention on rows in place: a row's slot */
+#define KVS_SITE_APPEND 7      /* append: the slot of the appended token, outside [-1, S) */
 
 /*
  * Shape of a pool.  B requests x L layers = B*L units; each unit has its own
@@ -195,6 +216,8 @@ typedef struct kvs_step_stats {
   int64_t evictions;    /* occupied slots overwritten */
   int64_t host_bytes;   /* bytes read from the host pool (misses * 1152) */
   int32_t status;       /* first device-detected error since the last sync, or KVS_OK */
+  int32_t fault_site;   /* status KVS_EBOUNDS: the failed access (KVS_SITE_*), else 0 */
+  int64_t fault_index;  /* status KVS_EBOUNDS: the index it was given, else 0 */
 } kvs_step_stats;
 
 /* Host copies of one unit's state, for tests (kvs_debug_read_state).  Each
@@ -327,8 +350,8 @@ int kvs_step_static(kvs_pool* pool, int32_t layer, const int32_t* topk, const vo
 int kvs_free_request(kvs_pool* pool, int32_t req, void* stream);
 
 /* Synchronise `stream`, then return the first device-detected error
- * (KVS_ERANGE / KVS_EDUP / KVS_ECORRUPT) since the last call, or KVS_OK, and
- * clear it.
+ * (KVS_ERANGE / KVS_EDUP / KVS_ECORRUPT, and KVS_EBOUNDS in the checked
+ * build) since the last call, or KVS_OK, and clear it.
  * `stats` (may be NULL) receives the running totals. */
 int kvs_sync_status(kvs_pool* pool, void* stream, kvs_step_stats* stats);
 

@@ -29,6 +29,26 @@ def test_library_exports_every_declared_symbol():
     assert sorted(kvs.EXPORTS) == declared
 
 
+def test_checked_build_exports_every_declared_symbol():
+    # the device-checked debug build is the same C ABI
+    lib = kvs.load_library(kvs.CHECKED_LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.kvs_strerror(kvs.KVS_EBOUNDS).decode() == kvs.strerror(kvs.KVS_EBOUNDS)
+    assert lib is not kvs.lib()
+
+
+def test_binding_constants_match_header():
+    # every integer #define of the header that the binding also names
+    text = open(HEADER).read()
+    defines = dict(re.findall(r"^#define\s+(KVS_\w+)\s+\(?(-?\d+)\)?", text, re.M))
+    named = [n for n in defines if hasattr(kvs, n)]
+    assert {"KVS_EBOUNDS", "KVS_ECORRUPT", "KVS_SITE_LRU_ORDER", "KVS_SITE_APPEND",
+            "KVS_FLAG_CHECK", "KVS_FLAG_SEPARATE_ATTENTION"} <= set(named)
+    for n in named:
+        assert getattr(kvs, n) == int(defines[n]), n
+
+
 def test_header_is_plain_c():
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "t.c")
@@ -153,6 +173,7 @@ def test_strerror():
     assert "outside" in kvs.strerror(kvs.KVS_ERANGE)
     assert kvs.strerror(kvs.KVS_OK) == "ok"
     assert "HIP" in kvs.strerror(kvs.KVS_EHIP_BASE - 2)
+    assert "bounds" in kvs.strerror(kvs.KVS_EBOUNDS)
 
 
 def test_fetch_blocks_resolve():

@@ -18,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # KVS_LIB selects another build of the same library (e.g. the host-sanitizer
 # build of the CPU tests); the default is the in-tree libkvs.so
 LIB_PATH = os.environ.get("KVS_LIB") or os.path.join(HERE, "libkvs.so")
+# the build with device-side bounds checks (a debugging aid; Pool(library=...))
+CHECKED_LIB_PATH = os.path.join(HERE, "libkvs_checked.so")
 
 KVS_OK = 0
 KVS_EINVAL = -22
@@ -25,6 +27,7 @@ KVS_ENOMEM = -12
 KVS_ERANGE = -34
 KVS_EDUP = -17
 KVS_ECORRUPT = -74
+KVS_EBOUNDS = -14
 KVS_EHIP_BASE = -1000
 
 HEADS, HEAD_DIM, V_DIM = 16, 576, 512
@@ -36,6 +39,14 @@ KVS_FLAG_DIRECT_HOT = 4
 KVS_FLAG_CHECK = 8
 KVS_FLAG_SEPARATE_ATTENTION = 16
 PROBE_SINK_WORDS = 65536
+# accesses checked by the device-checked build (kvs_step_stats.fault_site)
+KVS_SITE_LRU_ORDER = 1
+KVS_SITE_SLOT_TOKEN = 2
+KVS_SITE_DIFF_LIST = 3
+KVS_SITE_MISS = 4
+KVS_SITE_HIT = 5
+KVS_SITE_ROW_SLOT = 6
+KVS_SITE_APPEND = 7
 
 # Every exported symbol of include/kvs.h.
 EXPORTS = (
@@ -81,6 +92,7 @@ class kvs_step_stats(ctypes.Structure):
     _fields_ = [
         ("unit_steps", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
         ("evictions", ctypes.c_int64), ("host_bytes", ctypes.c_int64), ("status", ctypes.c_int32),
+        ("fault_site", ctypes.c_int32), ("fault_index", ctypes.c_int64),
     ]
 
 
@@ -106,18 +118,28 @@ class KvsError(RuntimeError):
         super().__init__(f"{what}: {strerror(code)} ({code})")
 
 
-_lib = None
+_libs = {}
 
 
 def lib() -> ctypes.CDLL:
     """Load libkvs.so (built by ``__graft_entry__.build()``); raise if it is absent."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+    return load_library(LIB_PATH)
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library (once per path) and declare its signatures."""
+    path = os.path.abspath(path)
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
                           "(python -m token_level_gather_amd._build)")
-    L = ctypes.CDLL(LIB_PATH)
+    # torch ships its own HIP runtime under the same soname; importing torch
+    # first makes the library bind to that one, so the process has a single
+    # HIP runtime (a library loaded before torch pulls in the system runtime,
+    # and torch's then finds no device)
+    import torch  # noqa: F401
+    L = ctypes.CDLL(path)
     vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
     sig = {
         "kvs_query_sizes": [ctypes.POINTER(kvs_config), ctypes.POINTER(kvs_sizes)],
@@ -147,7 +169,7 @@ def lib() -> ctypes.CDLL:
         f.restype = ctypes.c_int
     L.kvs_strerror.argtypes = [ctypes.c_int]
     L.kvs_strerror.restype = ctypes.c_char_p
-    _lib = L
+    _libs[path] = L
     return L
 
 
@@ -225,8 +247,9 @@ class Pool:
 
     def __init__(self, batch, layers, context, slots, topk, scale=None, attn_splits=0,
                  fetch_blocks=0, hit_blocks=0, flags=0, host: Optional[HostPool] = None,
-                 device=None, stream=None):
+                 device=None, stream=None, library: Optional[ctypes.CDLL] = None):
         import torch
+        self._lib = library if library is not None else lib()
         self.cfg = make_config(batch, layers, context, slots, topk, scale, attn_splits,
                                fetch_blocks, hit_blocks, flags)
         self.sizes = query_sizes(self.cfg)
@@ -251,7 +274,7 @@ class Pool:
                            self.scratch.numel())
         handle = ctypes.c_void_p()
         with torch.cuda.device(self.device):   # the library binds the pool to the current device
-            rc = lib().kvs_create_pool(ctypes.byref(self.cfg), ctypes.byref(bufs),
+            rc = self._lib.kvs_create_pool(ctypes.byref(self.cfg), ctypes.byref(bufs),
                                        _stream_ptr(stream, self.device), ctypes.byref(handle))
         _check(rc,
                "kvs_create_pool")
@@ -261,7 +284,7 @@ class Pool:
     def publish(self, req, layer, first_tok, rows: np.ndarray):
         rows = np.ascontiguousarray(rows, dtype=np.uint16)
         assert rows.ndim == 2 and rows.shape[1] == HEAD_DIM
-        _check(lib().kvs_publish(self.handle, req, layer, first_tok, rows.shape[0],
+        _check(self._lib.kvs_publish(self.handle, req, layer, first_tok, rows.shape[0],
                                  rows.ctypes.data), "kvs_publish")
 
     def publish_device(self, req, layer, first_tok, rows, stream=None):
@@ -269,7 +292,7 @@ class Pool:
         if not rows.is_cuda or rows.dim() != 2 or rows.shape[1] != HEAD_DIM \
                 or rows.element_size() != 2 or not rows.is_contiguous():
             raise ValueError("expected a contiguous device tensor [n][576] of bf16")
-        _check(lib().kvs_publish_device(self.handle, req, layer, first_tok, rows.shape[0],
+        _check(self._lib.kvs_publish_device(self.handle, req, layer, first_tok, rows.shape[0],
                                         rows.data_ptr(), _stream_ptr(stream, self.device)),
                "kvs_publish_device")
 
@@ -277,7 +300,7 @@ class Pool:
         """rows [B][576] bf16 and pos [B] int64 (-1 = nothing to append), device."""
         self._check_dev(rows, (self.B, HEAD_DIM), 2)
         self._check_dev(pos, (self.B,), 8)
-        _check(lib().kvs_append(self.handle, layer, rows.data_ptr(), pos.data_ptr(),
+        _check(self._lib.kvs_append(self.handle, layer, rows.data_ptr(), pos.data_ptr(),
                                 _stream_ptr(stream, self.device)), "kvs_append")
 
     def step(self, layer, topk, q, out, lse=None, stream=None):
@@ -289,7 +312,7 @@ class Pool:
         if lse is not None:
             self._check_dev(lse, (self.B, HEADS), 4)
             lse_ptr = lse.data_ptr()
-        _check(lib().kvs_step(self.handle, layer, topk.data_ptr(), q.data_ptr(), out.data_ptr(),
+        _check(self._lib.kvs_step(self.handle, layer, topk.data_ptr(), q.data_ptr(), out.data_ptr(),
                               lse_ptr, _stream_ptr(stream, self.device)), "kvs_step")
 
     def step_static(self, layer, topk, q, out, lse=None, stream=None):
@@ -301,20 +324,20 @@ class Pool:
         if lse is not None:
             self._check_dev(lse, (self.B, HEADS), 4)
             lse_ptr = lse.data_ptr()
-        _check(lib().kvs_step_static(self.handle, layer, topk.data_ptr(), q.data_ptr(),
+        _check(self._lib.kvs_step_static(self.handle, layer, topk.data_ptr(), q.data_ptr(),
                                      out.data_ptr(), lse_ptr, _stream_ptr(stream, self.device)),
                "kvs_step_static")
 
     def free_request(self, req, stream=None):
-        _check(lib().kvs_free_request(self.handle, req, _stream_ptr(stream, self.device)),
+        _check(self._lib.kvs_free_request(self.handle, req, _stream_ptr(stream, self.device)),
                "kvs_free_request")
 
     def sync_status(self, stream=None):
         """Returns (status code, kvs_step_stats); the status is cleared."""
         st = kvs_step_stats()
-        rc = lib().kvs_sync_status(self.handle, _stream_ptr(stream, self.device),
+        rc = self._lib.kvs_sync_status(self.handle, _stream_ptr(stream, self.device),
                                    ctypes.byref(st))
-        if rc not in (KVS_OK, KVS_ERANGE, KVS_EDUP, KVS_ECORRUPT):
+        if rc not in (KVS_OK, KVS_ERANGE, KVS_EDUP, KVS_ECORRUPT, KVS_EBOUNDS):
             raise KvsError(rc, "kvs_sync_status")
         return rc, st
 
@@ -327,7 +350,7 @@ class Pool:
             "counts": np.empty(4, np.int32), "row_slot": np.empty(self.K, np.int32),
         }
         st = kvs_unit_state(*[a.ctypes.data_as(_I32P) for a in arr.values()], 0)
-        _check(lib().kvs_debug_read_state(self.handle, req, layer, _stream_ptr(stream, self.device),
+        _check(self._lib.kvs_debug_read_state(self.handle, req, layer, _stream_ptr(stream, self.device),
                                           ctypes.byref(st)), "kvs_debug_read_state")
         arr["step"] = int(st.step)
         return arr
@@ -337,11 +360,11 @@ class Pool:
         mask = 0
         for k in kernels:
             mask |= 1 << KERNEL_NAMES.index(k)
-        _check(lib().kvs_profile_begin(self.handle, max_steps, mask), "kvs_profile_begin")
+        _check(self._lib.kvs_profile_begin(self.handle, max_steps, mask), "kvs_profile_begin")
 
     def profile_end(self) -> dict:
         t = kvs_kernel_times()
-        _check(lib().kvs_profile_end(self.handle, ctypes.byref(t)), "kvs_profile_end")
+        _check(self._lib.kvs_profile_end(self.handle, ctypes.byref(t)), "kvs_profile_end")
         return {"steps": t.steps,
                 "launches": {n: t.launches[i] for i, n in enumerate(KERNEL_NAMES)},
                 **{n: t.ms_total[i] for i, n in enumerate(KERNEL_NAMES)}}
@@ -356,15 +379,15 @@ class Pool:
         import torch
         g = ctypes.c_void_p()
         with torch.cuda.device(self.device):   # the capture stream is made on the current device
-            rc = lib().kvs_graph_capture(self.handle, layer, topk.data_ptr(), q.data_ptr(),
+            rc = self._lib.kvs_graph_capture(self.handle, layer, topk.data_ptr(), q.data_ptr(),
                                          out.data_ptr(), None if lse is None else lse.data_ptr(),
                                          ctypes.byref(g))
         _check(rc, "kvs_graph_capture")
-        return StepGraph(g, (topk, q, out, lse), self.device)
+        return StepGraph(g, (topk, q, out, lse), self.device, self._lib)
 
     def release(self):
         if self.handle:
-            _check(lib().kvs_release(self.handle), "kvs_release")
+            _check(self._lib.kvs_release(self.handle), "kvs_release")
             self.handle = None
 
     def close(self):
@@ -391,16 +414,17 @@ class Pool:
 class StepGraph:
     """A captured kvs_step; launch() replays it on a stream of the pool's device."""
 
-    def __init__(self, handle, keep_alive, device=None):
+    def __init__(self, handle, keep_alive, device=None, library=None):
+        self._lib = library if library is not None else lib()
         self.handle = handle
         self._keep = keep_alive
         self.device = device
 
     def launch(self, stream=None):
-        _check(lib().kvs_graph_launch(self.handle, _stream_ptr(stream, self.device)),
+        _check(self._lib.kvs_graph_launch(self.handle, _stream_ptr(stream, self.device)),
                "kvs_graph_launch")
 
     def destroy(self):
         if self.handle:
-            _check(lib().kvs_graph_destroy(self.handle), "kvs_graph_destroy")
+            _check(self._lib.kvs_graph_destroy(self.handle), "kvs_graph_destroy")
             self.handle = None

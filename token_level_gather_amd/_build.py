@@ -5,6 +5,12 @@ Compiles the gfx950 kernels and the C-ABI host runtime into
 gets ``-Xclang -target-feature -Xclang -packed-fp32-ops`` (no packed fp32 VALU
 instructions are emitted).
 
+``--device-checks`` builds ``token_level_gather_amd/libkvs_checked.so``: the
+same library with ``KVS_DEVICE_CHECKS=1``, device-side bounds checks on every
+index the kernels take from the Top-K, the maps, the LRU order and the step's
+lists (a debugging aid; ``kvs.load_library(kvs.CHECKED_LIB_PATH)`` or
+``KVS_LIB`` selects it).
+
 ``--host-sanitizers`` builds ``_build/hostsan/libkvs.so`` instead, with
 AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (each
 ``-fsanitize`` behind ``-Xarch_host``; device code is built as usual), for
@@ -25,6 +31,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvs.so")
+CHECKED_LIB = os.path.join(HERE, "libkvs_checked.so")
 SOURCES = ["kvs_kernels.hip", "kvs_api.cpp"]
 ARCH = "gfx950"
 
@@ -50,14 +57,20 @@ def compile_flags():
 HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
 
 
-def build(verbose: bool = False, out: str = LIB, host_sanitizers: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, host_sanitizers: bool = False,
+          device_checks: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
-    build_dir = os.path.join(ROOT, "_build", "hostsan" if host_sanitizers else "")
+    sub = "hostsan" if host_sanitizers else "checked" if device_checks else ""
+    build_dir = os.path.join(ROOT, "_build", sub)
     os.makedirs(build_dir, exist_ok=True)
     if host_sanitizers and out == LIB:
         out = os.path.join(build_dir, "libkvs.so")
+    if device_checks and out == LIB:
+        out = CHECKED_LIB
     extra = HOST_SANITIZE + ["-Xarch_host", "-fno-omit-frame-pointer", "-g"] \
         if host_sanitizers else []
+    if device_checks:
+        extra = extra + ["-DKVS_DEVICE_CHECKS=1"]
     objs = []
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
@@ -86,4 +99,5 @@ def _run(cmd, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, host_sanitizers="--host-sanitizers" in sys.argv))
+    print(build(verbose="-v" in sys.argv, host_sanitizers="--host-sanitizers" in sys.argv,
+                device_checks="--device-checks" in sys.argv))

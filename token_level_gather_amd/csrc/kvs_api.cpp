@@ -523,6 +523,10 @@ int kvs_sync_status(kvs_pool* p, void* stream, kvs_step_stats* stats) {
     }
     stats->host_bytes = stats->misses * kRowBytes;
     stats->status = status[0];
+    if (status[0] == KVS_EBOUNDS) {   // the checked build's site and index, words 1..3
+      stats->fault_site = status[1];
+      stats->fault_index = (int64_t)(((uint64_t)(uint32_t)status[3] << 32) | (uint32_t)status[2]);
+    }
   }
   KVS_TRY_HIP(hipStreamSynchronize(s));
   if (status[0] != 0) {
@@ -691,6 +695,7 @@ const char* kvs_strerror(int code) {
     case KVS_ERANGE: return "Top-K index or append position outside [0, context)";
     case KVS_EDUP: return "duplicate Top-K index within a request";
     case KVS_ECORRUPT: return "state check failed: maps, LRU order or victims break an invariant";
+    case KVS_EBOUNDS: return "device-side bounds check failed (checked build)";
     default: break;
   }
   if (code <= KVS_EHIP_BASE) return "HIP runtime error (KVS_EHIP_BASE - hipError_t)";

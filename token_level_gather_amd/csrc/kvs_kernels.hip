@@ -104,6 +104,42 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x + dpp_f32<0x140>(x);
 }
 
+// ------------------------------------------------------------------ device checks
+// The checked build (libkvs_checked.so, KVS_DEVICE_CHECKS=1) compares every
+// index a kernel takes from the Top-K, the maps, the LRU order or the step's
+// lists with the extent of the array it addresses before the access.  In the
+// normal build in_range() and in_bounds() are constant true and every check
+// compiles away.
+#ifndef KVS_DEVICE_CHECKS
+#define KVS_DEVICE_CHECKS 0
+#endif
+
+// First failure wins: the status word takes KVS_EBOUNDS, words 1..3 the site
+// (KVS_SITE_*) and the index (low, high 32 bits).
+__device__ __noinline__ void latch_bounds(int32_t* status, int site, long long idx) {
+  if (atomicCAS(status, 0, KVS_EBOUNDS) == 0) {
+    status[1] = site;
+    status[2] = (int32_t)(uint32_t)((unsigned long long)idx & 0xffffffffull);
+    status[3] = (int32_t)(uint32_t)((unsigned long long)idx >> 32);
+  }
+}
+
+// True when lo <= idx < hi; otherwise (checked build) latches the failure and
+// returns false, and the caller skips the access.
+__device__ __forceinline__ bool in_range(long long idx, long long lo, long long hi,
+                                         int32_t* status, int site) {
+  if constexpr (KVS_DEVICE_CHECKS) {
+    if (idx >= lo && idx < hi) return true;
+    latch_bounds(status, site, idx);
+    return false;
+  }
+  return true;
+}
+
+__device__ __forceinline__ bool in_bounds(long long idx, long long n, int32_t* status, int site) {
+  return in_range(idx, 0, n, status, site);
+}
+
 // ------------------------------------------------------------------ init
 // Empties units [u0, u0 + count): maps -1, last_used -1, LRU order 0..S-1.
 __global__ void init_units_kernel(int32_t* tok2slot, int32_t* slot2tok, int32_t* last_used,
@@ -268,7 +304,8 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
     const int p = p0 + q;
-    my_old[q] = kLdsTok ? slot2tok[min(p, S - 1)] : slot2tok[my_ord[q]];
+    my_old[q] = kLdsTok ? slot2tok[min(p, S - 1)]
+                        : slot2tok[KVS_DEVICE_CHECKS ? min(my_ord[q], S - 1) : my_ord[q]];
     if (q < spt && p < S) flag[p] = 0;
   }
   // 1a. slot lookup of every entry, issued before the first barrier and not
@@ -322,6 +359,28 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
       }
     }
   }
+  if constexpr (KVS_DEVICE_CHECKS) {
+    // the state the normal build trusts: the LRU order lists every slot once
+    // (bit 7 of the slot's flag byte marks it seen; cleared below, before the
+    // flags are read) and every slot's token lies in [-1, N)
+#pragma unroll
+    for (int q = 0; q < SPT; ++q) {
+      const int p = p0 + q;
+      if (q < spt && p < S) {
+        const int s = my_ord[q];
+        if (!in_bounds(s, S, a.status, KVS_SITE_LRU_ORDER)) {
+          atomicOr(&err_bits, 8);
+        } else {
+          const unsigned bit = 0x80u << ((s & 3) * 8);
+          if (atomicOr(&flagw[s >> 2], bit) & bit) {
+            latch_bounds(a.status, KVS_SITE_LRU_ORDER, s);
+            atomicOr(&err_bits, 8);
+          }
+        }
+        if (!in_range(my_old[q], -1, a.N, a.status, KVS_SITE_SLOT_TOKEN)) atomicOr(&err_bits, 8);
+      }
+    }
+  }
   __syncthreads();
   if (err_bits) {   // invalid Top-K or map: leave the unit untouched, latch the error
     if (tid == 0) {
@@ -330,7 +389,10 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
       a.counts[4 * b + 2] = 0;
       a.counts[4 * b + 3] = 0;
       atomicCAS(a.status, 0,
-                (err_bits & 1) ? KVS_ERANGE : (err_bits & 4) ? KVS_ECORRUPT : KVS_EDUP);
+                (err_bits & 1)   ? KVS_ERANGE
+                : (err_bits & 4) ? KVS_ECORRUPT
+                : (err_bits & 2) ? KVS_EDUP
+                                 : KVS_EBOUNDS);
     }
     return;
   }
@@ -339,6 +401,11 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   //    Top-K order (low 16 bits, m <= K <= 8192) and non-hit slots in LRU
   //    order (high 16 bits, at most S <= 16384).  The hit slots are distinct
   //    (a repeat was rejected above), so n_hit = S - non-hit slots.
+  if constexpr (KVS_DEVICE_CHECKS) {   // each slot's flag byte belongs to its order position
+#pragma unroll
+    for (int q = 0; q < SPT; ++q)
+      if (q < spt && p0 + q < S) flag[my_ord[q]] &= 0x7f;
+  }
   // 2. sparse diff: record slot_of, touch hits, compact misses in Top-K order
   int cnt = 0;
 #pragma unroll
@@ -366,7 +433,8 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
-    if (j < kpt && i < K && my_slot[j] == -1) {
+    if (j < kpt && i < K && my_slot[j] == -1 &&
+        in_bounds(r, K, a.status, KVS_SITE_DIFF_LIST)) {
       lmiss[r] = i;
       lmtok[r++] = my_tok[j];
     }
@@ -393,7 +461,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
             tok2slot[old] = -1;   // evicted tokens are outside the Top-K set
             ++my_evict;
           }
-        } else {
+        } else if (in_bounds(r - m, S, a.status, KVS_SITE_DIFF_LIST)) {
           gorder[r - m] = (uint16_t)s;
         }
         ++r;
@@ -424,14 +492,15 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
     const int s = p0 + q;
-    if (q < spt && s < S && flag[s] != 0) gorder[r++] = (uint16_t)s;
+    if (q < spt && s < S && flag[s] != 0 && in_bounds(r, S, a.status, KVS_SITE_DIFF_LIST))
+      gorder[r++] = (uint16_t)s;
   }
   // hits in Top-K order: entries before this thread's, less its misses and empties
   r = i0 - (ex & 0xffff) - (ex2 >> 16);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
-    if (j < kpt && i < K && my_slot[j] >= 0) {
+    if (j < kpt && i < K && my_slot[j] >= 0 && in_bounds(r, K, a.status, KVS_SITE_DIFF_LIST)) {
       a.hit_pos[bk + r] = i;
       a.hit_slot[bk + r++] = my_slot[j];
     }
@@ -454,6 +523,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     const int i = lmiss[j];
     const int tok = lmtok[j];
     const int v = lvict[j];
+    if (!in_bounds(v, S, a.status, KVS_SITE_DIFF_LIST)) continue;
     slot2tok[v] = tok;
     tok2slot[tok] = v;
     lu[v] = t;
@@ -486,6 +556,7 @@ struct GatherArgs {
   int hit_wgs;             // hit-role workgroups (each loops over 32-position groups)
   int hits_first;          // 0: fetch workgroups take the first grid indices; 1: hit ones do
   int write_cbuf;          // 0: rows are read in place from the hot buffer (no compute buffer)
+  int32_t* status;         // checked build: bounds failures
 };
 
 // The index copy of one layer.  Workgroups [0, fetch_wgs) fetch misses: row =
@@ -524,10 +595,15 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
         pos[j] = -1;
         if (jj < n) {
           const int i = a.miss_pos[bk + jj];
+          if (!in_bounds(i, K, a.status, KVS_SITE_MISS)) continue;
           const int tok = a.topk[bk + i];
+          const int vs = a.victims[bk + jj];
+          if (!in_bounds(tok, a.N, a.status, KVS_SITE_MISS) ||
+              !in_bounds(vs, a.S, a.status, KVS_SITE_MISS))
+            continue;
           v[j] = a.pool[(u * a.N + tok) * kRowChunks + col];
           pos[j] = i;
-          vic[j] = a.victims[bk + jj];
+          vic[j] = vs;
         }
       }
 #pragma unroll
@@ -559,6 +635,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
     if (i >= K) continue;
     const int s = a.slot_of[(long long)b * K + i];
     if (s == -1) continue;   // a miss: the fetch role writes it
+    if (!in_range(s, -2, a.S, a.status, KVS_SITE_HIT)) continue;
     u32x4* dst = a.cbuf + ((long long)b * K + i) * kRowChunks + sub;
     if (s < 0) {             // an empty entry of a padded Top-K gathers a zero row
 #pragma unroll
@@ -616,6 +693,7 @@ struct AttnArgs {
   float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units
   uint16_t* out;            // [B][16][512] bf16 when splits == 1 (no combine), else null
   float* lse;               // [B][16] or null; written here only when out is
+  int32_t* status;          // checked build: bounds failures
 };
 
 // One 64-row tile in LDS: scores of the 16 heads against every row, the
@@ -815,8 +893,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   auto load_tile = [&](u32x4 (&dst)[kAttnItems], int& dv, int tile, int slot) {
     const int tok = tile * kTile + lrow;
     const bool in = tile < te && tok < K;
-    const int off = !in       ? rec_bytes
-                    : DIRECT ? (slot >= 0 ? slot * kRowBytes + lsub * 16 : rec_bytes)
+    const bool ok = !DIRECT || !in || in_range(slot, -1, a.S, a.status, KVS_SITE_ROW_SLOT);
+    const int off = !in || !ok ? rec_bytes
+                    : DIRECT   ? (slot >= 0 ? slot * kRowBytes + lsub * 16 : rec_bytes)
                                : tok * kRowBytes + lsub * 16;
 #pragma unroll
     for (int j = 0; j < kAttnItems; ++j)
@@ -946,6 +1025,7 @@ struct AssembleArgs {
   int hits_first;           // 1: the hit workgroups take the first grid indices
   int padded;               // 1: zero the compute-buffer rows of empty entries
   float scale_log2;
+  int32_t* status;          // checked build: bounds failures
 };
 
 __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) {
@@ -1005,9 +1085,15 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
         pos[jj] = -1;
         if (jm < n_miss) {
           const int tok = a.miss_tok[bk + jm];
+          const int mp = a.miss_pos[bk + jm];
+          const int vs = a.victims[bk + jm];
+          if (!in_bounds(tok, a.N, a.status, KVS_SITE_MISS) ||
+              !in_bounds(mp, K, a.status, KVS_SITE_MISS) ||
+              !in_bounds(vs, a.S, a.status, KVS_SITE_MISS))
+            continue;
           v[jj] = a.pool[(u * a.N + tok) * kRowChunks + col];
-          pos[jj] = a.miss_pos[bk + jm];
-          vic[jj] = a.victims[bk + jm];
+          pos[jj] = mp;
+          vic[jj] = vs;
         }
       }
 #pragma unroll
@@ -1067,7 +1153,8 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
       pos = __builtin_amdgcn_raw_buffer_load_b32(psrc, off, 0, 0);
     };
     auto load_tile = [&](u32x4 (&dst)[kAttnItems], int tile, int slot) {
-      const bool in = tile < te && tile * kTile + lrow < n_hit;
+      const bool in = tile < te && tile * kTile + lrow < n_hit &&
+                      in_bounds(slot, a.S, a.status, KVS_SITE_HIT);
       const int off = in ? slot * kRowBytes + lsub * 16 : hot_bytes;
 #pragma unroll
       for (int j = 0; j < kAttnItems; ++j)
@@ -1076,7 +1163,8 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
     const int lsw = lds_swz(lrow);
     auto store_tile = [&](const u32x4 (&src)[kAttnItems], int tile, int pos) {
       unsigned char* d = kv + lrow * kLdsRow + ((lsub ^ lsw) * 16);
-      const bool in = tile < te && tile * kTile + lrow < n_hit;
+      const bool in = tile < te && tile * kTile + lrow < n_hit &&
+                      in_bounds(pos, K, a.status, KVS_SITE_HIT);
       const int coff = in ? pos * kRowBytes + lsub * 16 : cb_bytes;
 #pragma unroll
       for (int j = 0; j < kAttnItems; ++j) {
@@ -1275,6 +1363,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
   }
   const long long u = (long long)b * L + layer;
   const int s = tok2slot[u * N + p];
+  if (!in_range(s, -1, S, status, KVS_SITE_APPEND)) return;   // the row is not appended
   if (tid < kRowChunks) {
     const u32x4 v = rows[(long long)b * kRowChunks + tid];
     pool[(u * N + p) * kRowChunks + tid] = v;
@@ -1444,6 +1533,7 @@ hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const i
   a.hit_wgs = (int)(lay.hit_blocks > 0 && lay.hit_blocks < all_groups ? lay.hit_blocks : all_groups);
   a.hits_first = (lay.flags & KVS_FLAG_HITS_FIRST) != 0;
   a.write_cbuf = (lay.flags & KVS_FLAG_DIRECT_HOT) == 0;
+  a.status = d.status;
   if (!a.write_cbuf) a.hit_wgs = 0;   // hits stay where they are
   const long long grid = (long long)a.fetch_wgs + (long long)a.hit_wgs;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, s, a);
@@ -1469,6 +1559,7 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, cons
   a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
   a.out = lay.splits == 1 ? out : nullptr;
   a.lse = lay.splits == 1 ? lse : nullptr;
+  a.status = d.status;
   const bool direct = (lay.flags & KVS_FLAG_DIRECT_HOT) != 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   if (direct)
@@ -1505,6 +1596,7 @@ hipError_t launch_assemble(const Layout& lay, const DevPtrs& d, int layer, const
   a.fetch_wgs = lay.fetch_per_req * lay.B;
   a.hits_first = (lay.flags & KVS_FLAG_HITS_FIRST) != 0;
   a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
+  a.status = d.status;
   a.scale_log2 = scale * 1.4426950408889634f;
   const long long grid = (long long)(lay.fetch_per_req + lay.splits) * lay.B;
   hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)grid), dim3(kAttnThreads), 0, s, a);
