@@ -377,7 +377,7 @@ class Workload:
             # hit rows are read once from the hot buffer (and written to the
             # compute buffer); miss rows arrive over PCIe and are written to the
             # victim slot (and the compute buffer); then the partials
-            hbm = (ROW * h if direct else 2 * ROW * h + 2 * ROW * m) + q_bytes + part
+            hbm = (ROW * (h + m) if direct else 2 * ROW * (h + m)) + q_bytes + part
             alg["assemble"] = {"bound": "pcie", "bytes": ROW * m, "hbm_bytes": hbm,
                                "flop": flop}
             alg["combine"] = {"bound": "hbm", "bytes": part + out_bytes}
