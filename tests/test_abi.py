@@ -190,8 +190,8 @@ def test_fetch_blocks_resolve():
 @pytest.mark.parametrize("batch,topk,hit_splits,fetch_blocks", [
     (1, 256, 4, 64),      # 8 hit workgroups wanted, but only 4 tiles of 64
     (4, 2048, 8, 64),     # at most 8 per request; at least 64 fetch workgroups
-    (32, 2048, 4, 64),
-    (48, 2048, 3, 96),    # two fetch workgroups per request
+    (32, 2048, 4, 96),    # three fetch workgroups per request
+    (48, 2048, 3, 128),
     (64, 2048, 2, 128),
     (192, 2048, 1, 128),  # at most 128 fetch workgroups (still one per request)
     (3, 8192, 8, 64),

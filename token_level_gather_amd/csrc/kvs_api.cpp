@@ -65,10 +65,10 @@ int make_layout(const kvs_config* c, Layout* lay) {
     if (c->fetch_blocks != 0) {
       fetch_blocks = c->fetch_blocks;
     } else {
-      const uint64_t two_per_req = 2 * B;
-      fetch_blocks = two_per_req < (uint64_t)kAssembleFetchMin   ? kAssembleFetchMin
-                     : two_per_req > (uint64_t)kAssembleFetchMax ? kAssembleFetchMax
-                                                                 : (int)two_per_req;
+      const uint64_t three_per_req = 3 * B;
+      fetch_blocks = three_per_req < (uint64_t)kAssembleFetchMin   ? kAssembleFetchMin
+                     : three_per_req > (uint64_t)kAssembleFetchMax ? kAssembleFetchMax
+                                                                   : (int)three_per_req;
     }
     fetch_per_req = (int)((fetch_blocks + B - 1) / B);
     if (fetch_per_req > ntiles) fetch_per_req = ntiles;

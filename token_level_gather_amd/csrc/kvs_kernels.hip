@@ -1072,7 +1072,12 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
     // chunk c = 512 jj + tid of the pass's 64 x 72 chunks: row c / 72, column c % 72
     u32x4* hot = reinterpret_cast<u32x4*>(a.hot);
     u32x4* cbuf = reinterpret_cast<u32x4*>(a.cbuf);
-    for (int j0 = x * kTile; j0 < n_miss; j0 += a.fetch_per_req * kTile) {
+    // this workgroup's share of the request's misses: rows [lo, hi), an equal
+    // split by rows (not by 64-row passes), so the request's fetch workgroups
+    // finish together
+    const int lo = (int)((long long)x * n_miss / a.fetch_per_req);
+    const int hi = (int)((long long)(x + 1) * n_miss / a.fetch_per_req);
+    for (int j0 = lo; j0 < hi; j0 += kTile) {
       u32x4 v[kAttnItems];
       int pos[kAttnItems], vic[kAttnItems];
 #pragma unroll
@@ -1081,9 +1086,9 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
         const int r = c / kRowChunks;
         const int col = c - r * kRowChunks;
         const int jm = j0 + r;
-        v[jj] = u32x4{0u, 0u, 0u, 0u};   // rows past the last miss stay zero in LDS
+        v[jj] = u32x4{0u, 0u, 0u, 0u};   // rows past the share stay zero in LDS
         pos[jj] = -1;
-        if (jm < n_miss) {
+        if (jm < hi) {
           const int tok = a.miss_tok[bk + jm];
           const int mp = a.miss_pos[bk + jm];
           const int vs = a.victims[bk + jm];
@@ -1108,7 +1113,7 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
         *reinterpret_cast<u32x4*>(kv + r * kLdsRow + ((col ^ lds_swz(r)) * 16)) = v[jj];
       }
       __syncthreads();
-      attend_tile(kv, sc, pb, alpha_s, vmark, qf, m_run, l_run, acc, n_miss - j0, -1,
+      attend_tile(kv, sc, pb, alpha_s, vmark, qf, m_run, l_run, acc, hi - j0, -1,
                   a.scale_log2);
     }
   } else {
