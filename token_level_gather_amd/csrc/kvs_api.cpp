@@ -1,6 +1,7 @@
 // Host runtime behind the C ABI in include/kvs.h: configuration and buffer
 // validation, host-pool allocation, launch orchestration of one decode step
-// (three or four kernels on the caller's stream), status and statistics
+// (diff, the assembling launch and the merge of its partials on the caller's
+// stream; or diff, gather, attention and the merge), status and statistics
 // readback, and per-kernel event timing.
 //
 // The request lifecycle follows "XM-Sparse" (HiSparse integration section):

@@ -1,20 +1,26 @@
 // gfx950 (MI355X) kernels of the per-decode-step sparse KV assembly path.
 //
-// One kvs_step of layer l runs three or four launches for the B units (b, l):
+// One kvs_step of layer l runs, for the B units (b, l):
 //   diff_lru   one workgroup per unit: slot lookup + validation, sparse diff
 //              (misses compacted in Top-K order by a workgroup prefix sum),
 //              hit touch, LRU victim choice from the unit's LRU order array,
-//              eviction and map update.
-//   gather     the index copy: miss rows read from pinned host memory over
-//              PCIe into the compute buffer and the victim slots, hit rows
-//              copied from the hot buffer to the compute buffer, in one grid
-//              (rows read in place: only the misses, into their slots).
+//              eviction and map update; also the compacted hit list.
+//   assemble   (default) the index copy and the attention in one grid: fetch
+//              workgroups read miss rows from pinned host memory over PCIe
+//              into the compute buffer and the victim slots and attend over
+//              them; hit workgroups copy resident rows from the hot buffer to
+//              the compute buffer and attend over them meanwhile.  Each
+//              workgroup writes one attention partial
+//              (v_mfma_f32_16x16x32_bf16 for Q.K^T and P.V, fp32 online
+//              softmax).
+//   combine    merges the partials, writes bf16 out and fp32 lse.
+// With KVS_FLAG_SEPARATE_ATTENTION the copy and the attention are separate
+// launches instead:
+//   gather     the index copy (rows read in place: only the misses, into their
+//              slots);
 //   attention  split-K sparse MLA decode over the K gathered rows (or over
-//              the hot buffer through row_slot): v_mfma_f32_16x16x32_bf16 for
-//              Q.K^T and P.V, fp32 online softmax.
-//   combine    merges the split partials, writes bf16 out and fp32 lse (only
-//              with more than one split: a single-split attention writes out
-//              and lse itself).
+//              the hot buffer through row_slot); a single split writes out and
+//              lse itself, more are merged by combine.
 // Outside the step: init/reset kernels (pool creation, kvs_free_request), the
 // append kernel (kvs_append) and the host-read probe (a measurement helper).
 //
