@@ -144,6 +144,24 @@ def measure_h2d_peak(torch, nbytes=1 << 30, reps=5) -> float:
     return best
 
 
+def measure_d2d_peak(torch, nbytes=1 << 30, reps=5) -> float:
+    """Best of `reps` device-to-device copies of 1 GiB (torch's copy, which the
+    runtime runs as its own copy kernel), GB/s counting the read and the write:
+    the HBM rate a plain contiguous copy reaches on this GPU."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        best = max(best, 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -663,7 +681,9 @@ def main():
     log(f"inputs ready, pool {wo.pool.host.nbytes / 1e9:.2f} GB pinned")
     h2d = measure_h2d_peak(torch)
     zc = measure_zero_copy_peak(torch, kvs, wo.pool.host)
-    log(f"H2D copy peak {h2d:.1f} GB/s, zero-copy read peak {zc:.1f} GB/s")
+    d2d = measure_d2d_peak(torch)
+    log(f"H2D copy peak {h2d:.1f} GB/s, zero-copy read peak {zc:.1f} GB/s, "
+        f"D2D copy {d2d:.0f} GB/s")
     cr = wo.contract_run(args.warmup, args.steps, graph=args.graph)
     log(f"timed {args.steps} steps in {cr['elapsed'] * 1e3:.2f} ms")
     parity = None
@@ -790,6 +810,7 @@ def main():
         "hbm_gbs_step": round(hbm_bytes_step / (ms_step * 1e-3) / 1e9, 2),
         "h2d_peak_measured_gbs": round(h2d, 2),
         "zero_copy_read_peak_gbs": round(zc, 2),
+        "hbm_copy_peak_measured_gbs": round(d2d, 1),
         # decode steps/s if the step were only its miss bytes at the link's rate
         "steps_per_s_link_ceiling": {
             "pcie_gen5_x16_63gbs": round(63.0e9 / max(1.0, ROW * misses / args.steps), 1),

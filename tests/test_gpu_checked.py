@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import kvs_workload as W
-from test_gpu_parity import Harness, _meta_offsets, _torch, _u16
+from test_gpu_parity import Harness, _meta_offsets, _slot_stride, _torch, _u16
 
 pytestmark = pytest.mark.gpu
 
@@ -112,8 +112,9 @@ def test_checked_build_rejects_bad_lru_order(kind, slots):
     h = Harness(wl, wl.steps, [0, 2], library=_checked())
     try:
         _, _, order_off = _meta_offsets(h.pool)
-        base = (1 * wl.layers + 0) * wl.slots
-        order = h.pool.meta[order_off:order_off + wl.batch * wl.layers * wl.slots * 2] \
+        sp = _slot_stride(wl.slots)
+        base = (1 * wl.layers + 0) * sp
+        order = h.pool.meta[order_off:order_off + wl.batch * wl.layers * sp * 2] \
             .view(torch.int16)
 
         def plant():
@@ -139,11 +140,12 @@ def test_checked_build_rejects_bad_slot_token(value):
         s2t_off, _, _ = _meta_offsets(h.pool)
         u = 1 * wl.layers + 0
         bad = wl.context + 7 if value == "past_context" else -3
-        s2t = h.pool.meta[s2t_off:s2t_off + wl.batch * wl.layers * wl.slots * 4] \
+        sp = _slot_stride(wl.slots)
+        s2t = h.pool.meta[s2t_off:s2t_off + wl.batch * wl.layers * sp * 4] \
             .view(torch.int32)
 
         def plant():
-            s2t[u * wl.slots + 11] = bad
+            s2t[u * sp + 11] = bad
             return bad
 
         _planted(h, plant, kvs.KVS_SITE_SLOT_TOKEN)

@@ -690,17 +690,23 @@ def test_state_check_passes_on_valid_runs(case):
 
 def _meta_offsets(pool):
     # byte offsets of the per-unit arrays inside the pool's meta buffer: the
-    # library lays out tok2slot [U][N] int32, slot2tok [U][S] int32, last_used
-    # [U][S] int32 and the LRU order [U][S] uint16 in that order, each 256-byte
-    # aligned (white-box knowledge, used only to corrupt state on purpose)
+    # library lays out tok2slot [U][N] int32, slot2tok [U][Sp] int32, last_used
+    # [U][Sp] int32 and the LRU order [U][Sp] uint16 in that order, each
+    # 256-byte aligned, with Sp = S rounded up to 16 (white-box knowledge, used
+    # only to corrupt state on purpose)
     def up(x):
         return (x + 255) // 256 * 256
     U = pool.B * pool.L
     t2s = 0
     s2t = up(t2s + U * pool.N * 4)
-    lu = up(s2t + U * pool.S * 4)
-    order = up(lu + U * pool.S * 4)
+    lu = up(s2t + U * _slot_stride(pool.S) * 4)
+    order = up(lu + U * _slot_stride(pool.S) * 4)
     return s2t, lu, order
+
+
+def _slot_stride(slots):
+    """Entries between two units' slot arrays in the meta buffer (white-box)."""
+    return (slots + 15) // 16 * 16
 
 
 @pytest.mark.parametrize("what", ["maps", "order"])

@@ -53,7 +53,7 @@ int make_layout(const kvs_config* c, Layout* lay) {
     return KVS_EINVAL;
   if ((int64_t)c->batch * c->layers > 0x7fffffffLL) return KVS_EINVAL;
 
-  const uint64_t B = c->batch, L = c->layers, N = c->context, S = c->slots, K = c->topk;
+  const uint64_t B = c->batch, L = c->layers, N = c->context, K = c->topk;
   const uint64_t U = B * L;
   const int ntiles = (int)((K + 63) / 64);
   const bool separate = (c->flags & KVS_FLAG_SEPARATE_ATTENTION) != 0;
@@ -111,6 +111,9 @@ int make_layout(const kvs_config* c, Layout* lay) {
   lay->B = c->batch;
   lay->L = c->layers;
   lay->S = c->slots;
+  // the slot arrays of a unit start 16 entries apart, so each diff thread's
+  // run of order entries and slot tokens is aligned for wide loads
+  lay->Sp = (c->slots + 15) & ~15;
   lay->K = c->topk;
   lay->N = c->context;
   lay->splits = splits;
@@ -127,9 +130,10 @@ int make_layout(const kvs_config* c, Layout* lay) {
     return at;
   };
   lay->tok2slot = take(U * N * 4);
-  lay->slot2tok = take(U * S * 4);
-  lay->last_used = take(U * S * 4);
-  lay->order = take(U * S * 2);
+  const uint64_t Sp = (uint64_t)lay->Sp;
+  lay->slot2tok = take(U * Sp * 4);
+  lay->last_used = take(U * Sp * 4);
+  lay->order = take(U * Sp * 2);
   lay->stepctr = take(U * 4);
   lay->stats = take(U * 4 * 8);
   lay->status = take(16);
@@ -551,8 +555,8 @@ int kvs_debug_read_state(kvs_pool* p, int32_t req, int32_t layer, void* stream,
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
   };
   KVS_TRY_HIP(get(st->tok2slot, d.tok2slot + u * L.N, (size_t)L.N * 4));
-  KVS_TRY_HIP(get(st->slot2tok, d.slot2tok + u * L.S, (size_t)L.S * 4));
-  KVS_TRY_HIP(get(st->last_used, d.last_used + u * L.S, (size_t)L.S * 4));
+  KVS_TRY_HIP(get(st->slot2tok, d.slot2tok + u * L.Sp, (size_t)L.S * 4));
+  KVS_TRY_HIP(get(st->last_used, d.last_used + u * L.Sp, (size_t)L.S * 4));
   KVS_TRY_HIP(get(st->slot_of, ls.slot_of + (long long)req * L.K, (size_t)L.K * 4));
   KVS_TRY_HIP(get(st->miss_pos, ls.miss_pos + (long long)req * L.K, (size_t)L.K * 4));
   KVS_TRY_HIP(get(st->victims, ls.victims + (long long)req * L.K, (size_t)L.K * 4));
@@ -560,7 +564,7 @@ int kvs_debug_read_state(kvs_pool* p, int32_t req, int32_t layer, void* stream,
   KVS_TRY_HIP(get(st->counts, ls.counts + 4LL * req, 16));
   KVS_TRY_HIP(get(st->row_slot, ls.row_slot + (long long)req * L.K, (size_t)L.K * 4));
   std::vector<uint16_t> order(st->lru_order ? L.S : 0);
-  KVS_TRY_HIP(get(st->lru_order ? order.data() : nullptr, d.order + u * L.S, (size_t)L.S * 2));
+  KVS_TRY_HIP(get(st->lru_order ? order.data() : nullptr, d.order + u * L.Sp, (size_t)L.S * 2));
   int32_t step = 0;
   KVS_TRY_HIP(get(&step, d.stepctr + u, 4));
   KVS_TRY_HIP(hipStreamSynchronize(s));

@@ -25,12 +25,13 @@ struct Layout {
   int32_t fetch_per_req; // assembling launch: fetch workgroups per request
   int32_t hit_blocks;    // hit-copy workgroups of the gather launch (0 = one per 32 positions)
   int32_t flags;
+  int32_t Sp;            // per-unit stride of slot2tok / last_used / order: S rounded up to 16
   int64_t N;
   // meta (persistent state)
   uint64_t tok2slot;   // int32 [B*L][N]
-  uint64_t slot2tok;   // int32 [B*L][S]
-  uint64_t last_used;  // int32 [B*L][S]
-  uint64_t order;      // uint16 [B*L][S]: slots in ascending (last_used, slot)
+  uint64_t slot2tok;   // int32 [B*L][Sp]
+  uint64_t last_used;  // int32 [B*L][Sp]
+  uint64_t order;      // uint16 [B*L][Sp]: slots in ascending (last_used, slot)
   uint64_t stepctr;    // int32 [B*L]
   uint64_t stats;      // int64 [B*L][4]: steps, hits, misses, evictions
   uint64_t status;     // int32 [4]: sticky first error

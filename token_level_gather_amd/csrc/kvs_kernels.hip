@@ -87,6 +87,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Rows are streamed: each KV row a step moves is read once and written once
+// (no reuse within a launch), so row loads and stores carry the nontemporal
+// hint (`nt`).  On MI355X this lifts a random-row copy of 1152-byte rows from
+// 4.4 to 6.5 TB/s (measured; a plain device-to-device copy reaches 5.4).
+__device__ __forceinline__ u32x4 ld_row(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_row(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+// The same hint for buffer-resource loads and stores (cache-policy bit `nt`).
+constexpr int kNT = 2;
+
 // A lane's value from another lane of its 16-lane DPP row (gfx9 DPP control).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -148,15 +157,19 @@ __device__ __forceinline__ bool in_bounds(long long idx, long long n, int32_t* s
 
 // ------------------------------------------------------------------ init
 // Empties units [u0, u0 + count): maps -1, last_used -1, LRU order 0..S-1.
+// The slot arrays hold Sp >= S entries per unit; the padding entries are
+// never read as state (slot -1, order 0).
 __global__ void init_units_kernel(int32_t* tok2slot, int32_t* slot2tok, int32_t* last_used,
-                                  uint16_t* order, long long n_tok, long long n_slot, int S) {
+                                  uint16_t* order, long long n_tok, long long n_slot, int S,
+                                  int Sp) {
   const long long stride = (long long)gridDim.x * blockDim.x;
   const long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   for (long long i = i0; i < n_tok; i += stride) tok2slot[i] = -1;
   for (long long i = i0; i < n_slot; i += stride) {
+    const int s = (int)(i % Sp);
     slot2tok[i] = -1;
     last_used[i] = -1;
-    order[i] = (uint16_t)(i % S);
+    order[i] = (uint16_t)(s < S ? s : 0);
   }
 }
 
@@ -178,15 +191,20 @@ __global__ void clear_status_kernel(int32_t* status) {
 }
 
 // ------------------------------------------------------------------ diff + LRU
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: data format
+// 32 bits, everything else zero.  Untyped loads ignore the format, but a zero
+// format would mark the resource invalid.
+constexpr int kBufRsrcWord3 = 0x00020000;
+
 constexpr int kDiffThreads = 1024;
 constexpr int kDiffWaves = kDiffThreads / 64;
 
 struct DiffArgs {
   const int32_t* topk;     // [B][K]
   int32_t* tok2slot;       // [B*L][N]
-  int32_t* slot2tok;       // [B*L][S]
-  int32_t* last_used;      // [B*L][S]
-  uint16_t* order;         // [B*L][S]
+  int32_t* slot2tok;       // [B*L][Sp]
+  int32_t* last_used;      // [B*L][Sp]
+  uint16_t* order;         // [B*L][Sp]
   int32_t* stepctr;        // [B*L]
   long long* stats;        // [B*L][4]
   int32_t* status;
@@ -201,6 +219,7 @@ struct DiffArgs {
   int32_t* miss_tok;       // [B][K]: tokens of the misses, in Top-K order
   long long N;
   int S, K, L, layer, hash_bits;
+  int Sp;                  // per-unit stride of slot2tok / last_used / order: S rounded up to 16
   int padded;              // 1: a Top-K entry of -1 is empty
 };
 
@@ -238,15 +257,84 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wtot, int& total) {
   return off + x - v;
 }
 
+// Wide loads of a thread's run of W 32-bit words (16-byte aligned when W >= 4,
+// 8-byte when W == 2): one memory instruction per 16 bytes instead of one per
+// element.  Element-wise loads of the order and slot-token runs cost each CU
+// about one address-unit clock per cache line per instruction; at 8192 slots
+// they took 3.4 us of the diff kernel's start (measured).
+template <int W>
+__device__ __forceinline__ void load_words(const void* p, uint32_t (&w)[W]) {
+  if constexpr (W >= 4) {
+#pragma unroll
+    for (int v = 0; v < W / 4; ++v) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(p)[v];
+      w[4 * v + 0] = x[0];
+      w[4 * v + 1] = x[1];
+      w[4 * v + 2] = x[2];
+      w[4 * v + 3] = x[3];
+    }
+  } else if constexpr (W == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// The N uint16 order entries at p (aligned to 2N bytes), widened to int.
+template <int N>
+__device__ __forceinline__ void load_order(const uint16_t* p, int (&o)[N]) {
+  if constexpr (N == 1) {
+    o[0] = p[0];
+  } else {
+    uint32_t w[N / 2];
+    load_words<N / 2>(p, w);
+#pragma unroll
+    for (int q = 0; q < N; ++q) o[q] = (int)((w[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+  }
+}
+
+// Bit k set when byte k of the N bytes at p (LDS, aligned to N) is non-zero.
+template <int N>
+__device__ __forceinline__ unsigned nonzero_bytes(const uint8_t* p) {
+  unsigned mask = 0;
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int v = 0; v < N / 4; ++v) {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(p)[v];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mask |= (((w >> (8 * k)) & 0xffu) != 0u ? 1u : 0u) << (4 * v + k);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) mask |= (p[k] != 0 ? 1u : 0u) << k;
+  }
+  return mask;
+}
+
+// Zero N bytes of LDS at p (aligned to min(N, 16)) with the widest stores.
+template <int N>
+__device__ __forceinline__ void zero_bytes(uint8_t* p) {
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int v = 0; v < N / 16; ++v) reinterpret_cast<u32x4*>(p)[v] = u32x4{0u, 0u, 0u, 0u};
+  } else if constexpr (N == 8) *reinterpret_cast<uint2*>(p) = make_uint2(0u, 0u);
+  else if constexpr (N == 4) *reinterpret_cast<uint32_t*>(p) = 0u;
+  else if constexpr (N == 2) *reinterpret_cast<uint16_t*>(p) = 0;
+  else *p = 0;
+}
+
 // Thread t owns the contiguous Top-K entries [t*kpt, t*kpt + kpt) and the
-// contiguous order positions / slots [t*spt, t*spt + spt), so every
-// order-preserving compaction is one local count, one workgroup scan and one
-// local write-out.  Global loads are issued as early as their inputs allow:
-// the Top-K entries, the LRU order and the step counter at entry, then the
-// token-to-slot lookups and, for every order position, the token its slot
-// holds (so the thread that picks a victim already knows what it evicts).
-// KPT / SPT: compile-time upper bounds of the Top-K entries and slots per
-// thread (powers of two), so the per-thread loops carry no dead iterations.
+// order positions / slots [t*SPT, t*SPT + SPT), so every order-preserving
+// compaction is one local count, one workgroup scan and one local write-out.
+// The slot arrays of a unit are Sp = S rounded up to 16 entries apart, so a
+// thread's run of order entries and slot tokens is aligned for wide loads.
+// Global loads are issued as early as their inputs allow: the Top-K entries,
+// the LRU order, the slot tokens and the step counter at entry, then the
+// token-to-slot lookups.  KPT / SPT: compile-time upper bounds of the Top-K
+// entries and slots per thread (powers of two), so the per-thread loops carry
+// no dead iterations.
 template <int KPT, int SPT>
 __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -254,65 +342,81 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   __shared__ int err_bits;
   __shared__ int n_evict;
 
-  const int S = a.S, K = a.K;
+  // Every kernel argument is loaded at entry: the pointers used only after
+  // the first barrier would otherwise be loaded late, and the barrier's wait
+  // for LDS operations also waits for scalar loads (a memory round trip).
+  asm volatile("" ::"s"(a.slot_of), "s"(a.miss_pos), "s"(a.victims), "s"(a.evicted),
+               "s"(a.counts), "s"(a.row_slot), "s"(a.hit_pos), "s"(a.hit_slot));
+  const int S = a.S, K = a.K, Sp = a.Sp;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const long long u = (long long)b * a.L + a.layer;
   const int H = 1 << a.hash_bits;
   const int kpt = (K + kDiffThreads - 1) / kDiffThreads;   // <= KPT
-  const int spt = (S + kDiffThreads - 1) / kDiffThreads;   // <= SPT
   const int i0 = tid * kpt;
-  const int p0 = tid * spt;
+  const int p0 = tid * SPT;
+  const bool owns = p0 < Sp;          // the thread's run lies inside the (padded) slots
+  const int pl = min(p0, Sp - SPT);   // run loaded (past the slots: the last one, unused)
 
-  // LDS: per-slot flag [S] u8 (1 = hit, 2 = victim) | with S <= 4096 the
-  //      token of every slot [S] i32 | token hash set [H] i32, reused after
-  //      validation as miss positions [K] + victims [K] + miss tokens [K] (the
-  //      region holds max(H, 3K) words)
-  constexpr bool kLdsTok = SPT <= 4;
+  // LDS: per-slot flag [Sp] u8 (1 = hit, 2 = victim) | with S <= 8192 the
+  //      token of every slot [Sp] i32 | the new LRU order [Sp] u16 | token
+  //      hash set [H] i32, reused after validation as miss positions [K] +
+  //      victims [K] + miss tokens [K] (the region holds max(H, 3K) words)
+  constexpr bool kLdsTok = SPT <= 8;
   uint8_t* flag = smem;
   unsigned* flagw = reinterpret_cast<unsigned*>(smem);   // the same flags, 4 per word
-  int32_t* s2t = reinterpret_cast<int32_t*>(smem + ((S + 15) & ~15));
-  int32_t* hash = reinterpret_cast<int32_t*>(smem + ((S + 15) & ~15) +
-                                             (kLdsTok ? ((4 * S + 15) & ~15) : 0));
+  int32_t* s2t = reinterpret_cast<int32_t*>(smem + Sp);
+  uint16_t* lorder = reinterpret_cast<uint16_t*>(smem + Sp + (kLdsTok ? 4 * Sp : 0));
+  int32_t* hash = reinterpret_cast<int32_t*>(smem + 3 * Sp + (kLdsTok ? 4 * Sp : 0));
   int32_t* lmiss = hash;
   int32_t* lvict = hash + K;
   int32_t* lmtok = hash + 2 * K;
 
   int32_t* tok2slot = a.tok2slot + u * a.N;
-  int32_t* slot2tok = a.slot2tok + u * S;
-  int32_t* lu = a.last_used + u * S;
-  uint16_t* gorder = a.order + u * S;
+  int32_t* slot2tok = a.slot2tok + u * Sp;
+  int32_t* lu = a.last_used + u * Sp;
+  uint16_t* gorder = a.order + u * Sp;
   const int32_t* topk = a.topk + (long long)b * K;
   const long long bk = (long long)b * K;
 
-  // 0. independent loads first: Top-K entries, LRU order, step counter.  No
-  //    load sits behind a branch: indices are clamped into range and the
-  //    values of positions past K or S are never used (every later use is
-  //    guarded).  With a branch per load the compiler's wait counting takes
-  //    the path with no loads and drains every load before the next one is
-  //    issued, which serialises the two independent chains below.
+  // 0. independent loads first: Top-K entries, LRU order, slot tokens, step
+  //    counter.  No load sits behind a branch: indices are clamped into range
+  //    and the values of positions past K or S are never used (every later
+  //    use is guarded).  With a branch per load the compiler's wait counting
+  //    takes the path with no loads and drains every load before the next one
+  //    is issued, which serialises the two independent chains below.
   int my_tok[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) my_tok[j] = topk[min(i0 + j, K - 1)];
   int my_ord[SPT];
-#pragma unroll
-  for (int q = 0; q < SPT; ++q) my_ord[q] = (int)gorder[min(p0 + q, S - 1)];
-  const int t = a.stepctr[u];
-  // The token each victim's slot held.  With S <= 4096 each thread reads the
-  // tokens of its own slots [p0, p0 + spt) (contiguous, not waiting for the
-  // order) and puts them in LDS before the first scan: the gather below must
-  // wait for the order loads and held up the start of the kernel by 1.2 us at
-  // 4096 slots.  Otherwise it reads the token of the slot at each of its order
-  // positions (the order array is a permutation of the slots, so my_ord is in
-  // range); at 8192 slots over a 1M-token map the map lookups bound the start
-  // and the LDS copy gained nothing.
+  load_order<SPT>(gorder + pl, my_ord);
+  // The step counter through a buffer load, a vector-memory load that travels
+  // with the others (as a scalar load it was issued late and waited for before
+  // the first barrier: a second round trip).
+  const int t = (int)__builtin_amdgcn_raw_buffer_load_b32(
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.stepctr + u), (short)0, 4, kBufRsrcWord3), 0,
+      0, 0);
+  // The token each victim's slot held.  With S <= 8192 each thread reads the
+  // tokens of its own slots (contiguous, not waiting for the order) into LDS
+  // before the first scan; above that the LDS copy does not fit beside the
+  // other arrays, and each thread reads the token of the slot at each of its
+  // order positions (the order array is a permutation of the slots, so my_ord
+  // is in range).
   int my_old[SPT];
+  if constexpr (kLdsTok) {
+    uint32_t w[SPT];
+    load_words<SPT>(slot2tok + pl, w);
 #pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    const int p = p0 + q;
-    my_old[q] = kLdsTok ? slot2tok[min(p, S - 1)]
-                        : slot2tok[KVS_DEVICE_CHECKS ? min(my_ord[q], S - 1) : my_ord[q]];
-    if (q < spt && p < S) flag[p] = 0;
+    for (int q = 0; q < SPT; ++q) my_old[q] = (int)w[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < SPT; ++q)
+      my_old[q] = slot2tok[KVS_DEVICE_CHECKS ? min(my_ord[q], S - 1) : my_ord[q]];
+  }
+  if (owns) {
+    zero_bytes<SPT>(flag + p0);
+    // positions past S keep slot 0; every position below S is written once below
+    zero_bytes<2 * SPT>(reinterpret_cast<uint8_t*>(lorder + p0));
   }
   // 1a. slot lookup of every entry, issued before the first barrier and not
   //     used before it (an entry outside [0, N) reads token 0's slot; the
@@ -372,7 +476,7 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
 #pragma unroll
     for (int q = 0; q < SPT; ++q) {
       const int p = p0 + q;
-      if (q < spt && p < S) {
+      if (p < S) {
         const int s = my_ord[q];
         if (!in_bounds(s, S, a.status, KVS_SITE_LRU_ORDER)) {
           atomicOr(&err_bits, 8);
@@ -410,9 +514,9 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   if constexpr (KVS_DEVICE_CHECKS) {   // each slot's flag byte belongs to its order position
 #pragma unroll
     for (int q = 0; q < SPT; ++q)
-      if (q < spt && p0 + q < S) flag[my_ord[q]] &= 0x7f;
+      if (p0 + q < S) flag[my_ord[q]] &= 0x7f;
   }
-  // 2. sparse diff: record slot_of, touch hits, compact misses in Top-K order
+  // 2. sparse diff: record slot_of, compact misses in Top-K order
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -421,20 +525,43 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
       a.slot_of[bk + i] = my_slot[j];
       // a miss's row slot is its victim, written once in step 5
       if (my_slot[j] != -1) a.row_slot[bk + i] = my_slot[j] >= 0 ? my_slot[j] : -1;
-      if (my_slot[j] >= 0) lu[my_slot[j]] = t;
-      else if (my_slot[j] == -1) ++cnt;
+      if (my_slot[j] == -1) ++cnt;
     }
   }
+  // bit q: order position p0 + q holds a non-hit slot (each slot sits at one
+  // order position, so no other thread writes these flags before the victims
+  // below read the mask instead of the flags)
+  // (the flag reads are unconditional, so they are issued together; the order
+  // entries of positions past S are slot 0)
+  unsigned nonhit = 0;
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
-    const int p = p0 + q;
-    if (q < spt && p < S && flag[my_ord[q]] == 0) cnt += 1 << 16;
-    if (kLdsTok && q < spt && p < S) s2t[p] = my_old[q];   // read after the scan's barrier
+    const bool free_slot = flag[min(my_ord[q], Sp - 1)] == 0;
+    if (p0 + q < S && free_slot) {
+      cnt += 1 << 16;
+      nonhit |= 1u << q;
+    }
+  }
+  if (kLdsTok && owns) {   // read after the scan's barrier
+    if constexpr (SPT >= 4) {
+#pragma unroll
+      for (int v = 0; v < SPT / 4; ++v)
+        reinterpret_cast<int4*>(s2t + p0)[v] =
+            make_int4(my_old[4 * v], my_old[4 * v + 1], my_old[4 * v + 2], my_old[4 * v + 3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < SPT; ++q) s2t[p0 + q] = my_old[q];
+    }
   }
   int packed;
   const int ex = wg_exclusive_scan(cnt, wtot[0], packed);
   const int m = packed & 0xffff;
   const int n_hit = S - (packed >> 16);
+  // the token of the slot at each of this thread's order positions, read
+  // before any write below (victims use it)
+  int vold[SPT];
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) vold[q] = kLdsTok ? s2t[min(my_ord[q], Sp - 1)] : my_old[q];
   int r = ex & 0xffff;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -446,32 +573,32 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     }
   }
 
-  // 3. victims: the first m non-hit slots of the LRU order, evicted here; the
-  //    other non-hit slots keep their relative order at the front of the new
-  //    order.  Each slot sits at one order position, so each flag byte below
-  //    is read and written by one thread only.
+  // 3. victims: the first m non-hit slots of the LRU order; the other
+  //    non-hit slots keep their relative order at the front of the new order
+  //    (built in LDS, written out below).  Each slot sits at one order
+  //    position, so each flag byte below is written by one thread only.  The
+  //    victims sit at the front of the order, in the first few threads: with
+  //    the slot tokens in LDS their eviction stores wait for the map update,
+  //    which spreads them over every thread.
   r = ex >> 16;
   int my_evict = 0;
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
-    const int p = p0 + q;
-    if (q < spt && p < S) {
+    if ((nonhit >> q) & 1u) {
       const int s = my_ord[q];
-      if (flag[s] == 0) {
-        if (r < m) {
-          lvict[r] = s;
-          flag[s] = 2;
-          const int old = kLdsTok ? s2t[s] : my_old[q];
+      if (r < m) {
+        lvict[r] = s;
+        flag[s] = 2;
+        const int old = vold[q];
+        if (old >= 0) ++my_evict;
+        if constexpr (!kLdsTok) {
           a.evicted[bk + r] = old;
-          if (old >= 0) {
-            tok2slot[old] = -1;   // evicted tokens are outside the Top-K set
-            ++my_evict;
-          }
-        } else if (in_bounds(r - m, S, a.status, KVS_SITE_DIFF_LIST)) {
-          gorder[r - m] = (uint16_t)s;
+          if (old >= 0) tok2slot[old] = -1;   // evicted tokens are outside the Top-K set
         }
-        ++r;
+      } else if (in_bounds(r - m, S, a.status, KVS_SITE_DIFF_LIST)) {
+        lorder[r - m] = (uint16_t)s;
       }
+      ++r;
     }
   }
   // one LDS atomic per wave (the wave's sum sits in its last lane): an
@@ -482,24 +609,26 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
 
   // 4. the n_hit + m touched slots (hits and victims, all stamped t) close the
   //    order, ascending by slot.  The same scan counts the empty entries
-  //    (high 16 bits), which places each thread's hits in the hit list.
-  cnt = 0;
-#pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    const int s = p0 + q;
-    if (q < spt && s < S && flag[s] != 0) ++cnt;
-  }
+  //    (high 16 bits), which places each thread's hits in the hit list.  The
+  //    flags of slots past S are zero (cleared, never set).
+  const unsigned touched = owns ? nonzero_bytes<SPT>(flag + p0) : 0u;
+  cnt = __builtin_popcount(touched);
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (j < kpt && i0 + j < K && my_slot[j] == -2) cnt += 1 << 16;
   int n_touched;
   const int ex2 = wg_exclusive_scan(cnt, wtot[1], n_touched);
+  // touched slots are stamped t here, from each thread's own contiguous
+  // slots (stores a wave covers in a few cache lines, where stamping each hit
+  // and victim through its slot index scatters them)
   r = S - (n_hit + m) + (ex2 & 0xffff);
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
-    const int s = p0 + q;
-    if (q < spt && s < S && flag[s] != 0 && in_bounds(r, S, a.status, KVS_SITE_DIFF_LIST))
-      gorder[r++] = (uint16_t)s;
+    if ((touched >> q) & 1u) {
+      const int s = p0 + q;
+      lu[s] = t;
+      if (in_bounds(r, S, a.status, KVS_SITE_DIFF_LIST)) lorder[r++] = (uint16_t)s;
+    }
   }
   // hits in Top-K order: entries before this thread's, less its misses and empties
   r = i0 - (ex & 0xffff) - (ex2 >> 16);
@@ -524,15 +653,38 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     a.stepctr[u] = t + 1;
   }
 
-  // 5. map update: the j-th miss takes the j-th victim
+  __syncthreads();   // the new order is complete in LDS
+  // each thread writes its run of the new order with one wide store
+  if (owns) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(lorder + p0);
+    uint8_t* dst = reinterpret_cast<uint8_t*>(gorder + p0);
+    if constexpr (SPT >= 8) {
+#pragma unroll
+      for (int v = 0; v < SPT / 8; ++v)
+        reinterpret_cast<u32x4*>(dst)[v] = reinterpret_cast<const u32x4*>(src)[v];
+    } else if constexpr (SPT == 4) {
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    } else if constexpr (SPT == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+    } else {
+      *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
+    }
+  }
+
+  // 5. map update: the j-th miss takes the j-th victim (and, with the slot
+  //    tokens in LDS, the victim's old token leaves the map here)
   for (int j = tid; j < m; j += kDiffThreads) {
     const int i = lmiss[j];
     const int tok = lmtok[j];
     const int v = lvict[j];
     if (!in_bounds(v, S, a.status, KVS_SITE_DIFF_LIST)) continue;
+    if constexpr (kLdsTok) {
+      const int old = s2t[v];
+      a.evicted[bk + j] = old;
+      if (old >= 0) tok2slot[old] = -1;   // evicted tokens are outside the Top-K set
+    }
     slot2tok[v] = tok;
     tok2slot[tok] = v;
-    lu[v] = t;
     a.miss_pos[bk + j] = i;
     a.miss_tok[bk + j] = tok;
     a.victims[bk + j] = v;
@@ -617,8 +769,8 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
         if (pos[j] >= 0) {
           const int c = j * kCopyThreads + threadIdx.x;
           const int col = c - (c / kRowChunks) * kRowChunks;
-          if (a.write_cbuf) a.cbuf[(bk + pos[j]) * kRowChunks + col] = v[j];
-          a.hot[(u * a.S + vic[j]) * kRowChunks + col] = v[j];
+          if (a.write_cbuf) st_row(a.cbuf + (bk + pos[j]) * kRowChunks + col, v[j]);
+          st_row(a.hot + (u * a.S + vic[j]) * kRowChunks + col, v[j]);
         }
       }
     }
@@ -645,16 +797,16 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
     u32x4* dst = a.cbuf + ((long long)b * K + i) * kRowChunks + sub;
     if (s < 0) {             // an empty entry of a padded Top-K gathers a zero row
 #pragma unroll
-      for (int j = 0; j < kCopyItems; ++j) dst[8 * j] = u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < kCopyItems; ++j) st_row(dst + 8 * j, u32x4{0u, 0u, 0u, 0u});
       continue;
     }
     const long long u = (long long)b * a.L + a.layer;
     const u32x4* src = a.hot + (u * a.S + s) * kRowChunks + sub;
     u32x4 v[kCopyItems];
 #pragma unroll
-    for (int j = 0; j < kCopyItems; ++j) v[j] = src[8 * j];
+    for (int j = 0; j < kCopyItems; ++j) v[j] = ld_row(src + 8 * j);
 #pragma unroll
-    for (int j = 0; j < kCopyItems; ++j) dst[8 * j] = v[j];
+    for (int j = 0; j < kCopyItems; ++j) st_row(dst + 8 * j, v[j]);
   }
 }
 
@@ -667,10 +819,6 @@ constexpr int kKSteps = kRowElems / 32;         // 18 MFMA k-steps over 576 dims
 constexpr int kKHalf = kKSteps / 2;             // each Q.K^T wave takes half of them
 constexpr int kPRow = kTile + 8;                // bf16 P row stride (144 B)
 constexpr int kMaxParts = 256;   // attention partials per request merged by the combine
-// Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: data format
-// 32 bits, everything else zero.  Untyped loads ignore the format, but a zero
-// format would mark the resource invalid.
-constexpr int kBufRsrcWord3 = 0x00020000;
 static_assert(kTile * 8 == kAttnThreads && kAttnItems * 8 == kRowChunks, "attention tiling");
 static_assert(kKHalf * 2 == kKSteps, "k split");
 
@@ -905,7 +1053,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
                                : tok * kRowBytes + lsub * 16;
 #pragma unroll
     for (int j = 0; j < kAttnItems; ++j)
-      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + j * 128, 0, 0);
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + j * 128, 0, kNT);
     dv = __builtin_amdgcn_raw_buffer_load_b32(vsrc, tile < te ? (tile * kTile + lrow) * 4 : K * 4,
                                               0, 0);
   };
@@ -1113,8 +1261,8 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
         const int r = c / kRowChunks;
         const int col = c - r * kRowChunks;
         if (pos[jj] >= 0) {
-          hot[(u * a.S + vic[jj]) * kRowChunks + col] = v[jj];
-          if (cbuf != nullptr) cbuf[(bk + pos[jj]) * kRowChunks + col] = v[jj];
+          st_row(hot + (u * a.S + vic[jj]) * kRowChunks + col, v[jj]);
+          if (cbuf != nullptr) st_row(cbuf + (bk + pos[jj]) * kRowChunks + col, v[jj]);
         }
         *reinterpret_cast<u32x4*>(kv + r * kLdsRow + ((col ^ lds_swz(r)) * 16)) = v[jj];
       }
@@ -1169,7 +1317,7 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
       const int off = in ? slot * kRowBytes + lsub * 16 : hot_bytes;
 #pragma unroll
       for (int j = 0; j < kAttnItems; ++j)
-        dst[j] = __builtin_amdgcn_raw_buffer_load_b128(hsrc, off + j * 128, 0, 0);
+        dst[j] = __builtin_amdgcn_raw_buffer_load_b128(hsrc, off + j * 128, 0, kNT);
     };
     const int lsw = lds_swz(lrow);
     auto store_tile = [&](const u32x4 (&src)[kAttnItems], int tile, int pos) {
@@ -1180,7 +1328,7 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
 #pragma unroll
       for (int j = 0; j < kAttnItems; ++j) {
         *reinterpret_cast<u32x4*>(d + j * 128) = src[j];
-        __builtin_amdgcn_raw_buffer_store_b128(src[j], csrc, coff + j * 128, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(src[j], csrc, coff + j * 128, 0, kNT);
       }
     };
     auto compute = [&](int tile) {
@@ -1300,17 +1448,17 @@ __global__ __launch_bounds__(kCheckThreads) void check_state_kernel(
     const int32_t* __restrict__ tok2slot, const int32_t* __restrict__ slot2tok,
     const int32_t* __restrict__ last_used, const uint16_t* __restrict__ order,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ victims,
-    const int32_t* __restrict__ counts, int32_t* status, long long N, int S, int K, int L,
-    int layer) {
+    const int32_t* __restrict__ counts, int32_t* status, long long N, int S, int Sp, int K,
+    int L, int layer) {
   extern __shared__ unsigned hitbits[];   // one bit per slot: hit slots of this step
   __shared__ int bad;
   const int b = blockIdx.x, tid = threadIdx.x;
   if (counts[4 * b + 3] == 0) return;     // invalid input: the unit was left untouched
   const long long u = (long long)b * L + layer;
   const int32_t* t2s = tok2slot + u * N;
-  const int32_t* s2t = slot2tok + u * S;
-  const int32_t* lu = last_used + u * S;
-  const uint16_t* ord = order + u * S;
+  const int32_t* s2t = slot2tok + u * Sp;
+  const int32_t* lu = last_used + u * Sp;
+  const uint16_t* ord = order + u * Sp;
   const long long bk = (long long)b * K;
   for (int w = tid; w < (S + 31) / 32; w += kCheckThreads) hitbits[w] = 0u;
   if (tid == 0) bad = 0;
@@ -1416,8 +1564,9 @@ size_t diff_lds_bytes(int S, int K) {
   int hb = 1;
   while ((1 << hb) < 2 * K) ++hb;
   const size_t words = (1u << hb) > 3u * K ? (1u << hb) : 3u * K;
-  const size_t tok = S <= 4 * kDiffThreads ? (size_t)((4 * S + 15) & ~15) : 0;   // slot tokens
-  return (size_t)((S + 15) & ~15) + tok + 4 * words;
+  const size_t Sp = (size_t)((S + 15) & ~15);
+  const size_t tok = S <= 8 * kDiffThreads ? 4 * Sp : 0;   // slot tokens
+  return Sp + tok + 2 * Sp + 4 * words;                    // flags, tokens, new order, lists
 }
 
 static int hash_bits_for(int K) {
@@ -1429,15 +1578,15 @@ static int hash_bits_for(int K) {
 hipError_t launch_init_units(const Layout& lay, const DevPtrs& d, int unit_begin, int unit_count,
                              bool reset_counters, hipStream_t s) {
   const long long n_tok = (long long)unit_count * lay.N;
-  const long long n_slot = (long long)unit_count * lay.S;
+  const long long n_slot = (long long)unit_count * lay.Sp;
   const long long work = n_tok > n_slot ? n_tok : n_slot;
   long long blocks = (work + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(init_units_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      d.tok2slot + (long long)unit_begin * lay.N,
-                     d.slot2tok + (long long)unit_begin * lay.S,
-                     d.last_used + (long long)unit_begin * lay.S,
-                     d.order + (long long)unit_begin * lay.S, n_tok, n_slot, lay.S);
+                     d.slot2tok + (long long)unit_begin * lay.Sp,
+                     d.last_used + (long long)unit_begin * lay.Sp,
+                     d.order + (long long)unit_begin * lay.Sp, n_tok, n_slot, lay.S, lay.Sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !reset_counters) return e;
   const int units = lay.B * lay.L;
@@ -1472,8 +1621,9 @@ static_assert(KVS_MAX_TOPK <= 8 * kDiffThreads && KVS_MAX_SLOTS <= 16 * kDiffThr
               "diff_lru instantiations cover the limits");
 
 hipError_t prepare_kernels() {
-  // the diff kernel's dynamic LDS can exceed the 64 KiB default (up to 112 KiB)
-  const int max_lds = (int)std::max(diff_lds_bytes(4 * kDiffThreads, 4 * kDiffThreads),
+  // the diff kernel's dynamic LDS can exceed the 64 KiB default (up to 152 KiB,
+  // at 8192 slots with their tokens in LDS and the largest Top-K)
+  const int max_lds = (int)std::max(diff_lds_bytes(8 * kDiffThreads, KVS_MAX_TOPK),
                                     diff_lds_bytes(KVS_MAX_SLOTS, KVS_MAX_TOPK));
   for (int kpt = 1; kpt <= 8; kpt *= 2)
     for (int spt = 1; spt <= 16; spt *= 2) {
@@ -1512,6 +1662,7 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const
   a.L = lay.L;
   a.layer = layer;
   a.hash_bits = hash_bits_for(lay.K);
+  a.Sp = lay.Sp;
   a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
   const void* fn = diff_kernel_for(lay.K, lay.S);
   void* args[] = {&a};
@@ -1628,7 +1779,7 @@ hipError_t launch_check_state(const Layout& lay, const DevPtrs& d, int layer, hi
   const size_t lds = (size_t)((lay.S + 31) / 32) * 4;
   hipLaunchKernelGGL(check_state_kernel, dim3(lay.B), dim3(kCheckThreads), lds, s, d.tok2slot,
                      d.slot2tok, d.last_used, d.order, d.slot_of, d.victims, d.counts, d.status,
-                     (long long)lay.N, lay.S, lay.K, lay.L, layer);
+                     (long long)lay.N, lay.S, lay.Sp, lay.K, lay.L, layer);
   return hipGetLastError();
 }
 
