@@ -506,16 +506,11 @@ class Workload:
         alg = self.algorithmic(hits / calls, misses / calls)
         return self.kernel_stats(kt, alg, KERNEL_NAMES, zc_gbs), hits, misses, alg
 
-    def hit_copy(self, reps=3):
-        """The hit copy alone, with a working set well above the 256 MB Infinity
-        Cache.  Two all-hit Top-K sets per unit are replayed in turn, layer after
-        layer: A = the last step's Top-K and B = K other resident tokens (every
-        slot is occupied by then, and S >= 2K in every workload).  All of each
-        set is resident, so every entry is a hit and the gather launch is the HBM
-        hit copy only: 1152 B read + 1152 B written per row.  Between two reads
-        of a hot row come the reads of every other unit's two sets."""
-        if self.args.direct_hot:
-            return None
+    def hit_sets(self):
+        """Two all-hit Top-K sets per unit after the last step run: A = that
+        step's Top-K and B = K other resident tokens (every slot is occupied by
+        then, and S >= 2K in every workload).  Every entry of either set is a
+        hit, so a copy launch over it moves only HBM rows."""
         torch, pool, wl, t = self.torch, self.pool, self.wl, self.last_t
         B, L, K = wl.batch, wl.layers, wl.topk
         set_a = self.topk[t]                                     # [L][B][K]
@@ -528,9 +523,22 @@ class Workload:
                 if other.size < K:
                     return None
                 set_b[l, b] = torch.from_numpy(other[:K].astype(np.int32))
-        sets = (set_a, set_b)
-        kname = "gather" if self.args.separate else "assemble"
-        self.sync_ok()
+        return t, (set_a, set_b)
+
+    def hit_copy(self, sets, pool=None, kname=None, reps=3):
+        """The hit copy alone, with a working set well above the 256 MB Infinity
+        Cache: the two all-hit sets replayed in turn, layer after layer, so
+        between two reads of a hot row come the reads of every other unit's two
+        sets.  `pool` / `kname`: the copy launch timed (default: this pool's
+        own, the assembling launch, or the gather with separate launches)."""
+        if sets is None or self.args.direct_hot:
+            return None
+        t, sets = sets
+        wl = self.wl
+        B, L, K = wl.batch, wl.layers, wl.topk
+        pool = self.pool if pool is None else pool
+        if kname is None:
+            kname = "gather" if self.args.separate else "assemble"
         _, sa = pool.sync_status()
         pool.profile_begin(reps * 2 * L, kernels=(kname,))
         for _ in range(reps):
@@ -538,7 +546,9 @@ class Workload:
                 for l in range(L):
                     pool.step(l, tk[l], self.q[t, l], self.out[t, l], self.lse[t, l])
         kh = pool.profile_end()
-        sb = self.sync_ok()
+        rc, sb = pool.sync_status()
+        if rc != 0:
+            raise RuntimeError(f"{wl.name}: device status {self.kvs.strerror(rc)}")
         launches = kh["launches"][kname]
         assert launches == reps * 2 * L, launches
         assert sb.misses == sa.misses, "the hit-copy replay fetched rows"
@@ -546,14 +556,38 @@ class Workload:
         avg_ms = kh[kname] / launches
         gbs = 2 * ROW * rows / (avg_ms * 1e-3) / 1e9
         working_set = (2 * L * B * K + B * K) * ROW    # both sets' hot rows + the compute buffer
+        note = ("two disjoint all-hit Top-K sets per unit replayed in turn over every layer; "
+                "working set = both sets' hot rows + the compute buffer")
+        if kname == "assemble":
+            note += "; the assembling launch also attends over the rows it copies"
         return {"rows_per_launch": int(rows), "bytes_per_launch": int(2 * ROW * rows),
                 "avg_ms": round(avg_ms, 5), "achieved_gbs": round(gbs, 1),
                 "peak_gbs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
-                "working_set_mb": round(working_set / 1e6, 1), "kernel": kname,
-                "note": "two disjoint all-hit Top-K sets per unit replayed in turn over every "
-                        "layer; working set = both sets' hot rows + the compute buffer"
-                        + ("" if self.args.separate else
-                           "; the assembling launch also attends over the rows it copies")}
+                "working_set_mb": round(working_set / 1e6, 1), "kernel": kname, "note": note}
+
+    def index_copy(self, sets):
+        """The index copy alone (the gather kernel: hits copied within HBM into
+        the compute buffer, no attention), timed like hit_copy on a second pool
+        over the same host rows whose copy and attention are separate launches.
+        It runs the same decode steps first, so its hot buffers and maps equal
+        this pool's and the same all-hit sets apply."""
+        if sets is None or self.args.separate or self.args.direct_hot:
+            return None
+        kvs, wl = self.kvs, self.wl
+        t = sets[0]
+        p2 = kvs.Pool(wl.batch, wl.layers, wl.context, wl.slots, wl.topk, scale=wl.scale,
+                      flags=kvs.KVS_FLAG_SEPARATE_ATTENTION, host=self.pool.host)
+        try:
+            for s in range(t + 1):
+                for l in range(wl.layers):
+                    p2.step(l, self.topk[s, l], self.q[s, l], self.out[s, l], self.lse[s, l])
+            res = self.hit_copy(sets, pool=p2, kname="gather")
+        finally:
+            p2.release()
+        if res is not None:
+            res["note"] = ("index copy alone (gather kernel of the separate launches, pool over "
+                           "the same host rows run through the same steps); " + res["note"])
+        return res
 
     def parity(self, steps, reqs, rec):
         """GPU outputs of steps 0..steps-1 and final maps of the sampled requests
@@ -585,7 +619,7 @@ class Workload:
                 "lse_max_abs": round(max_lse, 6), "pass": ok}
 
 
-def summarize(wlo, times, kernels, hits, misses, hit_copy, parity, zc_gbs, wall):
+def summarize(wlo, times, kernels, hits, misses, hit_copy, index_copy, parity, zc_gbs, wall):
     """Per-workload results of the measurement protocol."""
     wl = wlo.wl
     steady = [statistics.mean(r[1:]) for r in times]
@@ -606,6 +640,7 @@ def summarize(wlo, times, kernels, hits, misses, hit_copy, parity, zc_gbs, wall)
         "host_link_gbs_step": round(ROW * misses / (len(times[0]) - 1) / (ms * 1e-3) / 1e9, 3),
         "kernels": kernels,
         "hit_copy": hit_copy,
+        "index_copy": index_copy,
         "parity": parity,
         "wall_s": round(wall, 1),
     }
@@ -698,9 +733,11 @@ def main():
             failed.append(head.name)
     times = wo.replays(args.replays, head.steps)
     kernels, hits_b, misses_b, _ = wo.breakdown(head.steps, zc)
-    hit_copy = wo.hit_copy()
-    results[head.name] = summarize(wo, times, kernels, hits_b, misses_b, hit_copy, parity, zc,
-                                   time.perf_counter() - t0)
+    sets = wo.hit_sets()
+    hit_copy = wo.hit_copy(sets)
+    index_copy = wo.index_copy(sets)
+    results[head.name] = summarize(wo, times, kernels, hits_b, misses_b, hit_copy, index_copy,
+                                   parity, zc, time.perf_counter() - t0)
     log(f"{head.name}: {results[head.name]['ms_per_step']} ms/step median of replays")
 
     ms_step = cr["elapsed"] * 1e3 / args.steps
@@ -766,9 +803,11 @@ def main():
                 failed.append(name)
         times = wo.replays(args.replays, wl.steps)
         kernels, hits_b, misses_b, _ = wo.breakdown(wl.steps, zc)
-        hit_copy = wo.hit_copy()
-        results[name] = summarize(wo, times, kernels, hits_b, misses_b, hit_copy, pr, zc,
-                                  time.perf_counter() - t0)
+        sets = wo.hit_sets()
+        hit_copy = wo.hit_copy(sets)
+        index_copy = wo.index_copy(sets)
+        results[name] = summarize(wo, times, kernels, hits_b, misses_b, hit_copy, index_copy,
+                                  pr, zc, time.perf_counter() - t0)
         log(f"{name}: {results[name]['ms_per_step']} ms/step, parity "
             f"{None if pr is None else pr['pass']}, {results[name]['wall_s']} s")
         wo.close()
@@ -819,7 +858,10 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "kernels": hr["kernels"],
-        "hit_gather": hr["hit_copy"],
+        # the index copy of the hits alone (gather kernel), and the assembling
+        # launch that copies and attends over them in one pass (the default step)
+        "hit_gather": hr["index_copy"] or hr["hit_copy"],
+        "hit_gather_fused": hr["hit_copy"] if hr["index_copy"] else None,
         "protocol": {k: hr[k] for k in ("steps", "replays", "ms_per_step", "ms_per_step_replays",
                                         "cold_step_ms", "miss_rate")},
         "configs": results,

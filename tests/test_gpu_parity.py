@@ -315,6 +315,41 @@ def test_padded_topk_explicit_splits():
 
 # ---------------------------------------------------------------- rows read in place
 
+@pytest.mark.parametrize("mode", ["default", "direct", "padded", "more_fetch"])
+def test_steps_without_misses_every_unit(mode):
+    # Steps whose Top-K is all resident (the previous step's set, reordered):
+    # every request has no miss, so its fetch workgroups take shares of the
+    # hit tiles in the assembling launch.  Normal steps before and after.
+    import token_level_gather_amd as kvs
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="all_hit", batch=3, layers=2, context=3000,
+                                                  slots=800, topk=300, steps=8, fresh_rate=0.3)
+    kw = {}
+    if mode == "direct":
+        kw["flags"] = kvs.KVS_FLAG_DIRECT_HOT
+    if mode == "more_fetch":   # more fetch than hit workgroups per request
+        kw.update(fetch_blocks=15, attn_splits=2)
+    h = Harness(wl, wl.steps, range(wl.batch), padded=mode == "padded", **kw)
+    rng = np.random.default_rng(7)
+    try:
+        for t in range(wl.steps):
+            for l in range(wl.layers):
+                tk = h.topk[t, l]
+                if t in (3, 4, 6):   # the previous step's Top-K in a new order
+                    prev = h.topk[t - 1, l]
+                    tk = np.stack([prev[b][rng.permutation(wl.topk)] for b in range(wl.batch)])
+                    h.topk[t, l] = tk
+                tk, q = h.device_step(t, l, topk=tk)
+                h.check(t, l, tk, q)
+                if t in (3, 4, 6):
+                    for b in range(wl.batch):
+                        assert h.pool.read_state(b, l)["counts"][1] == 0   # no miss
+        rc, stats = h.pool.sync_status()
+        assert rc == 0
+        h.check_stats(stats)
+    finally:
+        h.close()
+
+
 def _direct():
     import token_level_gather_amd as kvs
     return kvs.KVS_FLAG_DIRECT_HOT

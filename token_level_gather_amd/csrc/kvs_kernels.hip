@@ -788,10 +788,13 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
   for (long long grp = id - a.fetch_wgs; grp < n_groups; grp += a.hit_wgs) {
     const int b = (int)(grp / groups_per_req);
     const int x = (int)(grp - (long long)b * groups_per_req);
-    if (a.counts[4 * b + 3] == 0) continue;
     const int i = x * kCopyRows + rsub;
-    if (i >= K) continue;
-    const int s = a.slot_of[(long long)b * K + i];
+    // the request's valid flag and the slot are loaded together (the slot
+    // index is clamped into the request's K entries and discarded below when
+    // the position lies past K): one round trip before the row loads, not two
+    const int valid = a.counts[4 * b + 3];
+    const int s = a.slot_of[(long long)b * K + min(i, K - 1)];
+    if (valid == 0 || i >= K) continue;
     if (s == -1) continue;   // a miss: the fetch role writes it
     if (!in_range(s, -2, a.S, a.status, KVS_SITE_HIT)) continue;
     u32x4* dst = a.cbuf + ((long long)b * K + i) * kRowChunks + sub;
@@ -1146,14 +1149,16 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ assemble + attend
 // The index copy and the attention of one layer in one launch.  Two roles:
-//  fetch  workgroup (b, x), x < fetch_per_req: passes of 64 misses of request
-//         b (pass x, x + fetch_per_req, ...): each row read straight from
-//         pinned host memory over PCIe (each wave instruction reads 1 KB of
-//         consecutive host memory), written to cbuf[b][miss_pos_j] and to the
-//         victim slot hot[b][l][v_j], and attended from LDS; partial x + hits.
+//  fetch  workgroup (b, x), x < fetch_per_req: the x-th of fetch_per_req equal
+//         shares of request b's miss rows, in passes of up to 64: each row
+//         read straight from pinned host memory over PCIe (each wave
+//         instruction reads 1 KB of consecutive host memory), written to
+//         cbuf[b][miss_pos_j] and to the victim slot hot[b][l][v_j], and
+//         attended from LDS; partial hit_per_req + x.
 //  hits   workgroup (b, x), x < hit_per_req: the x-th share of request b's hit
 //         tiles (64 hits each, Top-K order), read from the hot buffer, written
-//         to cbuf[b][hit_pos_j] and attended; partial x.
+//         to cbuf[b][hit_pos_j] and attended; partial x.  A request with no
+//         miss spreads its hit tiles over its fetch workgroups too.
 // Hit rows are resident before the step, so their attention runs while the
 // host link delivers the misses; the combine merges every partial of a
 // request.  Hit slots and victim slots are disjoint, so the roles never touch
@@ -1222,7 +1227,11 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
   for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (tid < kTile) vmark[tid] = 0;
 
-  if (fetch) {
+  // A request with no miss this step leaves its fetch workgroups nothing to
+  // fetch: they take shares of its hit tiles beside the hit workgroups.  The
+  // split depends only on the step's counts, so it is the same on every run.
+  const bool all_hit = n_miss == 0;
+  if (fetch && !all_hit) {
     // chunk c = 512 jj + tid of the pass's 64 x 72 chunks: row c / 72, column c % 72
     u32x4* hot = reinterpret_cast<u32x4*>(a.hot);
     u32x4* cbuf = reinterpret_cast<u32x4*>(a.cbuf);
@@ -1271,11 +1280,15 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
                   a.scale_log2);
     }
   } else {
+    // this workgroup's share xh of nh: hit workgroups first, then (when the
+    // request has no miss) its fetch workgroups
+    const int nh = a.hit_per_req + (all_hit ? a.fetch_per_req : 0);
+    const int xh = fetch ? a.hit_per_req + x : x;
     // compute-buffer rows of empty entries (padded Top-K) are zero: this
     // workgroup's share of the positions, 8 threads per row
     if (a.padded && a.cbuf != nullptr) {
-      const int lo = (int)((long long)x * K / a.hit_per_req);
-      const int hi = (int)((long long)(x + 1) * K / a.hit_per_req);
+      const int lo = (int)((long long)xh * K / nh);
+      const int hi = (int)((long long)(xh + 1) * K / nh);
       u32x4* cb = reinterpret_cast<u32x4*>(a.cbuf) + bk * kRowChunks;
       for (int i = lo + (tid >> 3); i < hi; i += kAttnThreads / 8)
         if (a.slot_of[bk + i] == -2)
@@ -1284,8 +1297,8 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
             cb[(long long)i * kRowChunks + (tid & 7) + 8 * j] = u32x4{0u, 0u, 0u, 0u};
     }
     const int ntiles = (n_hit + kTile - 1) / kTile;
-    const int tb = (int)((long long)x * ntiles / a.hit_per_req);
-    const int te = (int)((long long)(x + 1) * ntiles / a.hit_per_req);
+    const int tb = (int)((long long)xh * ntiles / nh);
+    const int te = (int)((long long)(xh + 1) * ntiles / nh);
     // 8 threads per row: thread (row tid / 8, sub tid % 8) moves chunks sub + 8j.
     // Rows are read through a buffer resource over the unit's S hot rows and
     // written through one over request b's K compute-buffer rows (none when
