@@ -123,8 +123,13 @@ typedef struct kvs_config {
   float scale;          /* softmax scale > 0, e.g. 1/sqrt(576) */
   int32_t attn_splits;  /* token splits per request in attention, 1..64 and at most ceil(K/64):
                            the hit workgroups per request of the assembling launch (each
-                           attends over its share of the hits), or the attention's splits
-                           with KVS_FLAG_SEPARATE_ATTENTION; 0 = library's choice */
+                           attends over its share of the hits), or, with
+                           KVS_FLAG_SEPARATE_ATTENTION, the attention's workgroups per
+                           request (each takes an equal share of the request's 64-token
+                           tiles); 0 = library's choice (separate attention: the
+                           B*ceil(K/64) tiles shared evenly by at most 256 workgroups,
+                           request after request, so one workgroup's share may span
+                           requests) */
   int32_t fetch_blocks; /* workgroups that fetch misses over PCIe, 1..65535, spread evenly over
                            the requests (assembling launch: at most ceil(K/64) per request);
                            0 = library's choice */
@@ -166,7 +171,7 @@ typedef struct kvs_config {
 #define KVS_FLAG_CHECK 8
 /* kvs_config.flags: run the index copy and the attention as separate launches
  * (gather, then attention over the complete compute buffer, then the merge of
- * its token splits).  By default one assembling launch does both: workgroups
+ * its partials).  By default one assembling launch does both: workgroups
  * that fetch misses over PCIe attend over the rows they fetched, workgroups
  * that copy hits attend over the hits while the host link delivers the
  * misses, and a merge launch combines their partials.  Results are identical
@@ -181,7 +186,9 @@ typedef struct kvs_sizes {
   uint64_t cbuf_bytes;      /* B*K*576*2: compute buffer of one step, device (0 with
                                KVS_FLAG_DIRECT_HOT) */
   uint64_t scratch_bytes;   /* per-step lists and attention partials, device */
-  int32_t attn_splits;      /* the resolved kvs_config.attn_splits these sizes assume */
+  int32_t attn_splits;      /* the resolved kvs_config.attn_splits these sizes assume
+                               (KVS_FLAG_SEPARATE_ATTENTION: the attention partials per
+                               request, the most workgroups one request's tiles span) */
   int32_t fetch_blocks;     /* resolved kvs_config.fetch_blocks */
 } kvs_sizes;
 

@@ -187,6 +187,31 @@ def test_fetch_blocks_resolve():
     assert s.fetch_blocks == 256
 
 
+def _separate_parts(batch, topk):
+    """Partials per request of the separate attention: its workgroups share the
+    batch * ceil(topk/64) tiles evenly (one round of at most 256, the fewest
+    that reach ceil(tiles / 256) each); a request's partials are the
+    workgroups its tiles fall in."""
+    t = -(-topk // 64)
+    g = batch * t
+    per = -(-g // 256)
+    w = -(-g // per)
+
+    def share(tile):   # workgroup whose share [w*g//W, (w+1)*g//W) holds the tile
+        return next(i for i in range(w) if i * g // w <= tile < (i + 1) * g // w)
+    return max(share(b * t + t - 1) - share(b * t) + 1 for b in range(batch))
+
+
+@pytest.mark.parametrize("batch,topk,parts", [
+    (192, 2048, 2), (64, 2048, 4), (32, 2048, 8), (4, 2048, 32), (1, 256, 4), (17, 2048, 12),
+    (9, 2100, 17)])
+def test_separate_attention_partials(batch, topk, parts):
+    s = kvs.query_sizes(kvs.make_config(batch=batch, layers=1, context=max(4096, topk),
+                                        slots=topk, topk=topk,
+                                        flags=kvs.KVS_FLAG_SEPARATE_ATTENTION))
+    assert s.attn_splits == parts == _separate_parts(batch, topk)
+
+
 @pytest.mark.parametrize("batch,topk,hit_splits,fetch_blocks", [
     (1, 256, 4, 64),      # 8 hit workgroups wanted, but only 4 tiles of 64
     (4, 2048, 8, 64),     # at most 8 per request; at least 64 fetch workgroups

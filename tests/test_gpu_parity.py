@@ -255,7 +255,11 @@ def test_topk_3000_slots_6000_every_unit(mode):
     dict(batch=3, layers=1, context=5000, slots=700, topk=300, fresh_rate=0.3),
     dict(batch=2, layers=3, context=3000, slots=1100, topk=1025, fresh_rate=0.2),
     dict(batch=3, layers=2, context=20000, slots=6000, topk=3000, fresh_rate=0.4),
-], ids=["k300", "k1025_l3", "k3000"])
+    # more tiles than 256 workgroups: shares of 3 and 2 tiles cross request
+    # boundaries (17 x 32 tiles on 182 workgroups; 9 x 33 on 149, a 52-token last tile)
+    dict(batch=17, layers=1, context=6000, slots=2100, topk=2048, fresh_rate=0.3),
+    dict(batch=9, layers=1, context=5000, slots=2200, topk=2100, fresh_rate=0.25),
+], ids=["k300", "k1025_l3", "k3000", "b17_k2048", "b9_k2100"])
 def test_separate_attention_every_unit(shape, mode):
     # gather, attention over the complete compute buffer and merge as separate
     # launches: the same results as the assembling launch, checked the same way

@@ -31,10 +31,6 @@ constexpr int kAttnWorkgroupsPerRound = 256;
 // serial passes), and up to 8 hit workgroups per request, 128 in all.
 constexpr int kAssembleFetchMin = 64, kAssembleFetchMax = 128;
 constexpr int kAssembleHitBlocks = 128, kAssembleHitMaxPerReq = 8;
-// A workgroup's start-up (its first two tiles arriving during the all-CU
-// burst), in tile-times: fitted to measured split sweeps at 4, 32, 64 and 192
-// requests x 2048 selected tokens.
-constexpr int kAttnStartupTiles = 4;
 
 int make_layout(const kvs_config* c, Layout* lay) {
   if (c == nullptr || lay == nullptr) return KVS_EINVAL;
@@ -81,31 +77,39 @@ int make_layout(const kvs_config* c, Layout* lay) {
       return KVS_EINVAL;
     }
     parts = splits + fetch_per_req;
-  } else if (splits == 0) {
-    // An attention workgroup holds one CU (its LDS tile), so a launch runs in
-    // rounds of 256 workgroups, and every workgroup first waits for its first
-    // two tiles.  Pick the split count with the fewest tile-times, rounds x
-    // (tiles per split + that start-up); ties go to fewer splits (less to
-    // merge; one split needs no merge at all).
-    long long best = -1;
-    const int max_s = ntiles < 64 ? ntiles : 64;
-    for (int sp = 1; sp <= max_s; ++sp) {
-      const long long rounds = ((long long)B * sp + kAttnWorkgroupsPerRound - 1) /
-                               kAttnWorkgroupsPerRound;
-      const long long cost = rounds * ((ntiles + sp - 1) / sp + kAttnStartupTiles);
-      if (best < 0 || cost < best) {
-        best = cost;
-        splits = sp;
-      }
-    }
   } else if (splits > ntiles) {
     return KVS_EINVAL;
   }
+  int attn_wgs = 0;
   if (separate) {
+    // The attention's workgroups share the B * ntiles tiles evenly, request
+    // after request (a workgroup's share may span requests).  An attention
+    // workgroup holds one CU (its LDS tile), so at most 256 run at once, and
+    // every workgroup first waits for its first two tiles: one round of the
+    // fewest workgroups that reach the smallest share, ceil(G / 256) tiles.
+    // With attn_splits = s the share of each request is s workgroups.
+    const uint64_t G = B * (uint64_t)ntiles;
+    uint64_t W;
+    if (splits > 0) {
+      W = B * (uint64_t)splits;
+    } else {
+      const uint64_t per = (G + kAttnWorkgroupsPerRound - 1) / kAttnWorkgroupsPerRound;
+      W = (G + per - 1) / per;
+    }
+    if (W > 0x7fffffffu) return KVS_EINVAL;
+    attn_wgs = (int)W;
+    // partials per request: the most workgroups whose shares one request spans
+    auto share_of = [&](uint64_t g) { return ((g + 1) * W - 1) / G; };
+    parts = 1;
+    for (uint64_t b = 0; b < B; ++b) {
+      const int n = (int)(share_of((b + 1) * ntiles - 1) - share_of(b * ntiles) + 1);
+      if (n > parts) parts = n;
+    }
+    if (parts > 256) return KVS_EINVAL;   // the merge takes at most 256 partials per request
+    splits = parts;
     // 256 fetch workgroups (1 per CU) keep the host link saturated; more only
     // add outstanding PCIe reads, which slow the HBM traffic beside them
     fetch_blocks = c->fetch_blocks == 0 ? 256 : c->fetch_blocks;
-    parts = splits;
   }
 
   lay->B = c->batch;
@@ -118,6 +122,7 @@ int make_layout(const kvs_config* c, Layout* lay) {
   lay->N = c->context;
   lay->splits = splits;
   lay->parts = parts;
+  lay->attn_wgs = attn_wgs;
   lay->fetch_blocks = fetch_blocks;
   lay->fetch_per_req = fetch_per_req;
   lay->hit_blocks = c->hit_blocks;

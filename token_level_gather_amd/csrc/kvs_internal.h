@@ -21,6 +21,7 @@ struct Layout {
   int32_t splits;        // attention token splits per request: the hit splits of the
                          // assembling launch, or the splits of the separate attention
   int32_t parts;         // attention partials per request merged by the combine
+  int32_t attn_wgs;      // separate attention: workgroups sharing the B * ceil(K/64) tiles
   int32_t fetch_blocks;  // miss-fetch workgroups of the gather launch
   int32_t fetch_per_req; // assembling launch: fetch workgroups per request
   int32_t hit_blocks;    // hit-copy workgroups of the gather launch (0 = one per 32 positions)

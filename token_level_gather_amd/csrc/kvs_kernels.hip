@@ -843,12 +843,14 @@ struct AttnArgs {
   const int32_t* slot_of;   // [B][K]: -2 marks an empty entry of a padded Top-K
   const int32_t* row_slot;  // [B][K]: slot of position i's row, -1 empty
   const int32_t* counts;    // [B][4]
-  float* part_o;            // [B][splits][16][512]
-  float* part_ml;           // [B][splits][16][2]
-  int K, splits, S, L, layer;
+  float* part_o;            // [B][parts][16][512]
+  float* part_ml;           // [B][parts][16][2]
+  int K, B, S, L, layer;
+  int wgs;                  // workgroups sharing the B * ceil(K/64) tiles
+  int parts;                // partials per request (the most workgroups one request spans)
   int padded;               // 1: mask the empty entries of a padded Top-K
   float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units
-  uint16_t* out;            // [B][16][512] bf16 when splits == 1 (no combine), else null
+  uint16_t* out;            // [B][16][512] bf16 when parts == 1 (no combine), else null
   float* lse;               // [B][16] or null; written here only when out is
   int32_t* status;          // checked build: bounds failures
 };
@@ -970,10 +972,20 @@ __device__ __forceinline__ void attend_tile(unsigned char* kv, float* sc, uint16
   __syncthreads();
 }
 
-// One workgroup = (split sp, request b): the tiles [tb, te) of request b's
-// gathered rows, each through attend_tile.
+// Workgroup w of `wgs` takes the tiles [w*G/wgs, (w+1)*G/wgs) of the G =
+// B * ntiles tiles of every request's gathered rows in request-major order
+// (an even share whatever B is: at 192 requests, 24 tiles each on 256
+// workgroups instead of 32 on 192).  Its share is one or more segments, each
+// the tiles [tb, te) of one request, through attend_tile; each segment writes
+// one partial, the segment's index among the workgroups that share its
+// request (part_slot).  With one partial per request (every request in one
+// workgroup) the workgroup writes out and lse itself and no merge runs.
 // DIRECT: rows read in place from the hot buffer at row_slot (a separate
 // instantiation, so the assembled-buffer path carries no slot loads at all).
+__device__ __forceinline__ int share_of(long long g, long long G, int wgs) {
+  return (int)(((g + 1) * wgs - 1) / G);   // the workgroup whose share holds tile g
+}
+
 template <bool DIRECT>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char kv[kTile * kLdsRow];
@@ -981,170 +993,180 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t pb[kHeads * kPRow];
   __shared__ float alpha_s[kHeads];
   __shared__ __attribute__((aligned(16))) int vmark[kTile];   // the tile's empty-entry marks
+  __shared__ float inv_l[kHeads];
 
-  const int b = blockIdx.y, sp = blockIdx.x;
-  // invalid input, or no entry at all (padded): zero output, lse -inf (written
-  // here with a single split, by the combine otherwise)
-  if (a.counts[4 * b + 3] == 0 || a.counts[4 * b + 0] + a.counts[4 * b + 1] == 0) {
-    if (a.out != nullptr) {
-      u32x4* ob = reinterpret_cast<u32x4*>(a.out + (long long)b * kHeads * kVDim);
-      for (int i = threadIdx.x; i < kHeads * kVDim / 8; i += kAttnThreads)
-        ob[i] = u32x4{0u, 0u, 0u, 0u};
-      if (a.lse != nullptr && threadIdx.x < kHeads) a.lse[b * kHeads + threadIdx.x] = -INFINITY;
-    }
-    return;
-  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int kh = wave >> 2;
   const int K = a.K;
   const int ntiles = (K + kTile - 1) / kTile;
-  const int tb = (int)((long long)sp * ntiles / a.splits);
-  const int te = (int)((long long)(sp + 1) * ntiles / a.splits);
-
-  bf16x8 qf[kKHalf];
-  float m_run = -INFINITY, l_run = 0.f;   // per head, replicated over its 16 softmax threads
-  f32x4 acc[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // two register buffers: the rows of the next two tiles are in flight while a
-  // tile is consumed from LDS
-  u32x4 ra[kAttnItems], rb[kAttnItems];
-  int va, vb;   // empty-entry mark of this thread's tile row, stored to LDS with the rows
-  // 8 threads per row: thread (row tid / 8, sub tid % 8) moves chunks sub + 8j.
-  // The rows are read through a buffer resource that spans this request's K
-  // rows: the hardware range check returns zeros for rows >= K and for the
-  // out-of-range offset given for tiles past te.  So every load is issued
-  // unconditionally, every path through the loop has the same number of loads
-  // in flight, and the wait before a tile's LDS store covers only that tile's
-  // own loads (a branch per load would make the count path-dependent and the
-  // compiler would then drain everything before each use).
+  const long long G = (long long)a.B * ntiles;
+  const int w = blockIdx.x;
+  const long long g0 = (long long)w * G / a.wgs, g1 = (long long)(w + 1) * G / a.wgs;
   const int lrow = tid >> 3, lsub = tid & 7;
-  // Rows: request b's K assembled rows in position order, or (direct) the
-  // rows of unit (b, layer)'s hot buffer, indexed by row_slot.
-  const uint16_t* base = DIRECT ? a.hot + ((long long)b * a.L + a.layer) * a.S * kRowElems
-                                  : a.cbuf + (long long)b * K * kRowElems;
-  const int rec_bytes = (DIRECT ? a.S : K) * kRowBytes;
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rec_bytes, kBufRsrcWord3);
-  // row_slot of this thread's tile row, loaded one tile ahead of the rows
-  // (DIRECT instantiation only)
-  const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.row_slot + (long long)b * K), (short)0, DIRECT ? K * 4 : 0, kBufRsrcWord3);
-  // The entry of each tile row that marks an empty position (slot_of -2, or
-  // row_slot -1 when DIRECT) travels with the row and is stored beside it.
-  // Without padding the resource is empty: the loads return 0 (valid) and
-  // read nothing.
-  const __amdgpu_buffer_rsrc_t vsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((DIRECT ? a.row_slot : a.slot_of) + (long long)b * K), (short)0,
-      a.padded ? K * 4 : 0, kBufRsrcWord3);
+  const int lsw = lds_swz(lrow);
   const int pad_mark = DIRECT ? -1 : -2;
   // softmax: threads 0..255, 16 lanes per head (one DPP row)
   const bool sm_on = tid < kHeads * 16;
-  auto load_slot = [&](int tile) -> int {
-    if (!DIRECT) return 0;
-    return __builtin_amdgcn_raw_buffer_load_b32(
-        ssrc, tile < te ? (tile * kTile + lrow) * 4 : K * 4, 0, 0);
-  };
-  auto load_tile = [&](u32x4 (&dst)[kAttnItems], int& dv, int tile, int slot) {
-    const int tok = tile * kTile + lrow;
-    const bool in = tile < te && tok < K;
-    const bool ok = !DIRECT || !in || in_range(slot, -1, a.S, a.status, KVS_SITE_ROW_SLOT);
-    const int off = !in || !ok ? rec_bytes
-                    : DIRECT   ? (slot >= 0 ? slot * kRowBytes + lsub * 16 : rec_bytes)
-                               : tok * kRowBytes + lsub * 16;
-#pragma unroll
-    for (int j = 0; j < kAttnItems; ++j)
-      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + j * 128, 0, kNT);
-    dv = __builtin_amdgcn_raw_buffer_load_b32(vsrc, tile < te ? (tile * kTile + lrow) * 4 : K * 4,
-                                              0, 0);
-  };
-  const int lsw = lds_swz(lrow);
-  auto store_tile = [&](const u32x4 (&src)[kAttnItems], int mark) {
-    unsigned char* d = kv + lrow * kLdsRow + ((lsub ^ lsw) * 16);
-#pragma unroll
-    for (int j = 0; j < kAttnItems; ++j) *reinterpret_cast<u32x4*>(d + j * 128) = src[j];
-    if (lsub == 0) vmark[lrow] = mark;
-  };
 
-  // one tile from LDS: scores, online softmax, P.V; ends with a barrier after
-  // which the LDS tile may be overwritten
-  auto compute = [&](int tile) {
-    attend_tile(kv, sc, pb, alpha_s, vmark, qf, m_run, l_run, acc, K - tile * kTile, pad_mark,
-                a.scale_log2);
-  };
+  for (long long gs = g0; gs < g1;) {
+    const int b = (int)(gs / ntiles);
+    const int tb = (int)(gs - (long long)b * ntiles);
+    const int te = (int)min((long long)ntiles, g1 - (long long)b * ntiles);
+    const int part_slot = w - share_of((long long)b * ntiles, G, a.wgs);
+    gs = (long long)(b + 1) * ntiles;
+    // invalid input, or no entry at all (padded): zero output, lse -inf
+    // (written here with one partial per request, by the combine otherwise)
+    if (a.counts[4 * b + 3] == 0 || a.counts[4 * b + 0] + a.counts[4 * b + 1] == 0) {
+      if (a.out != nullptr) {
+        u32x4* ob = reinterpret_cast<u32x4*>(a.out + (long long)b * kHeads * kVDim);
+        for (int i = tid; i < kHeads * kVDim / 8; i += kAttnThreads) ob[i] = u32x4{0u, 0u, 0u, 0u};
+        if (a.lse != nullptr && tid < kHeads) a.lse[b * kHeads + tid] = -INFINITY;
+      }
+      continue;
+    }
 
-  // tiles two at a time so the register buffers alternate without copies:
-  // at the top of each iteration LDS holds `tile` and rb holds tile + 1
-  if (tb < te) {
-    // Q as A-operand fragments: head r16, dims (kh*9 + ks)*32 + g*8 .. +7
-    const u32x4* qh =
-        reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
+    bf16x8 qf[kKHalf];
+    float m_run = -INFINITY, l_run = 0.f;   // per head, replicated over its 16 softmax threads
+    f32x4 acc[4];
 #pragma unroll
-    for (int ks = 0; ks < kKHalf; ++ks) qf[ks] = as_bf16x8(qh[(kh * kKHalf + ks) * 4 + g]);
-    // every slot load is issued before the rows of the tile ahead of it, in
-    // the prologue as in the loop, so the wait for a slot never covers rows
-    int sa = load_slot(tb), sb = load_slot(tb + 1);
-    load_tile(ra, va, tb, sa);
-    sa = load_slot(tb + 2);
-    load_tile(rb, vb, tb + 1, sb);
-    store_tile(ra, va);
-    __syncthreads();
-    // full pairs; one exit, so the loads in flight are the same (rb's) on the
-    // back edge and at the exit.  The last pair's ra load and store are of the
-    // tile past te: the range check makes them zeros that nothing reads.
-    int tile = tb;
-    for (; tile + 1 < te; tile += 2) {
-      sb = load_slot(tile + 3);
-      load_tile(ra, va, tile + 2, sa);
-      compute(tile);
-      store_tile(rb, vb);
-      __syncthreads();
-      sa = load_slot(tile + 4);
-      load_tile(rb, vb, tile + 3, sb);
-      compute(tile + 1);
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // two register buffers: the rows of the next two tiles are in flight while
+    // a tile is consumed from LDS
+    u32x4 ra[kAttnItems], rb[kAttnItems];
+    int va, vb;   // empty-entry mark of this thread's tile row, stored to LDS with the rows
+    // 8 threads per row: thread (row tid / 8, sub tid % 8) moves chunks sub + 8j.
+    // The rows are read through a buffer resource that spans this request's K
+    // rows: the hardware range check returns zeros for rows >= K and for the
+    // out-of-range offset given for tiles past te.  So every load is issued
+    // unconditionally, every path through the loop has the same number of
+    // loads in flight, and the wait before a tile's LDS store covers only that
+    // tile's own loads (a branch per load would make the count path-dependent
+    // and the compiler would then drain everything before each use).
+    // Rows: request b's K assembled rows in position order, or (direct) the
+    // rows of unit (b, layer)'s hot buffer, indexed by row_slot.
+    const uint16_t* base = DIRECT ? a.hot + ((long long)b * a.L + a.layer) * a.S * kRowElems
+                                    : a.cbuf + (long long)b * K * kRowElems;
+    const int rec_bytes = (DIRECT ? a.S : K) * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rec_bytes, kBufRsrcWord3);
+    // row_slot of this thread's tile row, loaded one tile ahead of the rows
+    // (DIRECT instantiation only)
+    const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.row_slot + (long long)b * K), (short)0, DIRECT ? K * 4 : 0, kBufRsrcWord3);
+    // The entry of each tile row that marks an empty position (slot_of -2, or
+    // row_slot -1 when DIRECT) travels with the row and is stored beside it.
+    // Without padding the resource is empty: the loads return 0 (valid) and
+    // read nothing.
+    const __amdgpu_buffer_rsrc_t vsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((DIRECT ? a.row_slot : a.slot_of) + (long long)b * K), (short)0,
+        a.padded ? K * 4 : 0, kBufRsrcWord3);
+    auto load_slot = [&](int tile) -> int {
+      if (!DIRECT) return 0;
+      return __builtin_amdgcn_raw_buffer_load_b32(
+          ssrc, tile < te ? (tile * kTile + lrow) * 4 : K * 4, 0, 0);
+    };
+    auto load_tile = [&](u32x4 (&dst)[kAttnItems], int& dv, int tile, int slot) {
+      const int tok = tile * kTile + lrow;
+      const bool in = tile < te && tok < K;
+      const bool ok = !DIRECT || !in || in_range(slot, -1, a.S, a.status, KVS_SITE_ROW_SLOT);
+      const int off = !in || !ok ? rec_bytes
+                      : DIRECT   ? (slot >= 0 ? slot * kRowBytes + lsub * 16 : rec_bytes)
+                                 : tok * kRowBytes + lsub * 16;
+#pragma unroll
+      for (int j = 0; j < kAttnItems; ++j)
+        dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + j * 128, 0, kNT);
+      dv = __builtin_amdgcn_raw_buffer_load_b32(vsrc,
+                                                tile < te ? (tile * kTile + lrow) * 4 : K * 4, 0,
+                                                0);
+    };
+    auto store_tile = [&](const u32x4 (&src)[kAttnItems], int mark) {
+      unsigned char* d = kv + lrow * kLdsRow + ((lsub ^ lsw) * 16);
+#pragma unroll
+      for (int j = 0; j < kAttnItems; ++j) *reinterpret_cast<u32x4*>(d + j * 128) = src[j];
+      if (lsub == 0) vmark[lrow] = mark;
+    };
+
+    // one tile from LDS: scores, online softmax, P.V; ends with a barrier
+    // after which the LDS tile may be overwritten
+    auto compute = [&](int tile) {
+      attend_tile(kv, sc, pb, alpha_s, vmark, qf, m_run, l_run, acc, K - tile * kTile, pad_mark,
+                  a.scale_log2);
+    };
+
+    // tiles two at a time so the register buffers alternate without copies:
+    // at the top of each iteration LDS holds `tile` and rb holds tile + 1
+    {
+      // Q as A-operand fragments: head r16, dims (kh*9 + ks)*32 + g*8 .. +7
+      const u32x4* qh =
+          reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
+#pragma unroll
+      for (int ks = 0; ks < kKHalf; ++ks) qf[ks] = as_bf16x8(qh[(kh * kKHalf + ks) * 4 + g]);
+      // every slot load is issued before the rows of the tile ahead of it, in
+      // the prologue as in the loop, so the wait for a slot never covers rows
+      int sa = load_slot(tb), sb = load_slot(tb + 1);
+      load_tile(ra, va, tb, sa);
+      sa = load_slot(tb + 2);
+      load_tile(rb, vb, tb + 1, sb);
       store_tile(ra, va);
       __syncthreads();
+      // full pairs; one exit, so the loads in flight are the same (rb's) on
+      // the back edge and at the exit.  The last pair's ra load and store are
+      // of the tile past te: the range check makes them zeros that nothing
+      // reads.
+      int tile = tb;
+      for (; tile + 1 < te; tile += 2) {
+        sb = load_slot(tile + 3);
+        load_tile(ra, va, tile + 2, sa);
+        compute(tile);
+        store_tile(rb, vb);
+        __syncthreads();
+        sa = load_slot(tile + 4);
+        load_tile(rb, vb, tile + 3, sb);
+        compute(tile + 1);
+        store_tile(ra, va);
+        __syncthreads();
+      }
+      if (tile < te) compute(tile);   // odd tile count: LDS holds the last tile
     }
-    if (tile < te) compute(tile);   // odd tile count: LDS holds the last tile
-  }
 
-  // acc lane holds O[h = 4g + j][e = 64w + 16nt + r16]
-  if (a.out != nullptr) {
-    // single split: this workgroup saw every token, so it finishes the request
-    // with the combine's arithmetic (weight 2^(m - m) = 1): out = O / l,
-    // lse = (m + log2 l) ln 2
-    __shared__ float inv_l[kHeads];
-    if (sm_on && (tid & 15) == 0) {
-      const int h = tid >> 4;
-      inv_l[h] = 1.f / l_run;
-      if (a.lse != nullptr) a.lse[b * kHeads + h] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    // acc lane holds O[h = 4g + j][e = 64w + 16nt + r16]
+    if (a.out != nullptr) {
+      // one partial per request: this workgroup saw every token, so it
+      // finishes the request with the combine's arithmetic (weight
+      // 2^(m - m) = 1): out = O / l, lse = (m + log2 l) ln 2
+      if (sm_on && (tid & 15) == 0) {
+        const int h = tid >> 4;
+        inv_l[h] = 1.f / l_run;
+        if (a.lse != nullptr)
+          a.lse[b * kHeads + h] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+      }
+      __syncthreads();
+      uint16_t* ob = a.out + (long long)b * kHeads * kVDim;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ob[(4 * g + j) * kVDim + wave * 64 + nt * 16 + r16] =
+              f32_to_bf16_rne((0.f + acc[nt][j]) * inv_l[4 * g + j]);   // 0 + x: the
+                                                                        // combine's zero sign
+      continue;
     }
-    __syncthreads();
-    uint16_t* ob = a.out + (long long)b * kHeads * kVDim;
+    // partial of this segment for the combine
+    const long long part = (long long)b * a.parts + part_slot;
+    float* po = a.part_o + part * kHeads * kVDim;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        ob[(4 * g + j) * kVDim + wave * 64 + nt * 16 + r16] =
-            f32_to_bf16_rne((0.f + acc[nt][j]) * inv_l[4 * g + j]);   // 0 + x: the
-                                                                      // combine's zero sign
-    return;
+        po[(4 * g + j) * kVDim + wave * 64 + nt * 16 + r16] = acc[nt][j];
+    if (sm_on && (tid & 15) == 0) {
+      const int h = tid >> 4;
+      a.part_ml[(part * kHeads + h) * 2 + 0] = m_run;
+      a.part_ml[(part * kHeads + h) * 2 + 1] = l_run;
+    }
   }
-  // partials for the combine
-  const long long part = (long long)b * a.splits + sp;
-  float* po = a.part_o + part * kHeads * kVDim;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) po[(4 * g + j) * kVDim + wave * 64 + nt * 16 + r16] = acc[nt][j];
-  if (sm_on && (tid & 15) == 0) {
-    const int h = tid >> 4;
-    a.part_ml[(part * kHeads + h) * 2 + 0] = m_run;
-    a.part_ml[(part * kHeads + h) * 2 + 1] = l_run;
-  }
-
 }
 
 // ------------------------------------------------------------------ assemble + attend
@@ -1398,14 +1420,24 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
 // out = sum_s 2^(m_s - M) O_s / L, L = sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2.
 // A partial that saw no row has m_s = -inf and weight 0.  One workgroup of
 // 128 threads per (h, b), 4 outputs per thread.
+// stride = partial slots per request; with a work split over `wgs`
+// workgroups (wgs > 0) request b has the partials of the workgroups its tiles
+// span, the first ones of its slots.
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const int32_t* __restrict__ counts,
                                                       uint16_t* __restrict__ out,
-                                                      float* __restrict__ lse, int splits) {
+                                                      float* __restrict__ lse, int stride,
+                                                      int wgs, int ntiles) {
   __shared__ float w[kMaxParts];
   __shared__ float inv_l;
   const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+  int splits = stride;
+  if (wgs > 0) {
+    const long long G = (long long)gridDim.y * ntiles;
+    splits = share_of((long long)(b + 1) * ntiles - 1, G, wgs) -
+             share_of((long long)b * ntiles, G, wgs) + 1;
+  }
   uint2* ob = reinterpret_cast<uint2*>(out + ((long long)b * kHeads + h) * kVDim);
   // invalid Top-K, or no entry at all (padded): zero output, lse = -inf
   if (counts[4 * b + 3] == 0 || counts[4 * b + 0] + counts[4 * b + 1] == 0) {
@@ -1413,7 +1445,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     if (lse != nullptr && tid == 0) lse[b * kHeads + h] = -INFINITY;
     return;
   }
-  const float* ml = part_ml + (long long)b * splits * kHeads * 2;
+  const float* ml = part_ml + (long long)b * stride * kHeads * 2;
   if (tid < 64) {   // one wave: max and weighted sum over the splits
     float m = -INFINITY;
     for (int s = tid; s < splits; s += 64) m = fmaxf(m, ml[(s * kHeads + h) * 2]);
@@ -1433,7 +1465,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     }
   }
   __syncthreads();
-  const float* pob = part_o + (long long)b * splits * kHeads * kVDim + h * kVDim + tid * 4;
+  const float* pob = part_o + (long long)b * stride * kHeads * kVDim + h * kVDim + tid * 4;
   float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
   for (int s = 0; s < splits; ++s) {
     const float ws = w[s];
@@ -1727,20 +1759,22 @@ hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, cons
   a.part_o = d.part_o;
   a.part_ml = d.part_ml;
   a.K = lay.K;
-  a.splits = lay.splits;
+  a.B = lay.B;
   a.S = lay.S;
   a.L = lay.L;
   a.layer = layer;
+  a.wgs = lay.attn_wgs;
+  a.parts = lay.parts;
   a.padded = (lay.flags & KVS_FLAG_PADDED_TOPK) != 0;
-  a.out = lay.splits == 1 ? out : nullptr;
-  a.lse = lay.splits == 1 ? lse : nullptr;
+  a.out = lay.parts == 1 ? out : nullptr;
+  a.lse = lay.parts == 1 ? lse : nullptr;
   a.status = d.status;
   const bool direct = (lay.flags & KVS_FLAG_DIRECT_HOT) != 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   if (direct)
-    hipLaunchKernelGGL(attention_kernel<true>, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
+    hipLaunchKernelGGL(attention_kernel<true>, dim3(lay.attn_wgs), dim3(kAttnThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(attention_kernel<false>, dim3(lay.splits, lay.B), dim3(kAttnThreads), 0, s, a);
+    hipLaunchKernelGGL(attention_kernel<false>, dim3(lay.attn_wgs), dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1805,8 +1839,11 @@ hipError_t launch_host_read_probe(const void* src, long long chunks, uint32_t* s
 
 hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, float* lse,
                           hipStream_t s) {
+  // the separate attention's work split: its partials per request vary
+  const bool split = (lay.flags & KVS_FLAG_SEPARATE_ATTENTION) != 0;
   hipLaunchKernelGGL(combine_kernel, dim3(kHeads, lay.B), dim3(128), 0, s, d.part_o, d.part_ml,
-                     d.counts, out, lse, lay.parts);
+                     d.counts, out, lse, lay.parts, split ? lay.attn_wgs : 0,
+                     (lay.K + kTile - 1) / kTile);
   return hipGetLastError();
 }
 
