@@ -1423,6 +1423,12 @@ __global__ __launch_bounds__(kAttnThreads) void assemble_kernel(AssembleArgs a) 
 // stride = partial slots per request; with a work split over `wgs`
 // workgroups (wgs > 0) request b has the partials of the workgroups its tiles
 // span, the first ones of its slots.
+// R > 0 (R >= every request's partial count, R <= 64): the request's counts,
+// the partials' (max, sum) pairs (one per lane of the first wave) and this
+// thread's four outputs of every partial are all loaded before any is used,
+// one memory round trip; R == 0: any count, the pairs and then the outputs.
+// The sums run in partial order either way.
+template <int R>
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const int32_t* __restrict__ counts,
@@ -1430,7 +1436,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
                                                       float* __restrict__ lse, int stride,
                                                       int wgs, int ntiles) {
   __shared__ float w[kMaxParts];
-  __shared__ float inv_l;
+  __shared__ float inv_l, lse_h;
   const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   int splits = stride;
   if (wgs > 0) {
@@ -1438,47 +1444,89 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     splits = share_of((long long)(b + 1) * ntiles - 1, G, wgs) -
              share_of((long long)b * ntiles, G, wgs) + 1;
   }
-  uint2* ob = reinterpret_cast<uint2*>(out + ((long long)b * kHeads + h) * kVDim);
-  // invalid Top-K, or no entry at all (padded): zero output, lse = -inf
-  if (counts[4 * b + 3] == 0 || counts[4 * b + 0] + counts[4 * b + 1] == 0) {
-    ob[tid] = make_uint2(0u, 0u);
-    if (lse != nullptr && tid == 0) lse[b * kHeads + h] = -INFINITY;
-    return;
-  }
   const float* ml = part_ml + (long long)b * stride * kHeads * 2;
-  if (tid < 64) {   // one wave: max and weighted sum over the splits
+  const float* pob = part_o + (long long)b * stride * kHeads * kVDim + h * kVDim + tid * 4;
+  // the counts through a buffer (vector-memory) load issued with the others:
+  // as a scalar load the compiler waits for it before issuing them
+  const u32x4 cnt = __builtin_amdgcn_raw_buffer_load_b128(
+      __builtin_amdgcn_make_buffer_rsrc((void*)(counts + 4 * b), (short)0, 16, kBufRsrcWord3), 0,
+      0, 0);
+  float2 pair = make_float2(-INFINITY, 0.f);   // (max, sum) of partial tid (R > 0)
+  float4 x[R > 0 ? R : 1];
+  if constexpr (R > 0) {
+    // unconditional loads at clamped indices (a partial past the request's
+    // count repeats the last one and is never used)
+    pair = *reinterpret_cast<const float2*>(ml + (min(tid, splits - 1) * kHeads + h) * 2);
+#pragma unroll
+    for (int s = 0; s < R; ++s)
+      x[s] = *reinterpret_cast<const float4*>(pob + (long long)min(s, splits - 1) * kHeads * kVDim);
+  }
+  uint2* ob = reinterpret_cast<uint2*>(out + ((long long)b * kHeads + h) * kVDim);
+  // An invalid Top-K, or no entry at all (padded), gives a zero output and
+  // lse = -inf.  The merge below runs either way (on partials nobody wrote,
+  // whose result is then discarded) and the counts are looked at only at the
+  // end: otherwise the compiler issues the loads above after they arrive.
+  if (tid < 64) {   // one wave: max and weighted sum over the partials
     float m = -INFINITY;
-    for (int s = tid; s < splits; s += 64) m = fmaxf(m, ml[(s * kHeads + h) * 2]);
+    if constexpr (R > 0) {
+      if (tid < splits) m = pair.x;
+    } else {
+      for (int s = tid; s < splits; s += 64) m = fmaxf(m, ml[(s * kHeads + h) * 2]);
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     float l = 0.f;
-    for (int s = tid; s < splits; s += 64) {
-      const float ws = exp2f(ml[(s * kHeads + h) * 2] - m);
-      w[s] = ws;
-      l += ws * ml[(s * kHeads + h) * 2 + 1];
+    if constexpr (R > 0) {
+      if (tid < splits) {
+        const float ws = exp2f(pair.x - m);
+        w[tid] = ws;
+        l = ws * pair.y;
+      }
+    } else {
+      for (int s = tid; s < splits; s += 64) {
+        const float ws = exp2f(ml[(s * kHeads + h) * 2] - m);
+        w[s] = ws;
+        l += ws * ml[(s * kHeads + h) * 2 + 1];
+      }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
     if (tid == 0) {
       inv_l = 1.f / l;
-      if (lse != nullptr) lse[b * kHeads + h] = (m + log2f(l)) * 0.69314718055994531f;
+      lse_h = (m + log2f(l)) * 0.69314718055994531f;
     }
   }
   __syncthreads();
-  const float* pob = part_o + (long long)b * stride * kHeads * kVDim + h * kVDim + tid * 4;
   float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float ws = w[s];
-    const float4 x = *reinterpret_cast<const float4*>(pob + (long long)s * kHeads * kVDim);
-    o0 += ws * x.x;
-    o1 += ws * x.y;
-    o2 += ws * x.z;
-    o3 += ws * x.w;
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+      if (s < splits) {
+        const float ws = w[s];
+        o0 += ws * x[s].x;
+        o1 += ws * x[s].y;
+        o2 += ws * x[s].z;
+        o3 += ws * x[s].w;
+      }
+    }
+  } else {
+    for (int s = 0; s < splits; ++s) {
+      const float ws = w[s];
+      const float4 y = *reinterpret_cast<const float4*>(pob + (long long)s * kHeads * kVDim);
+      o0 += ws * y.x;
+      o1 += ws * y.y;
+      o2 += ws * y.z;
+      o3 += ws * y.w;
+    }
   }
   const float il = inv_l;
-  ob[tid] = make_uint2(
-      (uint32_t)f32_to_bf16_rne(o0 * il) | ((uint32_t)f32_to_bf16_rne(o1 * il) << 16),
-      (uint32_t)f32_to_bf16_rne(o2 * il) | ((uint32_t)f32_to_bf16_rne(o3 * il) << 16));
+  const bool empty = cnt[3] == 0 || cnt[0] + cnt[1] == 0;
+  if (lse != nullptr && tid == 0) lse[b * kHeads + h] = empty ? -INFINITY : lse_h;
+  ob[tid] = empty ? make_uint2(0u, 0u)
+                  : make_uint2((uint32_t)f32_to_bf16_rne(o0 * il) |
+                                   ((uint32_t)f32_to_bf16_rne(o1 * il) << 16),
+                               (uint32_t)f32_to_bf16_rne(o2 * il) |
+                                   ((uint32_t)f32_to_bf16_rne(o3 * il) << 16));
 }
 
 // ------------------------------------------------------------------ state check
@@ -1841,9 +1889,12 @@ hipError_t launch_combine(const Layout& lay, const DevPtrs& d, uint16_t* out, fl
                           hipStream_t s) {
   // the separate attention's work split: its partials per request vary
   const bool split = (lay.flags & KVS_FLAG_SEPARATE_ATTENTION) != 0;
-  hipLaunchKernelGGL(combine_kernel, dim3(kHeads, lay.B), dim3(128), 0, s, d.part_o, d.part_ml,
-                     d.counts, out, lse, lay.parts, split ? lay.attn_wgs : 0,
-                     (lay.K + kTile - 1) / kTile);
+  // the smallest register count that holds every request's partials
+  const int P = lay.parts;
+  auto fn = P <= 4 ? combine_kernel<4> : P <= 8 ? combine_kernel<8> : P <= 16 ? combine_kernel<16>
+          : P <= 32 ? combine_kernel<32> : combine_kernel<0>;
+  hipLaunchKernelGGL(fn, dim3(kHeads, lay.B), dim3(128), 0, s, d.part_o, d.part_ml, d.counts,
+                     out, lse, lay.parts, split ? lay.attn_wgs : 0, (lay.K + kTile - 1) / kTile);
   return hipGetLastError();
 }
 
