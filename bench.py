@@ -565,29 +565,38 @@ class Workload:
                 "peak_gbs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "working_set_mb": round(working_set / 1e6, 1), "kernel": kname, "note": note}
 
-    def index_copy(self, sets):
-        """The index copy alone (the gather kernel: hits copied within HBM into
-        the compute buffer, no attention), timed like hit_copy on a second pool
-        over the same host rows whose copy and attention are separate launches.
-        It runs the same decode steps first, so its hot buffers and maps equal
-        this pool's and the same all-hit sets apply."""
+    def index_copy(self, sets, reps=6):
+        """The index copy of the hits alone (the copy kernel of the separate
+        launches, no attention), after hit_copy: its last step was all hits, so
+        kvs_probe_hit_copy copies every request's K rows.  Launched back to back,
+        cycling the layers (each reads its own hot rows at the last step's
+        slots), between two events: HIP events around each launch would add
+        about 5 us to a 30 us kernel."""
         if sets is None or self.args.separate or self.args.direct_hot:
             return None
-        kvs, wl = self.kvs, self.wl
-        t = sets[0]
-        p2 = kvs.Pool(wl.batch, wl.layers, wl.context, wl.slots, wl.topk, scale=wl.scale,
-                      flags=kvs.KVS_FLAG_SEPARATE_ATTENTION, host=self.pool.host)
-        try:
-            for s in range(t + 1):
-                for l in range(wl.layers):
-                    p2.step(l, self.topk[s, l], self.q[s, l], self.out[s, l], self.lse[s, l])
-            res = self.hit_copy(sets, pool=p2, kname="gather")
-        finally:
-            p2.release()
-        if res is not None:
-            res["note"] = ("index copy alone (gather kernel of the separate launches, pool over "
-                           "the same host rows run through the same steps); " + res["note"])
-        return res
+        torch, pool, wl = self.torch, self.pool, self.wl
+        B, L, K = wl.batch, wl.layers, wl.topk
+        pool.probe_hit_copy(0)   # warm-up launch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for l in range(L):
+                pool.probe_hit_copy(l)
+        e1.record()
+        e1.synchronize()
+        self.sync_ok()
+        avg_ms = e0.elapsed_time(e1) / (reps * L)
+        rows = B * K
+        gbs = 2 * ROW * rows / (avg_ms * 1e-3) / 1e9
+        working_set = (L * B * K + B * K) * ROW   # every layer's rows at the slots + the buffer
+        return {"rows_per_launch": rows, "bytes_per_launch": 2 * ROW * rows,
+                "avg_ms": round(avg_ms, 5), "achieved_gbs": round(gbs, 1),
+                "peak_gbs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "working_set_mb": round(working_set / 1e6, 1), "kernel": "gather (hit copy)",
+                "note": f"index copy of the hits alone (kvs_probe_hit_copy: the copy kernel of "
+                        f"the separate launches), {reps} x {L} launches back to back cycling the "
+                        f"layers, timed between two events; working set = every layer's rows at "
+                        f"the last step's slots + the compute buffer"}
 
     def parity(self, steps, reqs, rec):
         """GPU outputs of steps 0..steps-1 and final maps of the sampled requests

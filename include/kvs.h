@@ -408,6 +408,24 @@ int kvs_release(kvs_pool* pool);
 #define KVS_PROBE_SINK_WORDS 65536
 int kvs_probe_host_read(const void* host, uint64_t bytes, uint32_t* sink, void* stream);
 
+/* The hit index copy alone (the index copy of "Sparse Attention-Driven KVCache
+ * Management for Domestic AI Supernodes", abstract: rows moved by index into a
+ * contiguous compute buffer), for timing it apart from the attention it is
+ * fused with in the default step: for every request whose last step was
+ * valid, copy the rows at the hit slots of the pool's last step (its per-step
+ * lists) from layer `layer`'s hot buffer to the compute buffer, within HBM,
+ * with the copy kernel of KVS_FLAG_SEPARATE_ATTENTION steps (1152 B read and
+ * 1152 B written per hit).  Miss rows are left alone; an empty entry of a
+ * padded Top-K gets a zero row, as in a step.  Enqueued on `stream` (a stream
+ * of the pool's device), nothing else changes; the caller times it with
+ * events on that stream.  When `layer` is not the last
+ * step's layer the compute buffer then holds rows of `layer` at the last
+ * step's slots: a measurement, not a step result.  KVS_EINVAL for a NULL
+ * pool, a layer outside [0, L), a pool without compute buffer
+ * (KVS_FLAG_DIRECT_HOT), a pool that has run no step, or a stream of another
+ * device. */
+int kvs_probe_hit_copy(kvs_pool* pool, int32_t layer, void* stream);
+
 /* Static description of a return code. */
 const char* kvs_strerror(int code);
 

@@ -155,6 +155,7 @@ def test_null_pool_calls_are_rejected():
     assert lib.kvs_append(None, 0, None, None, None) == kvs.KVS_EINVAL
     assert lib.kvs_probe_host_read(None, 0, None, None) == kvs.KVS_EINVAL
     assert lib.kvs_probe_host_read(None, 16, None, None) == kvs.KVS_EINVAL
+    assert lib.kvs_probe_hit_copy(None, 0, None) == kvs.KVS_EINVAL
     assert lib.kvs_profile_begin(None, 1, 1) == kvs.KVS_EINVAL
 
 

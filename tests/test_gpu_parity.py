@@ -354,6 +354,48 @@ def test_steps_without_misses_every_unit(mode):
         h.close()
 
 
+def test_probe_hit_copy_copies_only_the_hit_rows():
+    # kvs_probe_hit_copy (measurement helper) repeats the index copy of the
+    # last step's hits: hit rows of the compute buffer equal their hot rows
+    # again, miss rows are left alone and empty entries get zero rows; it
+    # refuses a pool that has run no step and one without compute buffer
+    import token_level_gather_amd as kvs
+    torch = _torch()
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="probe", batch=3, layers=2, context=3000,
+                                                  slots=800, topk=300, steps=3, fresh_rate=0.3)
+    h = Harness(wl, wl.steps, range(wl.batch), padded=True)
+    try:
+        with pytest.raises(kvs.KvsError):
+            h.pool.probe_hit_copy(0)
+        for t in range(wl.steps):
+            for l in range(wl.layers):
+                h.check(t, l, *h.device_step(t, l))
+        l = wl.layers - 1
+        row = wl.topk * 576
+        before = _u16(h.pool.cbuf[:wl.batch * row * 2]).reshape(wl.batch, wl.topk, 576)
+        h.pool.cbuf[:wl.batch * row * 2].fill_(0x5a)
+        h.pool.probe_hit_copy(l)
+        torch.cuda.synchronize()
+        after = _u16(h.pool.cbuf[:wl.batch * row * 2]).reshape(wl.batch, wl.topk, 576)
+        for b in range(wl.batch):
+            slot_of = h.pool.read_state(b, l)["slot_of"]
+            hit = slot_of >= 0
+            assert np.array_equal(after[b][hit], before[b][hit])
+            assert np.all(after[b][slot_of == -1] == 0x5a5a)   # misses: untouched
+            assert np.all(after[b][slot_of == -2] == 0)        # empty entries: zero rows
+        with pytest.raises(kvs.KvsError):
+            h.pool.probe_hit_copy(wl.layers)
+    finally:
+        h.close()
+    d = Harness(wl, 1, [0], flags=kvs.KVS_FLAG_DIRECT_HOT)
+    try:
+        d.check(0, 0, *d.device_step(0, 0))
+        with pytest.raises(kvs.KvsError):
+            d.pool.probe_hit_copy(0)
+    finally:
+        d.close()
+
+
 def _direct():
     import token_level_gather_amd as kvs
     return kvs.KVS_FLAG_DIRECT_HOT

@@ -54,7 +54,7 @@ EXPORTS = (
     "kvs_step", "kvs_free_request", "kvs_sync_status", "kvs_debug_read_state",
     "kvs_profile_begin", "kvs_profile_end", "kvs_release", "kvs_strerror",
     "kvs_graph_capture", "kvs_graph_launch", "kvs_graph_destroy", "kvs_publish_device",
-    "kvs_append", "kvs_probe_host_read", "kvs_step_static",
+    "kvs_append", "kvs_probe_host_read", "kvs_step_static", "kvs_probe_hit_copy",
 )
 STATIC_SCRATCH_BYTES = 32 << 20
 
@@ -151,6 +151,7 @@ def load_library(path: str) -> ctypes.CDLL:
         "kvs_publish_device": [vp, i32, i32, i64, i64, vp, vp],
         "kvs_append": [vp, i32, vp, vp, vp],
         "kvs_probe_host_read": [vp, u64, vp, vp],
+        "kvs_probe_hit_copy": [vp, i32, vp],
         "kvs_step": [vp, i32, vp, vp, vp, vp, vp],
         "kvs_step_static": [vp, i32, vp, vp, vp, vp, vp],
         "kvs_free_request": [vp, i32, vp],
@@ -340,6 +341,12 @@ class Pool:
         if rc not in (KVS_OK, KVS_ERANGE, KVS_EDUP, KVS_ECORRUPT, KVS_EBOUNDS):
             raise KvsError(rc, "kvs_sync_status")
         return rc, st
+
+    def probe_hit_copy(self, layer, stream=None):
+        """kvs_probe_hit_copy (measurement helper): the index copy of the last
+        step's hits alone, reading layer ``layer``'s hot rows."""
+        _check(self._lib.kvs_probe_hit_copy(self.handle, layer, _stream_ptr(stream, self.device)),
+               "kvs_probe_hit_copy")
 
     def read_state(self, req, layer, stream=None) -> dict:
         arr = {

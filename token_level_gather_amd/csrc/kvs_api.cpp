@@ -184,6 +184,7 @@ struct kvs_pool {
   void* static_scratch;
   hipError_t static_scratch_err;
   DevPtrs last_scratch;  // device pointers of the last step (its lists for kvs_debug_read_state)
+  bool stepped;          // a step has been enqueued: last_scratch holds written lists
 };
 
 static int hip_err(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP_BASE - (int)e; }
@@ -386,6 +387,7 @@ int kvs_create_pool(const kvs_config* cfg, const kvs_buffers* bufs, void* stream
   d.status = (int32_t*)(meta + L.status);
   bind_scratch(L, scr, &d);
   p->last_scratch = d;
+  p->stepped = false;
 
   p->device = device;
   p->static_scratch = nullptr;
@@ -477,6 +479,7 @@ static int enqueue_step(kvs_pool* p, const DevPtrs& d, int32_t layer, const int3
                       [&] { return launch_combine(L, d, (uint16_t*)out, lse, s); }));
   if (p->prof_steps < p->prof_max_steps) ++p->prof_steps;
   p->last_scratch = d;
+  p->stepped = true;
   return KVS_OK;
 }
 
@@ -633,6 +636,9 @@ int kvs_graph_capture(kvs_pool* p, int32_t layer, const int32_t* topk, const voi
   // no timing events inside the graph
   const int saved_max = p->prof_max_steps;
   p->prof_max_steps = 0;
+  // a captured step runs only when the graph is launched: its lists are not
+  // written yet (kvs_probe_hit_copy keeps refusing a pool that has run no step)
+  const bool saved_stepped = p->stepped;
   hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   int rc = KVS_OK;
   hipGraph_t g = nullptr;
@@ -644,6 +650,7 @@ int kvs_graph_capture(kvs_pool* p, int32_t layer, const int32_t* topk, const voi
     rc = hip_err(e);
   }
   p->prof_max_steps = saved_max;
+  p->stepped = saved_stepped;
   hipGraphExec_t exec = nullptr;
   if (rc == KVS_OK) {
     e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
@@ -695,6 +702,14 @@ int kvs_probe_host_read(const void* host, uint64_t bytes, uint32_t* sink, void* 
     return KVS_EINVAL;
   }
   return hip_err(launch_host_read_probe(dev, (long long)(bytes / 16), sink, (hipStream_t)stream));
+}
+
+int kvs_probe_hit_copy(kvs_pool* p, int32_t layer, void* stream) {
+  if (p == nullptr || layer < 0 || layer >= p->lay.L) return KVS_EINVAL;
+  if ((p->lay.flags & KVS_FLAG_DIRECT_HOT) != 0 || !p->stepped) return KVS_EINVAL;
+  const hipStream_t s = (hipStream_t)stream;
+  KVS_TRY(check_device(p, s));
+  return hip_err(launch_hit_copy(p->lay, p->last_scratch, layer, s));
 }
 
 const char* kvs_strerror(int code) {

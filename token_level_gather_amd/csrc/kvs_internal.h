@@ -107,6 +107,9 @@ hipError_t launch_assemble(const Layout& lay, const DevPtrs& d, int layer, const
                            float scale, hipStream_t s);
 hipError_t launch_clear_status(const DevPtrs& d, hipStream_t s);
 hipError_t launch_check_state(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s);
+// Measurement helper: the gather kernel's hit role alone (no fetch
+// workgroups) over the lists in `d`, reading layer `layer`'s hot rows.
+hipError_t launch_hit_copy(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s);
 hipError_t launch_host_read_probe(const void* src, long long chunks, uint32_t* sink,
                                   hipStream_t s);
 hipError_t launch_append(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* rows,

@@ -1795,6 +1795,32 @@ hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const i
   return hipGetLastError();
 }
 
+hipError_t launch_hit_copy(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s) {
+  GatherArgs a;
+  a.pool = reinterpret_cast<const u32x4*>(d.pool);
+  a.hot = reinterpret_cast<u32x4*>(d.hot);
+  a.cbuf = reinterpret_cast<u32x4*>(d.cbuf);
+  a.topk = nullptr;   // read by the fetch role only, which has no workgroup here
+  a.slot_of = d.slot_of;
+  a.miss_pos = d.miss_pos;
+  a.victims = d.victims;
+  a.counts = d.counts;
+  a.N = lay.N;
+  a.S = lay.S;
+  a.K = lay.K;
+  a.L = lay.L;
+  a.layer = layer;
+  a.B = lay.B;
+  a.fetch_per_req = 1;
+  a.fetch_wgs = 0;
+  a.hit_wgs = (int)((long long)((lay.K + kCopyRows - 1) / kCopyRows) * lay.B);
+  a.hits_first = 0;
+  a.write_cbuf = 1;
+  a.status = d.status;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)a.hit_wgs), dim3(kCopyThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* q,
                             float scale, uint16_t* out, float* lse, hipStream_t s) {
   AttnArgs a;
