@@ -368,8 +368,10 @@ int kvs_debug_read_state(kvs_pool* pool, int32_t req, int32_t layer, void* strea
 
 /* Record HIP-event times (one event pair around every launch of a kernel
  * whose bit (1 << KVS_KERNEL_*) is set in `kernel_mask`, on the stream it runs
- * on) for the next `max_steps` kvs_step calls.  Each event pair adds a few
- * microseconds to the step, so timing runs bracket only the kernels they need. */
+ * on) for the next `max_steps` kvs_step calls.  The events are timing-only
+ * (created without a system-scope fence, so recording them writes back no
+ * cache); each pair still adds a little to the step, so timing runs bracket
+ * only the kernels they need. */
 int kvs_profile_begin(kvs_pool* pool, int32_t max_steps, uint32_t kernel_mask);
 /* Synchronise and report the recorded times; stops recording. */
 int kvs_profile_end(kvs_pool* pool, kvs_kernel_times* out);
