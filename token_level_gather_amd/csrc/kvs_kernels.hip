@@ -858,7 +858,13 @@ struct AttnArgs {
 // One 64-row tile in LDS: scores of the 16 heads against every row, the
 // online softmax update and P.V.  Rows at or past n_valid, and rows whose mark
 // equals pad_mark, score -inf.  Starts after the barrier that published the
-// tile and ends with a barrier after which the tile may be overwritten.
+// tile.  Two barriers inside: after the scores (sc complete; every wave is
+// past the previous tile's P.V) and after the softmax (pb and alpha_s
+// complete).  mid() runs in every thread between them, beside the softmax:
+// work that must follow the previous tile's P.V and be published before the
+// next tile's scores (the double-buffered attention stores the next tile
+// there).  There is no barrier at the end: the caller keeps the tile, sc, pb
+// and alpha_s unwritten until the next such barrier.
 // MFMA operand layout used (v_mfma_f32_16x16x32_bf16): lane l supplies row
 // (l % 16) of A and column (l % 16) of B with 8 consecutive k-values selected
 // by l / 16; the result lane l holds rows 4*(l/16)+j, column l % 16.  Both
@@ -873,11 +879,12 @@ struct AttnArgs {
 // State per thread: qf (Q fragments, head r16, this wave's k-half), m_run /
 // l_run (running max in log2 units and sum of its head, replicated over the
 // head's 16 softmax threads), acc (O[h = 4g + j][e = 64w + 16nt + r16]).
-__device__ __forceinline__ void attend_tile(unsigned char* kv, float* sc, uint16_t* pb,
-                                            float* alpha_s, const int* vmark,
-                                            const bf16x8 (&qf)[kKHalf], float& m_run,
-                                            float& l_run, f32x4 (&acc)[4], int n_valid,
-                                            int pad_mark, float scale_log2) {
+template <class Mid>
+__device__ __forceinline__ void attend_tile_mid(const unsigned char* kv, float* sc, uint16_t* pb,
+                                                float* alpha_s, const int* vmark,
+                                                const bf16x8 (&qf)[kKHalf], float& m_run,
+                                                float& l_run, f32x4 (&acc)[4], int n_valid,
+                                                int pad_mark, float scale_log2, Mid&& mid) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int tt = wave & 3, kh = wave >> 2;
@@ -930,6 +937,7 @@ __device__ __forceinline__ void attend_tile(unsigned char* kv, float* sc, uint16
                    (uint32_t)f32_to_bf16_rne(p[2]) | ((uint32_t)f32_to_bf16_rne(p[3]) << 16));
     if ((tid & 15) == 0) alpha_s[h] = alpha;
   }
+  mid();
   __syncthreads();
 
   // P.V: wave w owns value columns [64w, 64w + 64) as 4 MFMA column tiles
@@ -969,6 +977,18 @@ __device__ __forceinline__ void attend_tile(unsigned char* kv, float* sc, uint16
       }
     }
   }
+}
+
+// The tile routine with nothing between its barriers and a barrier at the
+// end, after which the tile, sc, pb and alpha_s may be overwritten (one LDS
+// tile: the assembling launch).
+__device__ __forceinline__ void attend_tile(unsigned char* kv, float* sc, uint16_t* pb,
+                                            float* alpha_s, const int* vmark,
+                                            const bf16x8 (&qf)[kKHalf], float& m_run,
+                                            float& l_run, f32x4 (&acc)[4], int n_valid,
+                                            int pad_mark, float scale_log2) {
+  attend_tile_mid(kv, sc, pb, alpha_s, vmark, qf, m_run, l_run, acc, n_valid, pad_mark,
+                  scale_log2, [] {});
   __syncthreads();
 }
 
@@ -988,11 +1008,12 @@ __device__ __forceinline__ int share_of(long long g, long long G, int wgs) {
 
 template <bool DIRECT>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char kv[kTile * kLdsRow];
+  // two LDS tiles (158.6 KB in all): one is attended while the next is stored
+  __shared__ __attribute__((aligned(16))) unsigned char kv[2][kTile * kLdsRow];
   __shared__ float sc[2 * kHeads * kTile];
   __shared__ __attribute__((aligned(16))) uint16_t pb[kHeads * kPRow];
   __shared__ float alpha_s[kHeads];
-  __shared__ __attribute__((aligned(16))) int vmark[kTile];   // the tile's empty-entry marks
+  __shared__ __attribute__((aligned(16))) int vmark[2][kTile];   // each tile's empty-entry marks
   __shared__ float inv_l[kHeads];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1081,23 +1102,31 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
                                                 tile < te ? (tile * kTile + lrow) * 4 : K * 4, 0,
                                                 0);
     };
-    auto store_tile = [&](const u32x4 (&src)[kAttnItems], int mark) {
-      unsigned char* d = kv + lrow * kLdsRow + ((lsub ^ lsw) * 16);
+    auto store_tile = [&](const u32x4 (&src)[kAttnItems], int mark, int buf) {
+      unsigned char* d = kv[buf] + lrow * kLdsRow + ((lsub ^ lsw) * 16);
 #pragma unroll
       for (int j = 0; j < kAttnItems; ++j) *reinterpret_cast<u32x4*>(d + j * 128) = src[j];
-      if (lsub == 0) vmark[lrow] = mark;
+      if (lsub == 0) vmark[buf][lrow] = mark;
     };
 
-    // one tile from LDS: scores, online softmax, P.V; ends with a barrier
-    // after which the LDS tile may be overwritten
-    auto compute = [&](int tile) {
-      attend_tile(kv, sc, pb, alpha_s, vmark, qf, m_run, l_run, acc, K - tile * kTile, pad_mark,
-                  a.scale_log2);
+    // tile `tile` from LDS buffer buf: scores, online softmax, P.V, with
+    // mid() between the tile routine's two barriers
+    auto compute = [&](int tile, int buf, auto&& mid) {
+      attend_tile_mid(kv[buf], sc, pb, alpha_s, vmark[buf], qf, m_run, l_run, acc,
+                      K - tile * kTile, pad_mark, a.scale_log2, mid);
     };
 
-    // tiles two at a time so the register buffers alternate without copies:
-    // at the top of each iteration LDS holds `tile` and rb holds tile + 1
+    // Tiles two at a time so the buffers alternate without copies.  At the
+    // top of each iteration LDS buffer 0 holds `tile` (published), rb holds
+    // tile + 1 and ra tile + 2 (in flight).  While a tile is attended, the
+    // register tile after it is stored to the other LDS buffer between the
+    // tile routine's barriers (every wave is past that buffer's last P.V by
+    // then, and the second barrier publishes it) and its register buffer is
+    // reloaded at once, two tiles ahead: two barriers per tile, and each load
+    // has two tiles of time before its store.
     {
+      // the previous segment's last tile may still be read by slower waves
+      __syncthreads();
       // Q as A-operand fragments: head r16, dims (kh*9 + ks)*32 + g*8 .. +7
       const u32x4* qh =
           reinterpret_cast<const u32x4*>(a.q + ((long long)b * kHeads + r16) * kRowElems);
@@ -1109,26 +1138,28 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
       load_tile(ra, va, tb, sa);
       sa = load_slot(tb + 2);
       load_tile(rb, vb, tb + 1, sb);
-      store_tile(ra, va);
+      sb = load_slot(tb + 3);
+      store_tile(ra, va, 0);
+      load_tile(ra, va, tb + 2, sa);
+      sa = load_slot(tb + 4);
       __syncthreads();
-      // full pairs; one exit, so the loads in flight are the same (rb's) on
-      // the back edge and at the exit.  The last pair's ra load and store are
-      // of the tile past te: the range check makes them zeros that nothing
-      // reads.
+      // full pairs; one exit, so the loads in flight are the same (rb's and
+      // ra's) on the back edge and at the exit.  Loads of tiles past te read
+      // the out-of-range offset: zeros that nothing attends.
       int tile = tb;
       for (; tile + 1 < te; tile += 2) {
-        sb = load_slot(tile + 3);
-        load_tile(ra, va, tile + 2, sa);
-        compute(tile);
-        store_tile(rb, vb);
-        __syncthreads();
-        sa = load_slot(tile + 4);
-        load_tile(rb, vb, tile + 3, sb);
-        compute(tile + 1);
-        store_tile(ra, va);
-        __syncthreads();
+        compute(tile, 0, [&] {
+          store_tile(rb, vb, 1);
+          load_tile(rb, vb, tile + 3, sb);
+          sb = load_slot(tile + 5);
+        });
+        compute(tile + 1, 1, [&] {
+          store_tile(ra, va, 0);
+          load_tile(ra, va, tile + 4, sa);
+          sa = load_slot(tile + 6);
+        });
       }
-      if (tile < te) compute(tile);   // odd tile count: LDS holds the last tile
+      if (tile < te) compute(tile, 0, [] {});   // odd tile count: buffer 0 holds the last tile
     }
 
     // acc lane holds O[h = 4g + j][e = 64w + 16nt + r16]
