@@ -461,7 +461,7 @@ static int enqueue_step(kvs_pool* p, const DevPtrs& d, int32_t layer, const int3
   if (L.flags & KVS_FLAG_SEPARATE_ATTENTION) {
     // index copy: misses over PCIe (fetch + write-back) and hits within HBM
     KVS_TRY_HIP(timed(p, KVS_KERNEL_GATHER, s,
-                      [&] { return launch_gather(L, d, layer, topk, s); }));
+                      [&] { return launch_gather(L, d, layer, s); }));
     // Top-K sparse attention over the compute buffer
     KVS_TRY_HIP(timed(p, KVS_KERNEL_ATTENTION, s, [&] {
       return launch_attention(L, d, layer, (const uint16_t*)q, p->cfg.scale, (uint16_t*)out,

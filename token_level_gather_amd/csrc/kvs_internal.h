@@ -94,8 +94,7 @@ hipError_t launch_init_units(const Layout& lay, const DevPtrs& d, int unit_begin
                              int unit_count, bool reset_counters, hipStream_t s);
 hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer,
                            const int32_t* topk, hipStream_t s);
-hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
-                         hipStream_t s);
+hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s);
 // With a single split the attention writes out / lse itself and no combine runs.
 hipError_t launch_attention(const Layout& lay, const DevPtrs& d, int layer, const uint16_t* q,
                             float scale, uint16_t* out, float* lse, hipStream_t s);

@@ -693,6 +693,9 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
 }
 
 // ------------------------------------------------------------------ gather
+// Host reads in flight, at one per fetch thread, below which the separate
+// gather issues all of a pass's reads at once (see its fetch role).
+constexpr long long kDeepFetchBytes = 384ll << 10;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyRows = 32;                                   // rows per block iteration
 constexpr int kCopyItems = kRowChunks / 8;                      // 9 chunks / thread
@@ -702,9 +705,9 @@ struct GatherArgs {
   const u32x4* pool;       // host pool (pinned, GPU-mapped) [B][L][N] rows
   u32x4* hot;              // [B][L][S] rows
   u32x4* cbuf;             // [B][K] rows
-  const int32_t* topk;     // [B][K]
   const int32_t* slot_of;  // [B][K]
   const int32_t* miss_pos; // [B][K]
+  const int32_t* miss_tok; // [B][K]: tokens of the misses, in Top-K order
   const int32_t* victims;  // [B][K]
   const int32_t* counts;   // [B][4]
   long long N;
@@ -714,6 +717,7 @@ struct GatherArgs {
   int hit_wgs;             // hit-role workgroups (each loops over 32-position groups)
   int hits_first;          // 0: fetch workgroups take the first grid indices; 1: hit ones do
   int write_cbuf;          // 0: rows are read in place from the hot buffer (no compute buffer)
+  int deep_fetch;          // 1: a unit's pool rows span under 4 GiB (N * 1152 bytes)
   int32_t* status;         // checked build: bounds failures
 };
 
@@ -739,29 +743,70 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
     const int n = a.counts[4 * b + 1];
     const long long u = (long long)b * a.L + a.layer;
     const long long bk = (long long)b * K;
+    // Two ways to issue a pass's host reads.  Where the workgroups that have
+    // misses hold kDeepFetchBytes or more with one read per thread, each
+    // thread keeps one read in flight, the lists of a chunk loaded just before
+    // its read: enough for the link, and more outstanding host reads
+    // measurably slow it.  Below that the link idles on round trips, so the
+    // pass's lists are loaded first and all its reads go out at once, through
+    // a buffer resource over the unit's pool rows: chunks past the misses
+    // read nothing, and no load sits under a branch (which would make the
+    // compiler's in-order wait counts path-dependent, its waits for later
+    // lists then draining the reads).  The resource needs the unit's rows
+    // below 4 GiB.  The estimate takes every request's misses as this one's.
+    const long long active =
+        (long long)a.B * min(a.fetch_per_req, (n + kCopyRows - 1) / kCopyRows);
+    const bool deep = a.deep_fetch && active * kCopyThreads * 16 < kDeepFetchBytes;
+    const __amdgpu_buffer_rsrc_t psrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.pool + u * a.N * kRowChunks), (short)0,
+        deep ? (int)(unsigned)(a.N * kRowBytes) : 0, kBufRsrcWord3);
     for (int j0 = x * kCopyRows; j0 < n; j0 += a.fetch_per_req * kCopyRows) {
       // per chunk only the Top-K position and the victim slot are kept (32-bit)
       // while the host loads are in flight; addresses are rebuilt for the stores
       u32x4 v[kCopyItems];
       int pos[kCopyItems], vic[kCopyItems];
+      if (deep) {
+        int tok[kCopyItems];
 #pragma unroll
-      for (int j = 0; j < kCopyItems; ++j) {
-        const int c = j * kCopyThreads + threadIdx.x;
-        const int r = c / kRowChunks;
-        const int col = c - r * kRowChunks;
-        const int jj = j0 + r;
-        pos[j] = -1;
-        if (jj < n) {
-          const int i = a.miss_pos[bk + jj];
-          if (!in_bounds(i, K, a.status, KVS_SITE_MISS)) continue;
-          const int tok = a.topk[bk + i];
-          const int vs = a.victims[bk + jj];
-          if (!in_bounds(tok, a.N, a.status, KVS_SITE_MISS) ||
-              !in_bounds(vs, a.S, a.status, KVS_SITE_MISS))
-            continue;
-          v[j] = a.pool[(u * a.N + tok) * kRowChunks + col];
-          pos[j] = i;
-          vic[j] = vs;
+        for (int j = 0; j < kCopyItems; ++j) {
+          const int jm = min(j0 + (j * kCopyThreads + (int)threadIdx.x) / kRowChunks, n - 1);
+          tok[j] = a.miss_tok[bk + jm];
+          pos[j] = a.miss_pos[bk + jm];
+          vic[j] = a.victims[bk + jm];
+        }
+#pragma unroll
+        for (int j = 0; j < kCopyItems; ++j) {
+          const int c = j * kCopyThreads + threadIdx.x;
+          const int r = c / kRowChunks;
+          const int col = c - r * kRowChunks;
+          const bool in = j0 + r < n && in_bounds(tok[j], a.N, a.status, KVS_SITE_MISS) &&
+                          in_bounds(pos[j], K, a.status, KVS_SITE_MISS) &&
+                          in_bounds(vic[j], a.S, a.status, KVS_SITE_MISS);
+          if (!in) pos[j] = -1;
+          const unsigned off = in ? (unsigned)tok[j] * kRowBytes + col * 16
+                                  : (unsigned)(a.N * kRowBytes);   // out of range: zeros
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(psrc, (int)off, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kCopyItems; ++j) {
+          const int c = j * kCopyThreads + threadIdx.x;
+          const int r = c / kRowChunks;
+          const int col = c - r * kRowChunks;
+          const int jj = j0 + r;
+          pos[j] = -1;
+          if (jj < n) {
+            const int tok = a.miss_tok[bk + jj];
+            const int i = a.miss_pos[bk + jj];
+            const int vs = a.victims[bk + jj];
+            if (!in_bounds(i, K, a.status, KVS_SITE_MISS) ||
+                !in_bounds(tok, a.N, a.status, KVS_SITE_MISS) ||
+                !in_bounds(vs, a.S, a.status, KVS_SITE_MISS))
+              continue;
+            v[j] = a.pool[(u * a.N + tok) * kRowChunks + col];
+            pos[j] = i;
+            vic[j] = vs;
+          }
         }
       }
 #pragma unroll
@@ -1793,14 +1838,14 @@ hipError_t launch_diff_lru(const Layout& lay, const DevPtrs& d, int layer, const
   return hipLaunchKernel(fn, dim3(lay.B), dim3(kDiffThreads), args, lds, s);
 }
 
-hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, const int32_t* topk,
-                         hipStream_t s) {
+hipError_t launch_gather(const Layout& lay, const DevPtrs& d, int layer, hipStream_t s) {
   GatherArgs a;
   a.pool = reinterpret_cast<const u32x4*>(d.pool);
   a.hot = reinterpret_cast<u32x4*>(d.hot);
   a.cbuf = reinterpret_cast<u32x4*>(d.cbuf);
-  a.topk = topk;
   a.slot_of = d.slot_of;
+  a.miss_tok = d.miss_tok;
+  a.deep_fetch = lay.N * kRowBytes <= 0xffffffffll;
   a.miss_pos = d.miss_pos;
   a.victims = d.victims;
   a.counts = d.counts;
@@ -1831,7 +1876,8 @@ hipError_t launch_hit_copy(const Layout& lay, const DevPtrs& d, int layer, hipSt
   a.pool = reinterpret_cast<const u32x4*>(d.pool);
   a.hot = reinterpret_cast<u32x4*>(d.hot);
   a.cbuf = reinterpret_cast<u32x4*>(d.cbuf);
-  a.topk = nullptr;   // read by the fetch role only, which has no workgroup here
+  a.miss_tok = d.miss_tok;   // read by the fetch role only, which has no workgroup here
+  a.deep_fetch = 0;
   a.slot_of = d.slot_of;
   a.miss_pos = d.miss_pos;
   a.victims = d.victims;
