@@ -262,7 +262,10 @@ def test_topk_3000_slots_6000_every_unit(mode):
 ], ids=["k300", "k1025_l3", "k3000", "b17_k2048", "b9_k2100"])
 def test_separate_attention_every_unit(shape, mode):
     # gather, attention over the complete compute buffer and merge as separate
-    # launches: the same results as the assembling launch, checked the same way
+    # launches: the same results as the assembling launch, checked the same way.
+    # The gather's two host-read forms both run: k300 and k1025_l3 have few
+    # fetch workgroups with misses (every read of a pass issued at once), k3000,
+    # b17 and b9 enough for one read per thread (0.45-1.1 MB in flight).
     import token_level_gather_amd as kvs
     wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="separate", steps=6, **shape)
     flags = kvs.KVS_FLAG_SEPARATE_ATTENTION | (_direct() if "direct" in mode else 0)
