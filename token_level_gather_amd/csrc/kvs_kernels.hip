@@ -282,6 +282,20 @@ __device__ __forceinline__ void load_words(const void* p, uint32_t (&w)[W]) {
   }
 }
 
+// The matching wide stores of a thread's run of W 32-bit words.
+template <int W>
+__device__ __forceinline__ void store_words(void* p, const uint32_t (&w)[W]) {
+  if constexpr (W >= 4) {
+#pragma unroll
+    for (int v = 0; v < W / 4; ++v)
+      reinterpret_cast<u32x4*>(p)[v] = u32x4{w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]};
+  } else if constexpr (W == 2) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  } else {
+    *reinterpret_cast<uint32_t*>(p) = w[0];
+  }
+}
+
 // The N uint16 order entries at p (aligned to 2N bytes), widened to int.
 template <int N>
 __device__ __forceinline__ void load_order(const uint16_t* p, int (&o)[N]) {
@@ -427,6 +441,15 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
     const int tok = my_tok[j];
     my_slot[j] = tok2slot[tok >= 0 && (long long)tok < a.N ? tok : 0];
   }
+  // This thread's run of last_used, rewritten below with wide stores (the
+  // touched slots stamped t): a store per touched slot scatters each wave's
+  // stores over sixteen cache lines per instruction, about one address-unit
+  // clock each.  Loaded after the lookups, which the next steps wait for
+  // first.  Above 8 slots per thread the run does not fit the registers
+  // beside the rest, and each touched slot is stamped on its own.
+  constexpr bool kLuWide = SPT <= 8;
+  uint32_t my_lu[kLuWide ? SPT : 1];
+  if constexpr (kLuWide) load_words<SPT>(lu + pl, my_lu);
   for (int h = tid; h < H; h += kDiffThreads) hash[h] = -1;
   if (tid == 0) {
     err_bits = 0;
@@ -619,16 +642,20 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   int n_touched;
   const int ex2 = wg_exclusive_scan(cnt, wtot[1], n_touched);
   // touched slots are stamped t here, from each thread's own contiguous
-  // slots (stores a wave covers in a few cache lines, where stamping each hit
-  // and victim through its slot index scatters them)
+  // slots (where stamping each hit and victim through its slot index would
+  // scatter the stores), in the run of last_used written back whole below
   r = S - (n_hit + m) + (ex2 & 0xffff);
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
     if ((touched >> q) & 1u) {
       const int s = p0 + q;
-      lu[s] = t;
+      if constexpr (kLuWide) my_lu[q] = (uint32_t)t;
+      else lu[s] = t;
       if (in_bounds(r, S, a.status, KVS_SITE_DIFF_LIST)) lorder[r++] = (uint16_t)s;
     }
+  }
+  if constexpr (kLuWide) {
+    if (owns) store_words<SPT>(lu + p0, my_lu);
   }
   // hits in Top-K order: entries before this thread's, less its misses and empties
   r = i0 - (ex & 0xffff) - (ex2 >> 16);
