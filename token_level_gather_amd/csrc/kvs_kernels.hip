@@ -581,10 +581,22 @@ __global__ __launch_bounds__(kDiffThreads) void diff_lru_kernel(DiffArgs a) {
   const int m = packed & 0xffff;
   const int n_hit = S - (packed >> 16);
   // the token of the slot at each of this thread's order positions, read
-  // before any write below (victims use it)
+  // before any write below (victims use it).  The victims are the first m
+  // non-hit entries of the order, in the first few threads: the others skip
+  // these LDS reads (whole waves branch around them).
   int vold[SPT];
+  if constexpr (kLdsTok) {
+    if ((ex >> 16) < m) {
 #pragma unroll
-  for (int q = 0; q < SPT; ++q) vold[q] = kLdsTok ? s2t[min(my_ord[q], Sp - 1)] : my_old[q];
+      for (int q = 0; q < SPT; ++q) vold[q] = s2t[min(my_ord[q], Sp - 1)];
+    } else {
+#pragma unroll
+      for (int q = 0; q < SPT; ++q) vold[q] = -1;   // never read: no victim here
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < SPT; ++q) vold[q] = my_old[q];
+  }
   int r = ex & 0xffff;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
