@@ -30,7 +30,7 @@ def _small(name, **kw):
 
 
 @pytest.mark.parametrize("case", ["default", "padded", "direct", "separate", "separate_direct",
-                                  "zipf", "k3000"])
+                                  "separate_wide", "zipf", "k3000"])
 def test_checked_build_matches_oracle(case):
     import token_level_gather_amd as kvs
     flags = 0
@@ -40,6 +40,9 @@ def test_checked_build_matches_oracle(case):
         flags |= kvs.KVS_FLAG_SEPARATE_ATTENTION
     if case == "zipf":
         wl = W.WORKLOADS["ctx128k_b32_l8_zipf"].shrunk(batch=3, layers=2, context=20000, steps=5)
+    elif case == "separate_wide":   # enough fetch workgroups for one host read per thread
+        wl = _small("checked_separate_wide", batch=17, layers=1, context=6000, slots=2100,
+                    topk=2048, steps=3, fresh_rate=0.3)
     elif case == "k3000":   # 3 Top-K entries and 6 slots per diff thread
         wl = _small("checked_k3000", batch=2, layers=1, context=9000, slots=6000, topk=3000,
                     steps=4)
