@@ -272,6 +272,19 @@ def test_separate_attention_every_unit(shape, mode):
     _case(wl, wl.steps, range(wl.batch), padded="padded" in mode, flags=flags)
 
 
+@pytest.mark.parametrize("mode", ["default", "separate"])
+def test_batch_above_256_every_unit(mode):
+    # 300 requests: more diff workgroups and merge rows than CUs, one fetch and
+    # one hit workgroup per request in the assembling launch (600 in all), and
+    # the separate attention's 600 tiles shared by 200 workgroups across
+    # request boundaries
+    import token_level_gather_amd as kvs
+    wl = W.WORKLOADS["ctx16k_b64_k2048"].shrunk(name="b300", batch=300, layers=1, context=1500,
+                                                slots=300, topk=128, steps=4, fresh_rate=0.3)
+    flags = kvs.KVS_FLAG_SEPARATE_ATTENTION if mode == "separate" else 0
+    _case(wl, wl.steps, range(wl.batch), flags=flags)
+
+
 @pytest.mark.parametrize("topk,splits", [
     (300, 1),    # 5 tiles in one split: two full pairs and an odd tail
     (300, 2),    # 2 + 3 tiles
